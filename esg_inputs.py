@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the group-sparse SwiGLU layer.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark.  It holds only random draws and the workload shapes: none of the
+layer's arithmetic lives here, so the two implementations that are compared
+against each other never share computation through it.
+
+Recipe (the same for every workload; the pages publish no dataset or weights,
+so these draws stand in for the model shapes they name):
+
+* one CPU ``torch.Generator`` seeded with ``seed``; draws in fp32, in the fixed
+  order x, W_gate, W_up, W_down, dy, bias;
+* x ~ N(0, 1); W_gate, W_up ~ N(0, 1/d_model); W_down ~ N(0, 1/d_ff) -- the
+  nn.Linear fan-in scale the eugen_sparse README uses in its quick start;
+* dy ~ N(0, 1);
+* bias ~ U(-0.1, 0.1) when the workload has a load-balance bias;
+* every tensor is then cast to the run dtype, so the oracle (which upcasts the
+  stored values to fp64, exactly) and the GPU see identical bytes.
+
+Workload shapes follow the model tables of the FlashFFN README
+("Model configurations": 128M d_model 768 / intermediate 2048, 370M 1024 /
+2688, 1.3B SwiGLU 2048 / 5504) at batch 8 (its "Efficiency" section), with the
+group sizes, active counts and subsample sizes that the eugen_sparse README's
+"Parameters and how to choose them" table allows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "f32" or "bf16"
+    tokens: int
+    d_model: int
+    d_ff: int
+    group_size: int
+    k: int                # active groups per token
+    spg: Optional[int]    # subsample rows per group; None = full gate rows
+    bias: bool            # draw a load-balance bias
+    bias_update: bool     # the step also runs the bias update
+    dense: bool = False   # all groups active, no selection
+
+    @property
+    def groups(self) -> int:
+        return self.d_ff // self.group_size
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", "f32", 256, 128, 512, 32, 4, None, False, False),
+    "s128m_bf16": Workload("s128m_bf16", "bf16", 8192, 768, 2048, 64, 8, 8, True, True),
+    "s370m_bf16": Workload("s370m_bf16", "bf16", 16384, 1024, 2688, 128, 5, 16, True, False),
+    "s1p3b_bf16": Workload("s1p3b_bf16", "bf16", 32768, 2048, 5504, 128, 11, 16, True, False),
+    "dense1p3b_bf16": Workload("dense1p3b_bf16", "bf16", 65536, 2048, 5504, 128, 43, None, False, False,
+                               dense=True),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def make_inputs(tokens: int, d_model: int, d_ff: int, group_size: int, dtype: str = "bf16",
+                seed: int = 0, with_bias: bool = True, bias_scale: float = 0.1):
+    """Draw (x, w_gate, w_up, w_down, dy, bias) on the CPU in the run dtype.
+
+    bias is fp32 (it never enters a contraction) or None.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    groups = d_ff // group_size
+    x = torch.randn(tokens, d_model, generator=g, dtype=torch.float32)
+    w_gate = torch.randn(d_ff, d_model, generator=g, dtype=torch.float32) * d_model ** -0.5
+    w_up = torch.randn(d_ff, d_model, generator=g, dtype=torch.float32) * d_model ** -0.5
+    w_down = torch.randn(d_model, d_ff, generator=g, dtype=torch.float32) * d_ff ** -0.5
+    dy = torch.randn(tokens, d_model, generator=g, dtype=torch.float32)
+    bias = None
+    if with_bias:
+        bias = (torch.rand(groups, generator=g, dtype=torch.float32) * 2.0 - 1.0) * bias_scale
+    td = torch_dtype(dtype)
+    return x.to(td), w_gate.to(td), w_up.to(td), w_down.to(td), dy.to(td), bias
+
+
+def make_workload_inputs(w: Workload, seed: int = 0):
+    return make_inputs(w.tokens, w.d_model, w.d_ff, w.group_size, w.dtype, seed, w.bias)
+
+
+def skewed_bias(groups: int, hot: int = 4, level: float = 0.5) -> torch.Tensor:
+    """A bias that favours the first ``hot`` groups (a trained model's popular
+    groups, which the eugen_sparse README's pitfalls list contrasts with random
+    inputs).  Used to stress uneven buckets."""
+    b = torch.zeros(groups, dtype=torch.float32)
+    b[:hot] = level
+    return b
+
+
+def random_group_idx(tokens: int, groups: int, k: int, seed: int = 0) -> torch.Tensor:
+    """Distinct, ascending group ids per token drawn uniformly (int32 [T, k]).
+
+    Used where a test needs valid routing without running a selection."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    scores = torch.rand(tokens, groups, generator=g)
+    idx = torch.topk(scores, k, dim=1).indices
+    return torch.sort(idx, dim=1).values.to(torch.int32)
