@@ -1,0 +1,292 @@
+"""group_sparse_swiglu_amd -- group-sparse SwiGLU feed-forward layer for AMD MI355X.
+
+A thin ctypes binding of ``libesg.so`` (declared in ``include/esg.h``).  Torch
+supplies device memory and the current HIP stream; every computation runs in
+the library's HIP kernels.  There is no fallback: if the library is not built
+or no GPU is present, the calls raise.
+
+Names follow the eugen_sparse README ("What it does"): make_subsample_index,
+grouped_topk_select, sparse_swiglu_ffn (forward + backward),
+update_load_balance_bias.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "ESG_F32", "ESG_BF16", "EsgError", "lib", "library_path", "make_subsample_index", "grouped_topk_select",
+    "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn", "update_load_balance_bias",
+    "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
+    "FfnContext", "EXPORTED_SYMBOLS",
+]
+
+ESG_F32 = 0
+ESG_BF16 = 1
+STATUS_GROUP_OUT_OF_RANGE = 1
+STATUS_GROUP_DUPLICATE = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_c_int, _c_size, _c_vp, _c_f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes)
+_SIGNATURES = {
+    "esg_status_string": (ctypes.c_char_p, [_c_int]),
+    "esg_version": (_c_int, []),
+    "esg_make_subsample_index": (_c_int, [_c_int, _c_int, _c_int, ctypes.c_uint64, _c_vp]),
+    "esg_grouped_topk_select": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp,
+                                         _c_int, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "esg_bucket_workspace_size": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
+    "esg_bucket_by_group": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
+                                     _c_vp]),
+    "esg_sparse_swiglu_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                  ctypes.POINTER(_c_size), ctypes.POINTER(_c_size),
+                                                  ctypes.POINTER(_c_size)]),
+    "esg_sparse_swiglu_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_vp, _c_vp, _c_vp, _c_size, _c_vp, _c_size, _c_vp, _c_vp]),
+    "esg_sparse_swiglu_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _c_vp, _c_vp, _c_size, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
+                                       _c_vp]),
+    "esg_update_load_balance_bias": (_c_int, [_c_vp, _c_vp, _c_vp, _c_f, _c_f, _c_f, _c_f, _c_int, _c_vp]),
+    "esg_update_load_balance_bias_from_counts": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_f, _c_f, _c_f, _c_f,
+                                                          _c_int, _c_vp]),
+    "esg_timing_enable": (_c_int, [_c_int]),
+    "esg_timing_reset": (_c_int, []),
+    "esg_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class EsgError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libesg.so")
+
+
+def lib():
+    """Load libesg.so (built in-tree by ``python -m group_sparse_swiglu_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise EsgError(f"{path} is not built; run `python -m group_sparse_swiglu_amd.build`")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().esg_status_string(status).decode()
+        raise EsgError(f"{what}: {msg} (status {status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ESG_F32
+    if t.dtype == torch.bfloat16:
+        return ESG_BF16
+    raise EsgError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise EsgError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise EsgError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise EsgError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_subsample_index(d_ff: int, group_size: int, samples_per_group: int, seed: int):
+    """Fixed random subset of gate rows per group -> (int32 CPU tensor [G*spg], spg)."""
+    groups = d_ff // group_size if group_size > 0 else 0
+    out = torch.empty(max(groups * samples_per_group, 1), dtype=torch.int32)
+    _check(lib().esg_make_subsample_index(d_ff, group_size, samples_per_group, seed, out.data_ptr()),
+           "make_subsample_index")
+    return out[:groups * samples_per_group], samples_per_group
+
+
+def grouped_topk_select(x, w_gate, group_size: int, num_active_groups: int, subsample_idx=None,
+                        samples_per_group: Optional[int] = None, load_balance_bias=None, return_counts=False):
+    """Per-token top-k groups by energy -> int32 [T, k] (and int32 counts [G])."""
+    T, d = x.shape
+    F = w_gate.shape[0]
+    G = F // group_size
+    code = _dtype_code(x)
+    if w_gate.dtype != x.dtype:
+        raise EsgError("x and w_gate must share a dtype")
+    idx = torch.empty(T, num_active_groups, dtype=torch.int32, device=x.device)
+    counts = torch.empty(G, dtype=torch.int32, device=x.device) if return_counts else None
+    spg = samples_per_group if samples_per_group is not None else 0
+    _check(lib().esg_grouped_topk_select(
+        _dev(x, "x"), _dev(w_gate, "w_gate"), code, T, d, F, group_size, num_active_groups,
+        _dev(subsample_idx, "subsample_idx", torch.int32), spg, _dev(load_balance_bias, "bias", torch.float32),
+        _dev(idx, "idx"), _dev(counts, "counts"), _stream(x.device)), "grouped_topk_select")
+    return (idx, counts) if return_counts else idx
+
+
+def bucket_by_group(idx, groups: int, status=None):
+    """CSR of (token, slot) pairs by group -> (offsets [G+1], perm_token [T*k], inv [T, k])."""
+    T, k = idx.shape
+    need = _c_size()
+    _check(lib().esg_bucket_workspace_size(T, k, groups, ctypes.byref(need)), "bucket_workspace_size")
+    dev = idx.device
+    scratch = torch.empty(max(need.value, 16), dtype=torch.uint8, device=dev)
+    offsets = torch.empty(groups + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty(T, k, dtype=torch.int32, device=dev)
+    _check(lib().esg_bucket_by_group(_dev(idx, "idx", torch.int32), T, k, groups, _dev(offsets, "offsets"),
+                                     _dev(perm, "perm"), _dev(inv, "inv"), _dev(status, "status", torch.int32),
+                                     _dev(scratch, "scratch"), scratch.numel(), _stream(dev)), "bucket_by_group")
+    return offsets, perm[:T * k], inv
+
+
+def workspace_size(tokens, d_model, d_ff, group_size, k, dtype_code, dense=False):
+    sv, fw, bw = _c_size(), _c_size(), _c_size()
+    _check(lib().esg_sparse_swiglu_workspace_size(tokens, d_model, d_ff, group_size, k, dtype_code, int(dense),
+                                                  ctypes.byref(sv), ctypes.byref(fw), ctypes.byref(bw)),
+           "workspace_size")
+    return sv.value, fw.value, bw.value
+
+
+@dataclass
+class FfnContext:
+    """What the backward needs from the forward (caller-owned buffers)."""
+    saved: torch.Tensor
+    idx: Optional[torch.Tensor]
+    group_size: int
+    k: int
+
+
+def _ws(nbytes: int, dev, cache: Optional[dict], key: str) -> torch.Tensor:
+    nbytes = max(int(nbytes), 256)
+    if cache is not None:
+        buf = cache.get(key)
+        if buf is None or buf.numel() < nbytes or buf.device != dev:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            cache[key] = buf
+        return buf
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, status=None, workspace=None,
+                      out=None):
+    """Forward -> (y [T, d], FfnContext).  group_idx None = every group active.
+
+    ``workspace``: optional dict reused across calls to hold scratch buffers."""
+    T, d = x.shape
+    F = w_gate.shape[0]
+    code = _dtype_code(x)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        if w.dtype != x.dtype:
+            raise EsgError(f"{name} must have the dtype of x")
+    k = group_idx.shape[1] if group_idx is not None else F // group_size
+    sv, fw, _ = workspace_size(T, d, F, group_size, k, code, group_idx is None)
+    dev = x.device
+    saved = torch.empty(max(sv, 256), dtype=torch.uint8, device=dev)
+    scratch = _ws(fw, dev, workspace, "fwd")
+    y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=dev)
+    _check(lib().esg_sparse_swiglu_fwd(
+        _dev(x, "x"), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"), code, T, d, F,
+        group_size, k, _dev(group_idx, "group_idx", torch.int32), _dev(y, "y"), _dev(saved, "saved"), saved.numel(),
+        _dev(scratch, "scratch"), scratch.numel(), _dev(status, "status", torch.int32), _stream(dev)),
+        "sparse_swiglu_fwd")
+    return y, FfnContext(saved, group_idx, group_size, k)
+
+
+def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=None, outs=None):
+    """Backward -> (dx, dW_gate, dW_up, dW_down), all overwritten."""
+    T, d = x.shape
+    F = w_gate.shape[0]
+    code = _dtype_code(x)
+    if dy.dtype != x.dtype:
+        raise EsgError("dy must have the dtype of x")
+    _, _, bw = workspace_size(T, d, F, ctx.group_size, ctx.k, code, ctx.idx is None)
+    dev = x.device
+    scratch = _ws(bw, dev, workspace, "bwd")
+    if outs is None:
+        outs = (torch.empty_like(x), torch.empty_like(w_gate), torch.empty_like(w_up), torch.empty_like(w_down))
+    dx, dwg, dwu, dwd = outs
+    _check(lib().esg_sparse_swiglu_bwd(
+        _dev(dy, "dy"), _dev(x, "x"), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"), code, T,
+        d, F, ctx.group_size, ctx.k, _dev(ctx.idx, "group_idx", torch.int32), _dev(ctx.saved, "saved"),
+        ctx.saved.numel(), _dev(dx, "dx"), _dev(dwg, "dw_gate"), _dev(dwu, "dw_up"), _dev(dwd, "dw_down"),
+        _dev(scratch, "scratch"), scratch.numel(), _stream(dev)), "sparse_swiglu_bwd")
+    return dx, dwg, dwu, dwd
+
+
+class _SparseSwiGLU(torch.autograd.Function):
+    @staticmethod
+    def forward(fctx, x, w_gate, w_up, w_down, group_idx, group_size):
+        y, c = sparse_swiglu_fwd(x.contiguous(), w_gate.contiguous(), w_up.contiguous(), w_down.contiguous(),
+                                 group_idx, group_size)
+        fctx.save_for_backward(x, w_gate, w_up, w_down)
+        fctx.esg = c
+        return y
+
+    @staticmethod
+    def backward(fctx, dy):
+        x, w_gate, w_up, w_down = fctx.saved_tensors
+        dx, dwg, dwu, dwd = sparse_swiglu_bwd(dy.contiguous(), x, w_gate, w_up, w_down, fctx.esg)
+        return dx, dwg, dwu, dwd, None, None
+
+
+def sparse_swiglu_ffn(x, W_gate, W_up, W_down, group_idx, group_size: int):
+    """Autograd entry: y = sum over selected groups of (SiLU(x W_g^T) * x W_u^T) W_d^T."""
+    return _SparseSwiGLU.apply(x, W_gate, W_up, W_down, group_idx, group_size)
+
+
+def update_load_balance_bias(bias, freq_ema, current_freq, target_freq: float, gamma: float, bias_max: float,
+                             momentum: float):
+    """In-place bias / EMA update (float32 device tensors [G])."""
+    G = bias.numel()
+    _check(lib().esg_update_load_balance_bias(
+        _dev(bias, "bias", torch.float32), _dev(freq_ema, "freq_ema", torch.float32),
+        _dev(current_freq, "current_freq", torch.float32), target_freq, gamma, bias_max, momentum, G,
+        _stream(bias.device)), "update_load_balance_bias")
+
+
+def update_load_balance_bias_from_counts(bias, freq_ema, counts, tokens: int, target_freq: float, gamma: float,
+                                         bias_max: float, momentum: float):
+    G = bias.numel()
+    _check(lib().esg_update_load_balance_bias_from_counts(
+        _dev(bias, "bias", torch.float32), _dev(freq_ema, "freq_ema", torch.float32),
+        _dev(counts, "counts", torch.int32), tokens, target_freq, gamma, bias_max, momentum, G,
+        _stream(bias.device)), "update_load_balance_bias_from_counts")
+
+
+def timing_enable(on: bool = True) -> None:
+    _check(lib().esg_timing_enable(int(on)), "timing_enable")
+
+
+def timing_reset() -> None:
+    _check(lib().esg_timing_reset(), "timing_reset")
+
+
+def timing_read(kernel: str):
+    """(total milliseconds, launches) of a library kernel since the last reset."""
+    ms, n = ctypes.c_double(), _c_int()
+    _check(lib().esg_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)), "timing_read")
+    return ms.value, n.value

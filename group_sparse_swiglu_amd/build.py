@@ -1,0 +1,70 @@
+"""Build libesg.so (the HIP/CDNA4 kernels and the C ABI) for gfx950, in-tree.
+
+    python -m group_sparse_swiglu_amd.build [--jobs N] [--verbose]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libesg.so")
+SOURCES = ["esg_select.hip", "esg_bucket.hip", "esg_ffn.hip", "esg_misc.hip", "esg_host.cpp", "esg_api.cpp"]
+ARCH = os.environ.get("ESG_OFFLOAD_ARCH", "gfx950")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+# packed fp32 ops are disabled for device code
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-munsafe-fp-atomics"]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON]
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip", *DEVICE]
+    else:
+        cmd += ["-D__HIP_PLATFORM_AMD__"]
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+    return obj
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed\n" + res.stdout + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("--verbose", action="store_true")
+    a = ap.parse_args()
+    print(build(a.jobs, a.verbose))
+    sys.exit(0)

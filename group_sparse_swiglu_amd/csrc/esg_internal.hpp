@@ -1,0 +1,78 @@
+// Host-side declarations shared by the esg translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace esg {
+
+// Kernel timing: when enabled, brackets a launch with events on its stream.
+struct LaunchTimer {
+  LaunchTimer(const char* name, hipStream_t stream);
+  ~LaunchTimer();
+  const char* name_;
+  hipStream_t stream_;
+  void* start_;
+};
+bool timing_enabled();
+
+// ---- selection -------------------------------------------------------------
+hipError_t launch_select(int dtype, const void* x, const void* w_gate, int tokens, int d_model,
+                         int groups, int k, const int32_t* sub, int rows_per_group, int group_size,
+                         const float* bias, int32_t* idx_out, int32_t* counts_out, hipStream_t stream);
+
+// ---- bucketing ---------------------------------------------------------------
+// Bucketing of (token, slot) pairs by group.  Tiles of `tile_rows` padded
+// positions are laid out group after group; see esg_bucket.hip.
+struct BucketOut {
+  int32_t* offsets;     // [G+1] or NULL
+  int32_t* perm_token;  // [T*k] (unpadded positions) or NULL
+  int32_t* inv;         // [T*k] unpadded positions or NULL
+  int32_t* tile_off;    // [G+1] prefix sums of tile counts, or NULL
+  int32_t* tile_group;  // [max_tiles] group of each tile (-1 = unused) or NULL
+  int32_t* ptoken;      // [max_tiles*tile_rows] token of each padded row (-1 = pad) or NULL
+  int32_t* pinv;        // [T*k] padded position of each pair (-1 = skipped) or NULL
+  int32_t* status;      // device status word or NULL
+};
+size_t bucket_scratch_bytes(int tokens, int groups);
+int max_tiles(int tokens, int k, int groups, int tile_rows);
+hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int tile_rows,
+                         const BucketOut& out, void* scratch, hipStream_t stream);
+
+// ---- FFN ----------------------------------------------------------------------
+struct FfnShape {
+  int dtype, tokens, d_model, d_ff, group_size, k;
+  int groups() const { return d_ff / group_size; }
+  // neurons per kernel block: 128 for bf16, 64 for fp32 (LDS capacity)
+  int gsb() const {
+    const int cap = dtype == 0 ? 64 : 128;
+    return group_size < cap ? group_size : cap;
+  }
+  int nsub() const { return group_size / gsb(); }                    // sub-blocks per group
+  int elem_bytes() const { return dtype == 0 ? 4 : 2; }
+};
+constexpr int kTileRows = 128;  // bucket positions per grouped-GEMM tile
+
+// Compact per-position activations [nsub][rows/EPC][gsb][EPC]
+hipError_t launch_fwd_grouped(const FfnShape& s, const void* x, const void* wg, const void* wu,
+                              const void* wd, const int32_t* tile_group, const int32_t* ptoken,
+                              int ntiles_max, void* hg_saved, void* hu_saved, void* partials,
+                              hipStream_t stream);
+hipError_t launch_rowsum(const FfnShape& s, const void* partials, size_t sub_stride_rows,
+                         const int32_t* pinv, void* out, hipStream_t stream);
+hipError_t launch_bwd_dh_dx(const FfnShape& s, const void* dy, const void* wg, const void* wu,
+                            const void* wd, const int32_t* tile_group, const int32_t* ptoken,
+                            int ntiles_max, const void* hg_saved, const void* hu_saved, void* dg,
+                            void* du, void* act, void* partials, hipStream_t stream);
+hipError_t launch_bwd_dw(const FfnShape& s, const void* x, const void* dy, const int32_t* tile_off,
+                         const int32_t* ptoken, int rows_total, const void* dg, const void* du,
+                         const void* act, void* dwg, void* dwu, void* dwd, hipStream_t stream);
+
+// ---- bias update / fills -------------------------------------------------------
+hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts,
+                              int tokens, float target, float gamma, float bias_max, float momentum,
+                              int groups, hipStream_t stream);
+hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stream);
+
+}  // namespace esg

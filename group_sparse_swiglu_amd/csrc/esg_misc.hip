@@ -1,0 +1,61 @@
+// Load-balance bias update (eugen_sparse README, "What it does",
+// update_load_balance_bias; "Parameters and how to choose them" gives
+// gamma 1e-3, bias_max 0.5, momentum 0.99 and target k/G) and small fills.
+//
+// Per group g, in float32 with every operation rounded separately (no fused
+// multiply-add, so a float32 host implementation reproduces it bit for bit):
+//   cur  = current_freq[g]            (or counts[g] / tokens)
+//   ema  = ema + (1 - momentum) * (cur - ema)
+//   bias = clamp(bias + gamma * sign(target - ema), -bias_max, bias_max)
+#include "esg_internal.hpp"
+
+namespace esg {
+namespace {
+
+__global__ void bias_update_kernel(float* __restrict__ bias, float* __restrict__ ema,
+                                   const float* __restrict__ freq, const int32_t* __restrict__ counts,
+                                   int tokens, float target, float gamma, float bias_max, float momentum,
+                                   int groups) {
+#pragma clang fp contract(off)
+  for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += gridDim.x * blockDim.x) {
+    const float cur = freq ? freq[g] : (float)counts[g] / (float)tokens;
+    const float e = ema[g];
+    const float om = 1.0f - momentum;
+    const float ne = e + om * (cur - e);
+    const float diff = target - ne;
+    const float step = diff > 0.0f ? gamma : (diff < 0.0f ? -gamma : 0.0f);
+    float nb = bias[g] + step;
+    nb = fminf(fmaxf(nb, -bias_max), bias_max);
+    ema[g] = ne;
+    bias[g] = nb;
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts, int tokens,
+                              float target, float gamma, float bias_max, float momentum, int groups,
+                              hipStream_t stream) {
+  if (groups == 0) return hipSuccess;
+  const int threads = 256;
+  const int blocks = (groups + threads - 1) / threads;
+  LaunchTimer timer("bias_update", stream);
+  hipLaunchKernelGGL(bias_update_kernel, dim3(blocks), dim3(threads), 0, stream, bias, ema, freq, counts, tokens,
+                     target, gamma, bias_max, momentum, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  LaunchTimer timer("fill", stream);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, value, n);
+  return hipGetLastError();
+}
+
+}  // namespace esg

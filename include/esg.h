@@ -1,0 +1,197 @@
+/*
+ * esg.h -- C ABI of the group-sparse SwiGLU feed-forward layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations are the ones the eugen_sparse README ("eugen_sparse --
+ * sparse SwiGLU FFN in Triton") lists under "What it does": the subsample of
+ * gate rows, the grouped top-k selection, the sparse SwiGLU forward and its
+ * gradients, and the load-balance bias update; plus the CSR bucketing the
+ * same page's "Pitfalls and limitations" section names as a deterministic
+ * internal step.  Shape rules follow that page's "Parameters and how to
+ * choose them" table.
+ *
+ * Conventions for every entry point:
+ *  - Returns an esg status code (ESG_OK = 0).  Argument and shape errors are
+ *    reported before anything is enqueued.
+ *  - Device pointers are plain HIP device addresses of contiguous row-major
+ *    buffers, 16-byte aligned.  Weights use nn.Linear layout: w_gate and w_up
+ *    are [d_ff, d_model], w_down is [d_model, d_ff].  Group g owns neurons
+ *    [g*group_size, (g+1)*group_size): rows of w_gate / w_up, columns of
+ *    w_down.
+ *  - The caller owns every buffer.  The library allocates no device memory and
+ *    keeps no state between calls (apart from optional kernel timing); all
+ *    scratch comes from caller buffers whose sizes the *_workspace_size calls
+ *    give.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    nothing synchronises.  Calls on one stream are ordered.
+ *  - dtype is ESG_F32 or ESG_BF16 for x, dy, the weights and the outputs
+ *    (y, dx, dW).  Group ids and counts are int32; bias, EMA and frequencies
+ *    are float32.  Accumulation is float32 in every contraction.
+ *  - tokens * k must stay below 2^31 (int32 positions).
+ */
+#ifndef ESG_H
+#define ESG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ESG_OK 0
+#define ESG_ERR_INVALID_ARG 1   /* null pointer, misaligned pointer, negative size */
+#define ESG_ERR_UNSUPPORTED 2   /* a shape rule is violated or the dtype is unknown */
+#define ESG_ERR_WORKSPACE 3     /* a workspace buffer is smaller than required */
+#define ESG_ERR_HIP 4           /* a HIP runtime call failed */
+
+/* dtypes */
+#define ESG_F32 0
+#define ESG_BF16 1
+
+/* bits OR-ed into the optional device status word by the bucketing pass */
+#define ESG_STATUS_GROUP_OUT_OF_RANGE 1   /* an id < 0 or >= G was skipped */
+#define ESG_STATUS_GROUP_DUPLICATE 2      /* a repeated id in one token was skipped */
+
+/* Human-readable name of a status code (static string). */
+const char* esg_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int esg_version(void);
+
+/*
+ * Fixed random subset of gate rows per group (eugen_sparse README, "What it
+ * does", make_subsample_index; drawn once per layer and kept with the model,
+ * "Pitfalls and limitations").
+ *
+ * Host only.  Writes G*samples_per_group int32 absolute w_gate row ids to the
+ * HOST buffer `out` (G = d_ff/group_size): group by group, ascending within a
+ * group, each group's ids inside its own row range.  The draw: one SplitMix64
+ * stream seeded with `seed`; per group, a partial Fisher-Yates shuffle of
+ * 0..group_size-1 with draw i taking (next() mod (group_size-i)) as the swap
+ * offset; the first samples_per_group ids are kept.  Deterministic per seed.
+ * Errors: ESG_ERR_INVALID_ARG (out NULL), ESG_ERR_UNSUPPORTED (shape rules, or
+ * samples_per_group outside 1..group_size).
+ */
+int esg_make_subsample_index(int d_ff, int group_size, int samples_per_group, uint64_t seed,
+                             int32_t* out);
+
+/*
+ * Grouped top-k selection (eugen_sparse README, "What it does",
+ * grouped_topk_select).  For every token t:
+ *   E[t,g] = sum over the group's gate rows r of |SiLU(x[t] . w_gate[r])|,
+ *   the rows being sub[g*spg .. g*spg+spg) when `sub` is given, else all
+ *   group_size rows of group g;
+ *   s[t,g] = E[t,g] + bias[g] (bias may be NULL = 0; selection only);
+ *   idx[t, 0..k) = the k groups with the largest s, equal scores ordered by
+ *   ascending group id, written in ascending group id.
+ * x: [tokens, d_model] dtype; w_gate: [d_ff, d_model] dtype; sub: device
+ * int32 [G*spg] or NULL (then spg is ignored); bias: device float [G] or NULL;
+ * idx_out: device int32 [tokens, k]; counts_out: device int32 [G] or NULL --
+ * overwritten with the number of tokens that selected each group.
+ * The energy is accumulated in float32; the ranking uses float32 scores.
+ * No gradient.  Constraints: G <= 1024.
+ */
+int esg_grouped_topk_select(const void* x, const void* w_gate, int dtype, int tokens, int d_model,
+                            int d_ff, int group_size, int k, const int32_t* sub, int samples_per_group,
+                            const float* bias, int32_t* idx_out, int32_t* counts_out, void* stream);
+
+/*
+ * Deterministic CSR bucketing of routed (token, slot) pairs by group (the
+ * eugen_sparse README, "Pitfalls and limitations", states that the CSR
+ * bucketing is deterministic).  Pairs are ordered by (group, token):
+ *   offsets[G+1]      exclusive prefix sums of the per-group counts;
+ *   perm_token[T*k]   the token at each bucket position;
+ *   inv[T*k]          the bucket position of pair (t, j) at t*k+j.
+ * Ids outside [0, G) and repeats of an id within a token are skipped: their
+ * inv entry is -1, they are not counted, and the matching ESG_STATUS_* bit is
+ * OR-ed into *status_dev (device int32, may be NULL; never cleared here).
+ * With skipped pairs, perm_token holds offsets[G] valid entries.
+ * scratch: device buffer of esg_bucket_workspace_size() bytes.
+ */
+int esg_bucket_workspace_size(int tokens, int k, int groups, size_t* scratch_bytes);
+int esg_bucket_by_group(const int32_t* idx, int tokens, int k, int groups, int32_t* offsets,
+                        int32_t* perm_token, int32_t* inv, int32_t* status_dev, void* scratch,
+                        size_t scratch_bytes, void* stream);
+
+/*
+ * Workspace sizes for the FFN.  `saved` is written by the forward and read by
+ * the backward of the same call pair (routing in CSR form and the compact
+ * gate/up pre-activations of the selected groups); it must not change in
+ * between.  `fwd_scratch` and `bwd_scratch` are free between calls.  dense=1
+ * sizes the all-groups-active path (idx = NULL).
+ */
+int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int group_size, int k,
+                                     int dtype, int dense, size_t* saved_bytes,
+                                     size_t* fwd_scratch_bytes, size_t* bwd_scratch_bytes);
+
+/*
+ * Forward (eugen_sparse README, "What it does", sparse_swiglu_ffn):
+ *   y[t] = sum over g in idx[t] of (SiLU(x[t] W_gate[g]^T) * (x[t] W_up[g]^T)) W_down[:,g]^T
+ * x: [tokens, d_model]; idx: device int32 [tokens, k] (distinct ids per token;
+ * see esg_bucket_by_group for what happens otherwise); y: [tokens, d_model]
+ * overwritten.  idx = NULL with k = G is the dense SwiGLU (every group
+ * active).  The gated activation of a group never leaves the chip; the k
+ * per-token contributions are summed in slot order without atomics, so the
+ * result is bitwise reproducible.  status_dev: as in esg_bucket_by_group.
+ */
+int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                          int dtype, int tokens, int d_model, int d_ff, int group_size, int k,
+                          const int32_t* idx, void* y, void* saved, size_t saved_bytes, void* scratch,
+                          size_t scratch_bytes, int32_t* status_dev, void* stream);
+
+/*
+ * Backward of the forward above with the routing held fixed (hard top-k: the
+ * README's pitfalls note that only selected groups receive weight gradients
+ * and the routing gets none).  With A = SiLU(Hg)*Hu on the selected groups:
+ *   dA = dy W_down (selected groups), dHu = dA*SiLU(Hg),
+ *   dHg = dA*Hu*SiLU'(Hg), dx = dHg W_gate + dHu W_up,
+ *   dW_gate = dHg^T x, dW_up = dHu^T x, dW_down = dy^T A.
+ * dy, dx: [tokens, d_model]; dw_gate, dw_up: [d_ff, d_model]; dw_down:
+ * [d_model, d_ff]; all overwritten (not accumulated).  Rows/columns of groups
+ * that no token selected are written as exact zeros.  `saved` and `idx` must
+ * be those of the matching forward call.  No atomics: bitwise reproducible.
+ */
+int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, const void* w_up,
+                          const void* w_down, int dtype, int tokens, int d_model, int d_ff,
+                          int group_size, int k, const int32_t* idx, const void* saved,
+                          size_t saved_bytes, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                          void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Load-balance bias update (eugen_sparse README, "What it does",
+ * update_load_balance_bias; constants in "Parameters and how to choose
+ * them"), once per optimizer step, in place on device float32 [groups]:
+ *   ema  <- ema + (1 - momentum) * (current_freq - ema)
+ *   bias <- clamp(bias + gamma * sign(target_freq - ema), -bias_max, bias_max)
+ * with sign(0) = 0, computed in float32 without fused multiply-add.
+ * current_freq[g] is the fraction of tokens that chose group g in the step
+ * (it sums to k); target_freq is normally k / G.
+ * The _from_counts form takes the int32 per-group counts of a selection call
+ * and the token count, and uses current_freq = counts / tokens.
+ */
+int esg_update_load_balance_bias(float* bias, float* freq_ema, const float* current_freq,
+                                 float target_freq, float gamma, float bias_max, float momentum,
+                                 int groups, void* stream);
+int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const int32_t* counts,
+                                             int tokens, float target_freq, float gamma,
+                                             float bias_max, float momentum, int groups,
+                                             void* stream);
+
+/*
+ * Kernel timing (instrumentation, off by default).  When enabled, every
+ * kernel the library launches is bracketed by HIP events recorded on the
+ * launch stream.  esg_timing_read synchronises on the recorded events and
+ * returns the summed duration in milliseconds and the launch count of the
+ * kernel named `kernel` since the last reset.  Not thread-safe.
+ */
+int esg_timing_enable(int on);
+int esg_timing_reset(void);
+int esg_timing_read(const char* kernel, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ESG_H */

@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every declared symbol, validates its
+arguments before any launch, and its host-only subsample draw matches the
+oracle bit for bit.  CPU only: no call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import group_sparse_swiglu_amd as E
+from oracle import esg_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "esg.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(esg_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = E.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(E.EXPORTED_SYMBOLS) == declared
+
+
+def test_status_strings():
+    lib = E.lib()
+    for code in range(5):
+        assert lib.esg_status_string(code)
+    assert lib.esg_version() >= 10000
+
+
+@pytest.mark.parametrize("d_ff,gs,spg,seed", [(2048, 64, 8, 0), (2688, 128, 16, 0), (5504, 128, 16, 0),
+                                              (512, 32, 32, 0), (96, 16, 5, 77), (16384, 16, 3, 2**63 + 5)])
+def test_subsample_matches_oracle(d_ff, gs, spg, seed):
+    sub, got_spg = E.make_subsample_index(d_ff, gs, spg, seed)
+    assert got_spg == spg
+    assert np.array_equal(sub.numpy(), O.make_subsample_index(d_ff, gs, spg, seed))
+
+
+@pytest.mark.parametrize("args", [(100, 32, 8), (128, 12, 8), (128, 32, 33), (128, 32, 0), (32, 32, 4),
+                                  (128, 8, 4)])
+def test_subsample_shape_rules(args):
+    with pytest.raises(E.EsgError):
+        E.make_subsample_index(*args, 0)
+
+
+def _sizes(*args):
+    sv, fw, bw = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    st = E.lib().esg_sparse_swiglu_workspace_size(*args, ctypes.byref(sv), ctypes.byref(fw), ctypes.byref(bw))
+    return st, sv.value, fw.value, bw.value
+
+
+def test_workspace_sizes_and_shape_rules():
+    st, sv, fw, bw = _sizes(8192, 768, 2048, 64, 8, E.ESG_BF16, 0)
+    assert st == 0 and sv > 0 and fw > 8192 * 8 * 768 * 2 and bw > fw
+    # shape rules of the README's parameter table
+    assert _sizes(8192, 760, 2048, 64, 8, E.ESG_BF16, 0)[0] == 2       # d_model % 16
+    assert _sizes(8192, 768, 2048, 48, 8, E.ESG_BF16, 0)[0] == 2       # gs not a power of two
+    assert _sizes(8192, 768, 2048, 8, 8, E.ESG_BF16, 0)[0] == 2        # gs < 16
+    assert _sizes(8192, 768, 64, 64, 1, E.ESG_BF16, 0)[0] == 2         # fewer than two groups
+    assert _sizes(8192, 768, 2048, 64, 33, E.ESG_BF16, 0)[0] == 2      # k > G
+    assert _sizes(8192, 768, 2048, 64, 8, 7, 0)[0] == 2                # dtype
+    assert _sizes(2**28, 768, 2048, 64, 8, E.ESG_BF16, 0)[0] == 2      # tokens*k >= 2^31
+    assert _sizes(-1, 768, 2048, 64, 8, E.ESG_BF16, 0)[0] == 1
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    lib = E.lib()
+    # NULL weights / misaligned pointers / bad shapes return before any HIP call
+    assert lib.esg_grouped_topk_select(None, None, 1, 16, 64, 128, 32, 2, None, 0, None, None, None, None) == 1
+    assert lib.esg_grouped_topk_select(8, 32, 1, 16, 64, 128, 32, 2, None, 0, None, 64, None, None) == 1
+    assert lib.esg_grouped_topk_select(32, 32, 1, 16, 64, 128, 32, 5, None, 0, None, 64, None, None) == 2
+    assert lib.esg_grouped_topk_select(32, 32, 1, 16, 64, 128, 32, 2, 64, 40, None, 64, None, None) == 2
+    assert lib.esg_sparse_swiglu_fwd(32, 32, 32, 32, 1, 16, 64, 128, 32, 2, 64, 64, 64, 0, 64, 0, None, None) == 3
+    assert lib.esg_sparse_swiglu_fwd(32, None, 32, 32, 1, 16, 64, 128, 32, 2, 64, 64, 64, 1 << 30, 64, 1 << 30,
+                                     None, None) == 1
+    assert lib.esg_sparse_swiglu_bwd(32, 32, 32, 32, 32, 1, 16, 64, 128, 32, 2, 64, 64, 0, 64, 64, 64, 64, 64, 0,
+                                     None) == 3
+    assert lib.esg_update_load_balance_bias(None, 64, 64, 0.25, 1e-3, 0.5, 0.99, 4, None) == 1
+    assert lib.esg_update_load_balance_bias_from_counts(64, 64, 64, 0, 0.25, 1e-3, 0.5, 0.99, 4, None) == 1
+    need = ctypes.c_size_t()
+    assert lib.esg_bucket_workspace_size(100, 200, 300, ctypes.byref(need)) == 2   # k above the bucket limit
+    assert lib.esg_bucket_workspace_size(100, 4, 2000, ctypes.byref(need)) == 2   # G above 1024
+    assert lib.esg_bucket_workspace_size(100, 4, 16, ctypes.byref(need)) == 0 and need.value > 0
+    assert lib.esg_bucket_by_group(64, 100, 4, 16, 64, 64, 64, None, 64, 0, None) == 3
+
+
+def test_timing_api_without_launches():
+    E.timing_reset()
+    E.timing_enable(True)
+    assert E.timing_read("fwd_grouped") == (0.0, 0)
+    E.timing_enable(False)

@@ -1,0 +1,185 @@
+"""GPU parity: sparse SwiGLU forward and backward vs the oracle, given the
+oracle's routing.  Bounds: relative max-abs 1e-4 (fp32), 2e-2 (bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import esg_inputs as I
+import group_sparse_swiglu_amd as E
+from gpu_common import DEV, f64, inputs, note, require_gpu, to_dev
+from oracle import esg_oracle as O
+from parity_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, idx_dev, ws=None):
+    x, wg, wu, wd, dy = (to_dev(inp[n]) for n in ("x", "wg", "wu", "wd", "dy"))
+    y, ctx = E.sparse_swiglu_fwd(x, wg, wu, wd, idx_dev, inp["gs"], workspace=ws)
+    grads = E.sparse_swiglu_bwd(dy, x, wg, wu, wd, ctx, workspace=ws)
+    torch.cuda.synchronize()
+    return (y,) + tuple(grads)
+
+
+def _oracle_routing(inp, k):
+    return O.grouped_topk_select(f64(inp["x"]), f64(inp["wg"]), inp["gs"], k,
+                                 None if inp["sub"] is None else inp["sub"].numpy(), inp["spg"],
+                                 None if inp["bias"] is None else inp["bias"].numpy())[0]
+
+
+def _full_compare(inp, idx, dtype):
+    outs = _run(inp, torch.as_tensor(idx, dtype=torch.int32).to(DEV))
+    y = O.sparse_swiglu_forward(f64(inp["x"]), f64(inp["wg"]), f64(inp["wu"]), f64(inp["wd"]), idx, inp["gs"])
+    grads = O.sparse_swiglu_backward(f64(inp["dy"]), f64(inp["x"]), f64(inp["wg"]), f64(inp["wu"]),
+                                     f64(inp["wd"]), idx, inp["gs"])
+    errs = {}
+    for name, g, r in zip(("y", "dx", "dW_gate", "dW_up", "dW_down"), outs, (y,) + tuple(grads)):
+        errs[name] = assert_close(name, f64(g), r, dtype)
+    print("  rel errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    return outs
+
+
+WORKLOAD_FULL = [
+    ("tiny_f32", 256, 128, 512, 32, 4, "f32", None, False),
+    ("s128m_bf16", 8192, 768, 2048, 64, 8, "bf16", 8, True),
+]
+
+
+@pytest.mark.parametrize("case", WORKLOAD_FULL, ids=[c[0] for c in WORKLOAD_FULL])
+def test_ffn_workload_full(case):
+    require_gpu()
+    name, T, d, F, gs, k, dtype, spg, bias = case
+    note(f"ffn full {name}")
+    inp = inputs(T, d, F, gs, dtype, seed=0, bias=bias, spg=spg)
+    _full_compare(inp, _oracle_routing(inp, k), dtype)
+
+
+WORKLOAD_SAMPLED = [
+    ("s370m_bf16", 16384, 1024, 2688, 128, 5, "bf16", 16, True),
+    ("s1p3b_bf16", 32768, 2048, 5504, 128, 11, "bf16", 16, True),
+]
+
+
+@pytest.mark.parametrize("case", WORKLOAD_SAMPLED, ids=[c[0] for c in WORKLOAD_SAMPLED])
+def test_ffn_workload_sampled(case):
+    """Full-size run; y and dx checked on sampled tokens (each depends on its
+    own token only), dW on sampled neurons (each needs that neuron's
+    activations over all tokens)."""
+    require_gpu()
+    name, T, d, F, gs, k, dtype, spg, bias = case
+    note(f"ffn sampled {name}")
+    inp = inputs(T, d, F, gs, dtype, seed=0, bias=bias, spg=spg)
+    idx = _oracle_routing(inp, k)
+    y, dx, dwg, dwu, dwd = _run(inp, torch.as_tensor(idx).to(DEV))
+    rng = np.random.default_rng(2)
+    toks = np.sort(rng.choice(T, 256, replace=False))
+    xs, dys = f64(inp["x"][toks]), f64(inp["dy"][toks])
+    W = [f64(inp[n]) for n in ("wg", "wu", "wd")]
+    assert_close("y", f64(y[toks]), O.swiglu_rows(xs, *W, idx[toks], gs), dtype)
+    assert_close("dx", f64(dx[toks]), O.dx_rows(dys, xs, *W, idx[toks], gs), dtype)
+    neu = np.sort(rng.choice(F, 24, replace=False))
+    rg, ru, rd = O.dw_neuron_rows(neu, f64(inp["dy"]), f64(inp["x"]), *W, idx, gs)
+    # rows of dW are compared against the scale of the sampled block
+    assert_close("dW_gate", f64(dwg[neu]), rg, dtype)
+    assert_close("dW_up", f64(dwu[neu]), ru, dtype)
+    assert_close("dW_down", f64(dwd[:, neu]), rd, dtype)
+
+
+EDGE = [
+    # name, T, d, F, gs, k, dtype
+    ("one_token", 1, 64, 256, 32, 2, "bf16"),
+    ("ragged_300", 300, 96, 512, 64, 3, "bf16"),
+    ("gs16_bf16", 200, 64, 256, 16, 5, "bf16"),
+    ("gs16_f32", 150, 48, 128, 16, 3, "f32"),
+    ("gs256_subblocks", 260, 128, 1024, 256, 2, "bf16"),
+    ("gs128_f32_subblocks", 200, 64, 512, 128, 2, "f32"),
+    ("f_not_pow2", 333, 80, 192, 64, 2, "bf16"),
+    ("d16", 100, 16, 128, 32, 2, "bf16"),
+    ("k1", 500, 128, 1024, 64, 1, "bf16"),
+    ("k_equals_g", 120, 64, 256, 32, 8, "bf16"),
+    ("empty_groups", 3, 64, 1024, 32, 2, "bf16"),
+    ("f32_wide", 513, 256, 1024, 64, 4, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_ffn_edge_shapes(case):
+    require_gpu()
+    name, T, d, F, gs, k, dtype = case
+    note(f"ffn edge {name}")
+    inp = inputs(T, d, F, gs, dtype, seed=11, bias=False)
+    idx = I.random_group_idx(T, F // gs, k, seed=T).numpy()
+    outs = _full_compare(inp, idx, dtype)
+    used = set(idx.ravel().tolist())
+    for g in range(F // gs):           # groups nobody chose: exact zeros
+        if g not in used:
+            sl = slice(g * gs, (g + 1) * gs)
+            assert torch.count_nonzero(outs[2][sl]) == 0
+            assert torch.count_nonzero(outs[3][sl]) == 0
+            assert torch.count_nonzero(outs[4][:, sl]) == 0
+
+
+def test_ffn_deterministic_and_unsorted_slots():
+    require_gpu()
+    note("ffn determinism")
+    inp = inputs(4096, 256, 2048, 64, "bf16", seed=12, bias=False)
+    idx = I.random_group_idx(4096, 32, 6, seed=3)
+    a = _run(inp, idx.to(DEV))
+    b = _run(inp, idx.to(DEV))
+    perm = torch.argsort(torch.rand(4096, 6, generator=torch.Generator().manual_seed(1)), dim=1)
+    c = _run(inp, torch.gather(idx, 1, perm).to(DEV))
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    # slot order only changes the order of the k-way sum
+    for name, u, v in zip(("y", "dx", "dWg", "dWu", "dWd"), a, c):
+        assert_close(name, f64(u), f64(v), "bf16")
+    for u, v in zip(a[2:], c[2:]):      # dW does not depend on slot order at all
+        assert torch.equal(u, v)
+
+
+def test_ffn_zero_tokens():
+    require_gpu()
+    note("ffn zero tokens")
+    inp = inputs(0, 64, 256, 32, "bf16", seed=1, bias=False)
+    idx = torch.zeros(0, 2, dtype=torch.int32)
+    y, dx, dwg, dwu, dwd = _run(inp, idx.to(DEV))
+    assert y.shape == (0, 64) and dx.shape == (0, 64)
+    for t in (dwg, dwu, dwd):
+        assert torch.count_nonzero(t) == 0
+
+
+def test_ffn_invalid_ids_are_skipped():
+    require_gpu()
+    note("ffn invalid ids")
+    T, d, F, gs = 64, 64, 256, 32
+    inp = inputs(T, d, F, gs, "bf16", seed=2, bias=False)
+    idx = I.random_group_idx(T, F // gs, 2, seed=5)
+    bad = idx.clone()
+    bad[::2, 1] = F // gs + 3            # out of range on even tokens
+    bad[1::4, 1] = bad[1::4, 0]          # duplicates on some odd tokens
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    x = to_dev(inp["x"])
+    y, _ = E.sparse_swiglu_fwd(x, to_dev(inp["wg"]), to_dev(inp["wu"]), to_dev(inp["wd"]), bad.to(DEV), gs,
+                               status=status)
+    torch.cuda.synchronize()
+    assert status.item() == (E.STATUS_GROUP_OUT_OF_RANGE | E.STATUS_GROUP_DUPLICATE)
+    keep = bad.clone()
+    W = [f64(inp[n]) for n in ("wg", "wu", "wd")]
+    for t in range(T):
+        valid = [g for j, g in enumerate(bad[t].tolist()) if 0 <= g < F // gs and g not in bad[t, :j].tolist()]
+        ref = O.swiglu_rows(f64(inp["x"][t:t + 1]), *W, np.array([valid]), gs)
+        assert_close(f"y[{t}]", f64(y[t:t + 1]), ref, "bf16")
+
+
+def test_autograd_wrapper_matches_entry_points():
+    require_gpu()
+    note("autograd wrapper")
+    inp = inputs(512, 128, 512, 32, "bf16", seed=9, bias=False)
+    idx = I.random_group_idx(512, 16, 3, seed=9).to(DEV)
+    params = [to_dev(inp[n]).requires_grad_(True) for n in ("x", "wg", "wu", "wd")]
+    y = E.sparse_swiglu_ffn(*params, idx, 32)
+    y.backward(to_dev(inp["dy"]))
+    ref = _run(inp, idx)
+    assert torch.equal(y.detach(), ref[0])
+    for p, r in zip(params, ref[1:]):
+        assert torch.equal(p.grad, r)
