@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the group-sparse SwiGLU hot path on one MI355X.
+
+One step is the whole path over one batch of seeded synthetic input already
+resident in HBM: grouped top-k selection (with per-group counts), the forward
+(CSR bucketing, fused grouped GEMMs, slot-order sum), the backward (dh+dx,
+dW) and the load-balance bias update from the step's counts.
+
+Prints ONE JSON line.  ``value`` is tokens per second of the whole step.  The
+``roofline`` object describes the kernel that takes the most time in the step:
+algorithmic FLOPs per launch divided by its average duration, measured with
+HIP events on its launch stream over the timed region.  ``cpu_baseline`` is
+the CPU oracle timed on this host's cores on a bounded slice of the same
+workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload s128m_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "sparse SwiGLU fwd+bwd tokens/s and active-FLOP MFMA % of bf16 peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (fp32: vector/MFMA fp32 peak)
+HBM_GBS = 8000.0
+
+# per-kernel algorithmic work (FLOPs) per launch, in units of T*k*gs*d
+KERNEL_FLOP_UNITS = {"fwd_grouped": 6, "bwd_dh_dx": 6, "bwd_dw": 6}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="s128m_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel HIP events")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, seconds):
+    """The CPU oracle (as it stands) on consecutive token slices of the same
+    inputs, until `seconds` have passed: selection, forward, backward and the
+    bias update per slice."""
+    import numpy as np
+    from oracle import esg_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 0) for p in threadpool_info()] or [0]) or os.cpu_count()
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    x, wg, wu, wd, dy, bias, sub = inp
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    W = (f64(wg), f64(wu), f64(wd))
+    subn = None if sub is None else sub.numpy()
+    biasn = None if bias is None else bias.numpy()
+    G = w.groups
+    slice_tokens = min(1024, w.tokens)
+    ema = np.full(G, w.k / G)
+    b = np.zeros(G) if biasn is None else biasn.astype(np.float64)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        s0 = done % w.tokens
+        xs, dys = f64(x[s0:s0 + slice_tokens]), f64(dy[s0:s0 + slice_tokens])
+        idx, _ = O.grouped_topk_select(xs, W[0], w.group_size, w.k, subn, w.spg, b)
+        O.sparse_swiglu_forward(xs, *W, idx, w.group_size)
+        O.sparse_swiglu_backward(dys, xs, *W, idx, w.group_size)
+        cur = O.frequency_from_counts(O.group_counts(idx, G), xs.shape[0])
+        b, ema = O.update_load_balance_bias(b, ema, cur, w.k / G, 1e-3, 0.5, 0.99)
+        done += xs.shape[0]
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} tokens of {w.name} in slices of {slice_tokens} (fp64 dense-masked select+fwd+bwd"
+                      f"+bias update), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU leg.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import esg_inputs as I
+    import group_sparse_swiglu_amd as E
+
+    w = I.WORKLOADS[args.workload]
+    if w.dense:
+        raise SystemExit(f"workload {w.name}: the dense path is not wired into this bench")
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    E.lib()
+
+    x, wg, wu, wd, dy, bias = I.make_workload_inputs(w, seed=0)
+    sub = E.make_subsample_index(w.d_ff, w.group_size, w.spg, 0)[0] if w.spg else None
+    host_inputs = (x, wg, wu, wd, dy, bias, sub)
+    X, WG, WU, WD, DY = (t.to(dev) for t in (x, wg, wu, wd, dy))
+    SUB = None if sub is None else sub.to(dev)
+    G = w.groups
+    BIAS = (bias if bias is not None else torch.zeros(G)).to(dev)
+    EMA = torch.full((G,), w.k / G, dtype=torch.float32, device=dev)
+    IDX = torch.empty(w.tokens, w.k, dtype=torch.int32, device=dev)
+    CNT = torch.empty(G, dtype=torch.int32, device=dev)
+    Y = torch.empty_like(X)
+    GRADS = (torch.empty_like(X), torch.empty_like(WG), torch.empty_like(WU), torch.empty_like(WD))
+    ws = {}
+    saved = [None]
+
+    def step():
+        E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, return_counts=True,
+                              out=IDX, counts_out=CNT)
+        _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, saved=saved[0])
+        saved[0] = ctx.saved
+        E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
+        if w.bias_update:
+            E.update_load_balance_bias_from_counts(BIAS, EMA, CNT, w.tokens, w.k / G, 1e-3, 0.5, 0.99)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    kernels = ["select", "fill", "bucket_count", "bucket_scan", "bucket_scatter", "fwd_grouped", "rowsum",
+               "bwd_dh_dx", "bwd_dw", "bias_update"]
+    timing = not args.no_kernel_timing
+    if timing:
+        E.timing_reset()
+        E.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_kernel = {}
+    if timing:
+        for k in kernels:
+            ms, n = E.timing_read(k)
+            if n:
+                per_kernel[k] = {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.steps,
+                                 "us_per_step": 1e3 * ms / args.steps}
+        E.timing_enable(False)
+        E.timing_reset()
+
+    ms_step = 1e3 * elapsed / args.steps
+    tokens_per_s = w.tokens / (elapsed / args.steps)
+    unit_flops = float(w.tokens) * w.k * w.group_size * w.d_model
+    active = 18.0 * unit_flops
+    peak = PEAK_TFLOPS[w.dtype]
+    roofline = None
+    fwd_bwd_us = None
+    if per_kernel:
+        dom = max((k for k in per_kernel if k in KERNEL_FLOP_UNITS), key=lambda k: per_kernel[k]["us_per_step"])
+        flops = KERNEL_FLOP_UNITS[dom] * unit_flops
+        achieved = flops / (per_kernel[dom]["avg_us"] * 1e-6) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                    "flops_per_launch": flops, "avg_launch_us": round(per_kernel[dom]["avg_us"], 2)}
+        # forward + backward kernels only (the counts fill belongs to the selection call)
+        fwd_bwd_us = sum(v["us_per_step"] for k, v in per_kernel.items()
+                         if k not in ("select", "fill", "bias_update"))
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "d_model": w.d_model, "d_ff": w.d_ff,
+                   "group_size": w.group_size, "groups": G, "k": w.k, "samples_per_group": w.spg,
+                   "bias": w.bias, "bias_update": w.bias_update,
+                   "step": "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else "")},
+        "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
+        "active_mfma_frac": round(active / (elapsed / args.steps) / 1e12 / peak, 4),
+        "roofline": roofline,
+    }
+    if fwd_bwd_us:
+        line["fwd_bwd_kernel_us"] = round(fwd_bwd_us, 2)
+        line["fwd_bwd_tokens_per_s"] = round(w.tokens / (fwd_bwd_us * 1e-6), 1)
+        line["fwd_bwd_active_mfma_frac"] = round(active / (fwd_bwd_us * 1e-6) / 1e12 / peak, 4)
+    if per_kernel:
+        line["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in per_kernel.items()}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, host_inputs, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

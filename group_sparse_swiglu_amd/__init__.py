@@ -129,7 +129,8 @@ def make_subsample_index(d_ff: int, group_size: int, samples_per_group: int, see
 
 
 def grouped_topk_select(x, w_gate, group_size: int, num_active_groups: int, subsample_idx=None,
-                        samples_per_group: Optional[int] = None, load_balance_bias=None, return_counts=False):
+                        samples_per_group: Optional[int] = None, load_balance_bias=None, return_counts=False,
+                        out=None, counts_out=None):
     """Per-token top-k groups by energy -> int32 [T, k] (and int32 counts [G])."""
     T, d = x.shape
     F = w_gate.shape[0]
@@ -137,8 +138,10 @@ def grouped_topk_select(x, w_gate, group_size: int, num_active_groups: int, subs
     code = _dtype_code(x)
     if w_gate.dtype != x.dtype:
         raise EsgError("x and w_gate must share a dtype")
-    idx = torch.empty(T, num_active_groups, dtype=torch.int32, device=x.device)
-    counts = torch.empty(G, dtype=torch.int32, device=x.device) if return_counts else None
+    idx = out if out is not None else torch.empty(T, num_active_groups, dtype=torch.int32, device=x.device)
+    counts = None
+    if return_counts:
+        counts = counts_out if counts_out is not None else torch.empty(G, dtype=torch.int32, device=x.device)
     spg = samples_per_group if samples_per_group is not None else 0
     _check(lib().esg_grouped_topk_select(
         _dev(x, "x"), _dev(w_gate, "w_gate"), code, T, d, F, group_size, num_active_groups,
@@ -192,7 +195,7 @@ def _ws(nbytes: int, dev, cache: Optional[dict], key: str) -> torch.Tensor:
 
 
 def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, status=None, workspace=None,
-                      out=None):
+                      out=None, saved=None):
     """Forward -> (y [T, d], FfnContext).  group_idx None = every group active.
 
     ``workspace``: optional dict reused across calls to hold scratch buffers."""
@@ -205,7 +208,8 @@ def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, statu
     k = group_idx.shape[1] if group_idx is not None else F // group_size
     sv, fw, _ = workspace_size(T, d, F, group_size, k, code, group_idx is None)
     dev = x.device
-    saved = torch.empty(max(sv, 256), dtype=torch.uint8, device=dev)
+    if saved is None or saved.numel() < sv:
+        saved = torch.empty(max(sv, 256), dtype=torch.uint8, device=dev)
     scratch = _ws(fw, dev, workspace, "fwd")
     y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=dev)
     _check(lib().esg_sparse_swiglu_fwd(

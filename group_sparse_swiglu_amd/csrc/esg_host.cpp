@@ -56,16 +56,28 @@ struct TimedLaunch {
 };
 bool g_timing = false;
 std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_pool;  // events reused across resets: no creation in timed loops
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
 }  // namespace
 
 bool timing_enabled() { return g_timing; }
 
 LaunchTimer::LaunchTimer(const char* name, hipStream_t stream) : name_(name), stream_(stream), start_(nullptr) {
   if (!g_timing) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEvent_t e = take_event();
+  if (e == nullptr) return;
   if (hipEventRecord(e, stream) != hipSuccess) {
-    (void)hipEventDestroy(e);
+    g_pool.push_back(e);
     return;
   }
   start_ = (void*)e;
@@ -73,9 +85,10 @@ LaunchTimer::LaunchTimer(const char* name, hipStream_t stream) : name_(name), st
 
 LaunchTimer::~LaunchTimer() {
   if (start_ == nullptr) return;
-  hipEvent_t stop;
-  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, stream_) != hipSuccess) {
-    (void)hipEventDestroy((hipEvent_t)start_);
+  hipEvent_t stop = take_event();
+  if (stop == nullptr || hipEventRecord(stop, stream_) != hipSuccess) {
+    g_pool.push_back((hipEvent_t)start_);
+    if (stop) g_pool.push_back(stop);
     return;
   }
   g_launches.push_back({name_, (hipEvent_t)start_, stop});
@@ -85,8 +98,9 @@ void timing_set(bool on) { g_timing = on; }
 
 void timing_reset() {
   for (auto& l : g_launches) {
-    (void)hipEventDestroy(l.start);
-    (void)hipEventDestroy(l.stop);
+    (void)hipEventSynchronize(l.stop);
+    g_pool.push_back(l.start);
+    g_pool.push_back(l.stop);
   }
   g_launches.clear();
 }
