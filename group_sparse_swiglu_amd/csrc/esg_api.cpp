@@ -193,8 +193,11 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
                 status_dev};
   hipError_t e = launch_bucket(idx, tokens, k, s.groups(), kTileRows, out, at<char>(scratch, L.f_bucket), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
-  e = launch_fwd_grouped(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, at<char>(saved, L.hg),
-                         at<char>(saved, L.hu), at<char>(scratch, L.f_part), stream_h);
+  e = bf16_pipelined(s, L.mt)
+          ? launch_fwd2(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, at<char>(saved, L.hg),
+                        at<char>(saved, L.hu), at<char>(scratch, L.f_part), stream_h)
+          : launch_fwd_grouped(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, at<char>(saved, L.hg),
+                               at<char>(saved, L.hu), at<char>(scratch, L.f_part), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
   e = launch_rowsum(s, at<char>(scratch, L.f_part), L.rows, out.pinv, y, stream_h);
   return hip_status(e);
@@ -230,14 +233,20 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
   const int32_t* tile_off = at<int32_t>(saved, L.tile_off);
   const int32_t* ptoken = at<int32_t>(saved, L.ptoken);
   const int32_t* pinv = at<int32_t>(saved, L.pinv);
-  hipError_t e = launch_bwd_dh_dx(s, dy, w_gate, w_up, w_down, tile_group, ptoken, L.mt, at<char>(saved, L.hg),
-                                  at<char>(saved, L.hu), at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
-                                  at<char>(scratch, L.b_act), at<char>(scratch, L.b_part), stream_h);
+  const bool v2 = bf16_pipelined(s, L.mt);
+  hipError_t e = v2 ? launch_dhdx2(s, dy, w_gate, w_up, w_down, tile_group, ptoken, L.mt, at<char>(saved, L.hg),
+                                   at<char>(saved, L.hu), at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
+                                   at<char>(scratch, L.b_act), at<char>(scratch, L.b_part), stream_h)
+                    : launch_bwd_dh_dx(s, dy, w_gate, w_up, w_down, tile_group, ptoken, L.mt, at<char>(saved, L.hg),
+                                       at<char>(saved, L.hu), at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
+                                       at<char>(scratch, L.b_act), at<char>(scratch, L.b_part), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
   e = launch_rowsum(s, at<char>(scratch, L.b_part), L.rows, pinv, dx, stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
-  e = launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
-                    at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, stream_h);
+  e = v2 ? launch_dw2(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
+                      at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, stream_h)
+         : launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
+                         at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, stream_h);
   return hip_status(e);
 }
 

@@ -83,7 +83,9 @@ __device__ int block_exclusive_scan(int v, int* buf, int* total) {
 constexpr int SCAN_NT = 1024;
 
 // bc[b][g] (counts) -> base[b][g] (CSR position of the block's first pair of
-// group g) and pbase[b][g] (same in the padded layout).
+// group g) and pbase[b][g] (same in the padded layout).  One workgroup: thread
+// t owns group g = t % G and a contiguous slice of the blocks; slice sums are
+// scanned per group in LDS, group totals are scanned across groups.
 __global__ __launch_bounds__(SCAN_NT) void bucket_scan_kernel(int nblocks, int groups, int tile_rows,
                                                               int max_tiles, const int32_t* __restrict__ bc,
                                                               int32_t* __restrict__ base,
@@ -91,36 +93,79 @@ __global__ __launch_bounds__(SCAN_NT) void bucket_scan_kernel(int nblocks, int g
                                                               int32_t* offsets, int32_t* tile_off,
                                                               int32_t* tile_group, int32_t* ptoken) {
   __shared__ int buf[SCAN_NT];
-  const int g = threadIdx.x;
-  int n = 0;
-  if (g < groups)
-    for (int b = 0; b < nblocks; ++b) n += bc[(size_t)b * groups + g];
-  int total = 0, total_tiles = 0;
-  const int off = block_exclusive_scan<SCAN_NT>(n, buf, &total);
-  const int nt = (n + tile_rows - 1) / tile_rows;
-  const int toff = block_exclusive_scan<SCAN_NT>(nt, buf, &total_tiles);
-  if (g < groups) {
-    if (offsets) offsets[g] = off;
-    if (tile_off) tile_off[g] = toff;
-    int run = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      const size_t i = (size_t)b * groups + g;
-      const int c = bc[i];
-      base[i] = off + run;
-      pbase[i] = toff * tile_rows + run;
-      run += c;
+  __shared__ int part[SCAN_NT];     // [slice][group] sums, then exclusive prefix over slices
+  __shared__ int g_off[SCAN_NT + 1], g_toff[SCAN_NT + 1];
+  const int tid = threadIdx.x;
+  const int slices = max(1, SCAN_NT / groups);
+  const int per = (nblocks + slices - 1) / slices;
+  const int g = tid % groups, sl = tid / groups;
+  const bool active = sl < slices;
+  const int b0 = min(nblocks, sl * per), b1 = min(nblocks, b0 + per);
+  int sum = 0;
+  if (active)
+    for (int b = b0; b < b1; ++b) sum += bc[(size_t)b * groups + g];
+  if (active) part[sl * groups + g] = sum;
+  __syncthreads();
+  int n = 0;  // total of group `tid`
+  if (tid < groups) {
+    for (int q = 0; q < slices; ++q) {
+      const int v = part[q * groups + tid];
+      part[q * groups + tid] = n;
+      n += v;
     }
-    if (tile_group)
-      for (int tt = toff; tt < toff + nt; ++tt) tile_group[tt] = g;
-    if (ptoken)
-      for (int p = toff * tile_rows + n; p < (toff + nt) * tile_rows; ++p) ptoken[p] = -1;
   }
-  if (g == 0) {
+  __syncthreads();
+  int total = 0, total_tiles = 0;
+  const int off = block_exclusive_scan<SCAN_NT>(tid < groups ? n : 0, buf, &total);
+  const int nt = tid < groups ? (n + tile_rows - 1) / tile_rows : 0;
+  const int toff = block_exclusive_scan<SCAN_NT>(nt, buf, &total_tiles);
+  if (tid < groups) {
+    g_off[tid] = off;
+    g_toff[tid] = toff;
+    if (offsets) offsets[tid] = off;
+    if (tile_off) tile_off[tid] = toff;
+  }
+  if (tid == 0) {
+    g_off[groups] = total;
+    g_toff[groups] = total_tiles;
     if (offsets) offsets[groups] = total;
     if (tile_off) tile_off[groups] = total_tiles;
   }
-  if (tile_group)
-    for (int tt = total_tiles + g; tt < max_tiles; tt += SCAN_NT) tile_group[tt] = -1;
+  __syncthreads();
+  if (active) {
+    int run = part[sl * groups + g];
+    const int o = g_off[g], po = g_toff[g] * tile_rows;
+    for (int b = b0; b < b1; ++b) {
+      const size_t i = (size_t)b * groups + g;
+      const int c = bc[i];
+      base[i] = o + run;
+      pbase[i] = po + run;
+      run += c;
+    }
+  }
+  // tile -> group by binary search over the tile offsets; -1 past the end
+  if (tile_group) {
+    for (int tt = tid; tt < max_tiles; tt += SCAN_NT) {
+      int grp = -1;
+      if (tt < total_tiles) {
+        int lo = 0, hi = groups - 1;  // last group with g_toff[grp] <= tt
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (g_toff[mid] <= tt) lo = mid; else hi = mid - 1;
+        }
+        grp = lo;
+      }
+      tile_group[tt] = grp;
+    }
+  }
+  // padding rows of each group's last tile
+  if (ptoken) {
+    for (int i = tid; i < groups * tile_rows; i += SCAN_NT) {
+      const int gg = i / tile_rows;
+      const int p = g_toff[gg] * tile_rows + (g_off[gg + 1] - g_off[gg]) + i % tile_rows;
+      if (p < g_toff[gg + 1] * tile_rows) ptoken[p] = -1;
+    }
+  }
 }
 
 __global__ __launch_bounds__(TB) void bucket_scatter_kernel(const int32_t* __restrict__ idx, int tokens,

@@ -41,13 +41,18 @@ struct Elem<float> {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// float -> bf16, round to nearest even, NaN kept quiet.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two floats -> two bf16 packed in one dword (low = a), round to nearest even
+// by the hardware convert.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// float -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 template <typename T>
 __device__ __forceinline__ float load_elem(const T* p);
@@ -94,10 +99,7 @@ struct Quad<bf16_t> {
     v[3] = __uint_as_float(q.y & 0xffff0000u);
   }
   static __device__ __forceinline__ void store(void* p, const float (&v)[4]) {
-    uint2 q;
-    q.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-    q.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-    *(uint2*)p = q;
+    *(uint2*)p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
 };
 
@@ -309,7 +311,8 @@ struct TransLoader {
   }
 };
 
-// SiLU and its derivative from the logistic function.
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic function with the hardware exponential and reciprocal (about one
+// ulp each); SiLU(z) = z * sigmoid(z).
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace esg

@@ -254,12 +254,8 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const T* __restrict__ parti
     }
     T* o = out + (size_t)t * d + v * EPC;
     if constexpr (EPC == 8) {
-      uint4 q;
-      q.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-      q.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-      q.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-      q.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-      *(uint4*)o = q;
+      *(uint4*)o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
     } else {
       *(float4*)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }

@@ -69,6 +69,20 @@ hipError_t launch_bwd_dw(const FfnShape& s, const void* x, const void* dy, const
                          const int32_t* ptoken, int rows_total, const void* dg, const void* du,
                          const void* act, void* dwg, void* dwu, void* dwd, hipStream_t stream);
 
+// Pipelined bf16 path (group blocks of 64 or 128 neurons, buffers < 2 GiB).
+// Its saved activations are row-major [sub][pos][gsb]; the generic path above
+// uses [sub][pos/EPC][gsb][EPC].  Forward and backward pick the same path.
+bool bf16_pipelined(const FfnShape& s, int ntiles_max);
+hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
+                       const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg_saved,
+                       void* hu_saved, void* partials, hipStream_t stream);
+hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const void* wu, const void* wd,
+                        const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, const void* hg_saved,
+                        const void* hu_saved, void* dg, void* du, void* act, void* partials, hipStream_t stream);
+hipError_t launch_dw2(const FfnShape& s, const void* x, const void* dy, const int32_t* tile_off, const int32_t* ptoken,
+                      int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
+                      hipStream_t stream);
+
 // ---- bias update / fills -------------------------------------------------------
 hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts,
                               int tokens, float target, float gamma, float bias_max, float momentum,

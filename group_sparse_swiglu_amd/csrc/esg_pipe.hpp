@@ -1,0 +1,136 @@
+// Pipelined bf16 tile primitives for gfx950 (CDNA4).
+//
+// Global -> LDS moves use the direct-to-LDS buffer load: each lane loads 16
+// bytes, and one wavefront instruction fills 1 KB of LDS at a wave-uniform
+// base (lane i lands at base + 16*i).  Buffer resources bound each source, so
+// an offset past the buffer (kOOB) reads zeros: padding rows and K/N tails
+// need no branches.  Each pipeline stage is its own __shared__ object so the
+// compiler tracks the outstanding loads of every stage separately.
+//
+// Two LDS tile layouts, both in 16-byte chunks with an XOR swizzle that
+// spreads the rows a fragment read touches over distinct banks:
+//  - K-row tile: row r holds 64 consecutive K values (128 bytes); chunk c of
+//    row r sits at r*128 + ((c ^ (r & 7)) * 16).  MFMA fragments are 16-byte
+//    reads (8 consecutive K of one row).
+//  - N-row tile: row k is one K index holding NCH*8 consecutive M/N values;
+//    chunk j of row k sits at k*NCH*16 + ((j ^ swz(k)) * 16).  MFMA fragments
+//    come from the transposing LDS read: within each 16-lane group, lane i
+//    receives element i%4 of the 8 bytes addressed by lane 4e + i/4 as its
+//    e-th value, so 16 lanes addressing a 4 x 16 block receive one column each.
+// The MFMA lane mapping matches esg_device.hpp: lane l reads K elements
+// kblock*32 + (l/16)*8 + 0..7 of operand row/column l%16.
+#pragma once
+
+#include "esg_device.hpp"
+
+#define ESG_LDS __attribute__((address_space(3)))
+
+namespace esg {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kOOB = 0x80000000u;  // at or past every buffer's record count
+
+// Buffer resource over [base, base + bytes); bytes < 2^31 (checked by the host).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Scalar descriptor of a raw (unstrided) buffer for the direct-to-LDS loads:
+// base address, record count = `bytes` (offsets at or past it read zero) and
+// the same format word as make_rsrc.
+struct DmaSrc {
+  u32x4_t d;
+};
+__device__ __forceinline__ DmaSrc make_dma_src(const void* base, uint32_t bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  DmaSrc s;
+  s.d = (u32x4_t){(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)p),
+                  (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(p >> 32) & 0xffffu)),
+                  (unsigned)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+  return s;
+}
+
+// One lane's 16-byte direct-to-LDS load; `wave_base` must be wave-uniform.
+// Written as inline assembly on purpose: the compiler then does not treat the
+// load as an LDS write, so it adds no waits of its own before LDS reads (it
+// cannot tell pipeline stages apart for the transposing reads and would wait
+// for every load in flight).  The loads have no register results; the caller
+// orders them with explicit vmcnt waits and barriers (wait_vmcnt, barrier).
+__device__ __forceinline__ void dma16(const DmaSrc& s, ESG_LDS char* wave_base, uint32_t voff) {
+  const int m = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m), "v"(voff), "s"(s.d)
+               : "memory", "m0");
+}
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// Workgroup barrier without the release fence of __syncthreads (which would
+// drain every outstanding direct-to-LDS load); the memory clobber keeps the
+// compiler from moving LDS accesses across it.  Callers wait for their own
+// loads / LDS reads first.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wave index as a scalar (keeps LDS bases and buffer resources uniform).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// ---- K-row tiles -----------------------------------------------------------
+__device__ __forceinline__ int krow_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+__device__ __forceinline__ uint4 frag_krow(const ESG_LDS char* t, int r, int c) {
+  const u32x4_t v = *(const ESG_LDS u32x4_t*)(t + krow_off(r, c));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 8-byte LDS write of four bf16 (two packed dwords).
+__device__ __forceinline__ void lds_write8(ESG_LDS char* p, uint32_t lo, uint32_t hi) {
+  *(ESG_LDS u32x2_t*)p = (u32x2_t){lo, hi};
+}
+
+// ---- N-row tiles -----------------------------------------------------------
+template <int NCH>
+__device__ __forceinline__ int mn_swz(int k);
+template <>
+__device__ __forceinline__ int mn_swz<16>(int k) {
+  return ((k >> 3) & 3) | ((k & 3) << 2);
+}
+template <>
+__device__ __forceinline__ int mn_swz<8>(int k) {
+  return ((k >> 3) & 3) | (((k >> 1) & 1) << 2);
+}
+template <int NCH>
+__device__ __forceinline__ int mnrow_off(int k, int j) {
+  return k * NCH * 16 + ((j ^ mn_swz<NCH>(k)) << 4);
+}
+
+// Fragment of operand columns n0..n0+15 (n0 % 16 == 0) for K-block kb from an
+// N-row tile: lane (q = l/16, i = l%16) gets column n0+i at K rows
+// kb*32 + q*8 + 0..7.
+template <int NCH>
+__device__ __forceinline__ uint4 frag_nrow(const ESG_LDS char* t, int kb, int n0, int lane) {
+  const int q = lane >> 4, i = lane & 15;
+  const int row = kb * 32 + q * 8 + (i >> 2);
+  const int colb = n0 * 2 + (i & 3) * 8;  // byte column addressed by this lane
+  const int j = colb >> 4, half = colb & 15;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + mnrow_off<NCH>(row, j) + half));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + mnrow_off<NCH>(row + 4, j) + half));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+__device__ __forceinline__ void mma_bf16(f32x4& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                               acc, 0, 0, 0);
+}
+
+}  // namespace esg

@@ -3,13 +3,13 @@
 // sum over sampled gate rows of |SiLU(x . w_gate_row)|, plus the bias.
 //
 // One workgroup owns BM tokens.  The gate contraction over the sampled rows
-// runs on MFMA in column chunks of 64 sampled rows; each chunk's |SiLU|
-// values are staged in LDS and summed per (token, group) in column order into
-// an fp32 energy table E[BM][G] that starts at the bias.  The top-k is then a
-// wavefront rank test: lane g counts the groups that beat group g (higher
-// score, or equal score and lower id); the group is selected when fewer than
-// k beat it, and its output slot is its rank among the selected ids (a ballot
-// prefix).  Every token's result depends only on its own row: batch
+// runs on MFMA over super-chunks of sampled rows held in registers; each
+// super-chunk's |SiLU| values are staged in LDS and summed per (token, group)
+// in column order into an fp32 energy table E[BM][G] that starts at the bias.
+// The top-k is a wavefront rank test: lane g counts the groups that beat group
+// g (higher score, or equal score and lower id); the group is selected when
+// fewer than k beat it, and its output slot is its rank among the selected ids
+// (a ballot prefix).  Every token's result depends only on its own row: batch
 // invariant and bitwise reproducible.
 #include "esg_device.hpp"
 #include "esg_internal.hpp"
@@ -18,47 +18,51 @@ namespace esg {
 namespace {
 
 constexpr int NT = 256;
-constexpr int BN = 64;  // sampled rows per column chunk
-constexpr int KC = 8;   // chunks per K stage
+constexpr int KC = 4;  // chunks per K stage
 
-template <typename T, int BM>
+// BM tokens per workgroup; each wave owns FNW 16-column fragments of a
+// super-chunk of 4*FNW*16 sampled rows, interleaved across the waves, so the
+// x tile is read once per super-chunk.
+template <typename T, int BM, int FNW>
 struct SelCfg {
-  static constexpr int WAVES_M = BM >= 32 ? BM / 32 : 1;
-  static constexpr int WAVES_N = 4 / WAVES_M;
-  static constexpr int FM = BM / (16 * WAVES_M);
-  static constexpr int FN = BN / (16 * WAVES_N);
+  static constexpr int NSC = 4 * FNW * 16;  // sampled rows per super-chunk
+  static constexpr int FM = BM / 16;
   static constexpr int PA = Plane<BM>::BYTES;
-  static constexpr int PB = Plane<BN>::BYTES;
+  static constexpr int PB = Plane<NSC>::BYTES;
   static constexpr int A_BYTES = KC * PA;
   static constexpr int B_BYTES = KC * PB;
-  static constexpr int S_STRIDE = BN + 1;  // floats per staged row
+  static constexpr int STAGES = 2 * (A_BYTES + B_BYTES);
+  static constexpr int S_STRIDE = NSC + 1;  // odd float stride: conflict-free column walks
   static constexpr int S_BYTES = BM * S_STRIDE * 4;
-  static constexpr int FIXED = 2 * A_BYTES + 2 * B_BYTES + S_BYTES;
+  static constexpr int FIXED = STAGES > S_BYTES ? STAGES : S_BYTES;
 };
 
-template <typename T, int BM>
+template <typename T, int BM, int FNW>
 __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, const T* __restrict__ wg,
                                                      int tokens, int d_model, int groups, int k,
                                                      const int32_t* __restrict__ sub, int rpg,
                                                      const float* __restrict__ bias,
                                                      int32_t* __restrict__ idx_out,
                                                      int32_t* __restrict__ counts) {
-  using C = SelCfg<T, BM>;
+  using C = SelCfg<T, BM, FNW>;
   extern __shared__ __align__(16) char smem[];
-  auto la = [&](int i_) -> char* { return i_ ? (smem + C::A_BYTES) : (smem); };
-  auto lb = [&](int i_) -> char* { return i_ ? (smem + 2 * C::A_BYTES + C::B_BYTES) : (smem + 2 * C::A_BYTES); };
-  float* S = (float*)(smem + 2 * C::A_BYTES + 2 * C::B_BYTES);
-  float* E = (float*)(smem + C::FIXED);  // [BM][groups]
-  int* cnt = (int*)(E + BM * groups);    // [groups]
+  auto la = [&](int i_) -> char* { return smem + i_ * C::A_BYTES; };
+  auto lb = [&](int i_) -> char* { return smem + 2 * C::A_BYTES + i_ * C::B_BYTES; };
+  float* S = (float*)smem;                     // aliases the stage buffers after each K loop
+  const int ES = groups | 1;                   // odd row stride of the energy table
+  float* E = (float*)(smem + C::FIXED);        // [BM][ES]
+  int* cnt = (int*)(E + BM * ES);              // [groups]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int t0 = blockIdx.x * BM;
   const int ncols = groups * rpg;
   const int kbytes = d_model * (int)sizeof(T);
-  const int nk = (d_model * (int)sizeof(T) + KC * 16 - 1) / (KC * 16);
+  const int nk = (kbytes + KC * 16 - 1) / (KC * 16);
 
-  for (int i = tid; i < BM * groups; i += NT) E[i] = bias ? bias[i % groups] : 0.0f;
+  for (int i = tid; i < BM * ES; i += NT) {
+    const int g = i % ES;
+    E[i] = (bias != nullptr && g < groups) ? bias[g] : 0.0f;
+  }
   for (int i = tid; i < groups; i += NT) cnt[i] = 0;
 
   RowKLoader<BM, KC, NT> ldA;
@@ -66,26 +70,25 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
     const int t = t0 + r;
     return t < tokens ? (const char*)(x + (size_t)t * d_model) : nullptr;
   });
-
-  int arow[C::FM], brow[C::FN];
+  int arow[C::FM], brow[FNW];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) arow[i] = wm * (C::FM * 16) + i * 16 + (lane & 15);
+  for (int i = 0; i < C::FM; ++i) arow[i] = i * 16 + (lane & 15);
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) brow[j] = wn * (C::FN * 16) + j * 16 + (lane & 15);
+  for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + wave) * 16 + (lane & 15);
 
-  for (int n0 = 0; n0 < ncols; n0 += BN) {
-    RowKLoader<BN, KC, NT> ldB;
+  for (int n0 = 0; n0 < ncols; n0 += C::NSC) {
+    RowKLoader<C::NSC, KC, NT> ldB;
     ldB.init(tid, [&](int r) -> const char* {
       const int col = n0 + r;
       if (col >= ncols) return nullptr;
       const int row = sub ? sub[col] : col;  // without a subsample the columns are all gate rows
       return (const char*)(wg + (size_t)row * d_model);
     });
-    f32x4 acc[C::FM][C::FN];
+    f32x4 acc[C::FM][FNW];
     zero_acc(acc);
     ldA.load(0, kbytes);
     ldB.load(0, kbytes);
-    __syncthreads();  // E init and previous chunk's S reads are done
+    __syncthreads();  // previous super-chunk's S reads and the E init are done
     ldA.store(la(0));
     ldB.store(lb(0));
     __syncthreads();
@@ -94,66 +97,84 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
         ldA.load((kt + 1) * KC * 16, kbytes);
         ldB.load((kt + 1) * KC * 16, kbytes);
       }
-      mma_lds<T, C::FM, C::FN, KC, C::PA, C::PB>(acc, la(kt & 1), lb(kt & 1), arow, brow, lane);
+      mma_lds<T, C::FM, FNW, KC, C::PA, C::PB>(acc, la(kt & 1), lb(kt & 1), arow, brow, lane);
       if (kt + 1 < nk) {
         ldA.store(la((kt + 1) & 1));
         ldB.store(lb((kt + 1) & 1));
       }
       __syncthreads();
     }
-    // |SiLU| of the chunk into S
+    // |SiLU| of the super-chunk into S
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < FNW; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = arow[i] - (lane & 15) + (lane >> 4) * 4 + e;
-          const int c = brow[j];
+          const int r = i * 16 + (lane >> 4) * 4 + e;
           const float h = acc[i][j][e];
-          S[r * C::S_STRIDE + c] = fabsf(h * sigmoid_f(h));
+          S[r * C::S_STRIDE + brow[j]] = fabsf(h * sigmoid_f(h));
         }
     __syncthreads();
-    // per (token, group) sums over this chunk's columns, in column order
+    // per (token, group) sums over this super-chunk's columns, in column order
     const int g_lo = n0 / rpg;
-    const int g_hi = min(groups - 1, (min(n0 + BN, ncols) - 1) / rpg);
+    const int g_hi = min(groups - 1, (min(n0 + C::NSC, ncols) - 1) / rpg);
     const int ng = g_hi - g_lo + 1;
     for (int p = tid; p < BM * ng; p += NT) {
-      const int r = p / ng, g = g_lo + p % ng;
-      const int c0 = max(n0, g * rpg) - n0, c1 = min(n0 + BN, (g + 1) * rpg) - n0;
-      float s = E[r * groups + g];
-      for (int c = c0; c < c1; ++c) s += S[r * C::S_STRIDE + c];
-      E[r * groups + g] = s;
+      const int r = p % BM, g = g_lo + p / BM;
+      const int c0 = max(n0, g * rpg) - n0, c1 = min(n0 + C::NSC, (g + 1) * rpg) - n0;
+      float sum = E[r * ES + g];
+      for (int c = c0; c < c1; ++c) sum += S[r * C::S_STRIDE + c];
+      E[r * ES + g] = sum;
     }
-    // the next chunk's first __syncthreads orders these writes before reuse
+    // the next super-chunk's first __syncthreads orders these before S is reused
   }
   __syncthreads();
 
-  // rank top-k: one token per wave at a time, lanes over groups
+  // rank top-k, one token per wave at a time: group g is selected when fewer
+  // than k groups beat it (higher score, or equal score and lower id)
+  const uint64_t lt = (1ull << lane) - 1ull;
   for (int r = wave; r < BM; r += 4) {
     const int t = t0 + r;
     if (t >= tokens) break;
-    const float* row = E + r * groups;
+    const float* row = E + r * ES;
     int base = 0;
-    for (int g0 = 0; g0 < groups; g0 += 64) {
-      const int g = g0 + lane;
-      bool sel = false;
-      if (g < groups) {
-        const float sg = row[g];
-        int beat = 0;
-        for (int q = 0; q < groups; ++q) {
-          const float sq = row[q];
-          beat += (sq > sg) || (sq == sg && q < g);
-        }
-        sel = beat < k;
+    if (groups <= 64) {
+      const float sg = lane < groups ? row[lane] : 0.0f;
+      const int sbits = __float_as_int(sg);
+      int beat = 0;
+      for (int q = 0; q < groups; ++q) {
+        const float sq = __int_as_float(__builtin_amdgcn_readlane(sbits, q));
+        beat += (sq > sg) || (sq == sg && q < lane);
       }
+      const bool sel = lane < groups && beat < k;
       const uint64_t m = __ballot(sel);
-      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+      const int pos = __popcll(m & lt);
       if (sel && pos < k) {  // NaN scores could select more than k: never write past the row
-        idx_out[(size_t)t * k + pos] = g;
-        if (counts) atomicAdd(&cnt[g], 1);
+        idx_out[(size_t)t * k + pos] = lane;
+        if (counts) atomicAdd(&cnt[lane], 1);
       }
-      base += __popcll(m);
+    } else {
+      for (int g0 = 0; g0 < groups; g0 += 64) {
+        const int g = g0 + lane;
+        bool sel = false;
+        if (g < groups) {
+          const float sg = row[g];
+          int beat = 0;
+          for (int q = 0; q < groups; ++q) {
+            const float sq = row[q];
+            beat += (sq > sg) || (sq == sg && q < g);
+          }
+          sel = beat < k;
+        }
+        const uint64_t m = __ballot(sel);
+        const int pos = base + __popcll(m & lt);
+        if (sel && pos < k) {
+          idx_out[(size_t)t * k + pos] = g;
+          if (counts) atomicAdd(&cnt[g], 1);
+        }
+        base += __popcll(m);
+      }
     }
   }
   if (counts) {
@@ -163,24 +184,48 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   }
 }
 
-template <typename T, int BM>
+template <typename T, int BM, int FNW>
 hipError_t launch_select_t(const void* x, const void* wg, int tokens, int d_model, int groups, int k,
                            const int32_t* sub, int rpg, const float* bias, int32_t* idx,
                            int32_t* counts, hipStream_t stream) {
-  using C = SelCfg<T, BM>;
-  const size_t smem = C::FIXED + (size_t)BM * groups * 4 + (size_t)groups * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_kernel<T, BM>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  using C = SelCfg<T, BM, FNW>;
+  const size_t smem = C::FIXED + (size_t)BM * (groups | 1) * 4 + (size_t)groups * 4;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
   const int blocks = (tokens + BM - 1) / BM;
   LaunchTimer timer("select", stream);
-  hipLaunchKernelGGL((select_kernel<T, BM>), dim3(blocks), dim3(NT), smem, stream, (const T*)x,
+  hipLaunchKernelGGL((select_kernel<T, BM, FNW>), dim3(blocks), dim3(NT), smem, stream, (const T*)x,
                      (const T*)wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts);
   return hipGetLastError();
+}
+
+// Fragments per wave: the choice with the least padded MFMA work (ties: wider).
+int pick_fnw(int ncols) {
+  int best = 8;
+  long long best_work = -1;
+  for (int f : {8, 6, 4, 2}) {
+    const long long nsc = 64LL * f;
+    const long long work = (ncols + nsc - 1) / nsc * nsc;
+    if (best_work < 0 || work < best_work) {
+      best_work = work;
+      best = f;
+    }
+  }
+  return best;
+}
+
+template <typename T>
+hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int groups, int k, const int32_t* sub,
+                    int rpg, const float* bias, int32_t* idx, int32_t* counts, hipStream_t st) {
+  if (groups > 256)
+    return launch_select_t<T, 16, 8>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+  switch (pick_fnw(groups * rpg)) {
+    case 2: return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+    case 4: return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+    case 6: return launch_select_t<T, 32, 6>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+    default: return launch_select_t<T, 32, 8>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+  }
 }
 
 }  // namespace
@@ -194,17 +239,10 @@ hipError_t launch_select(int dtype, const void* x, const void* w_gate, int token
     if (e != hipSuccess) return e;
   }
   if (tokens == 0) return hipSuccess;
-  const bool small_g = groups <= 256;
-  if (dtype == 0) {
-    return small_g ? launch_select_t<float, 64>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group,
-                                                bias, idx_out, counts_out, stream)
-                   : launch_select_t<float, 16>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group,
-                                                bias, idx_out, counts_out, stream);
-  }
-  return small_g ? launch_select_t<bf16_t, 64>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group,
-                                               bias, idx_out, counts_out, stream)
-                 : launch_select_t<bf16_t, 16>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group,
-                                               bias, idx_out, counts_out, stream);
+  return dtype == 0 ? select_d<float>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group, bias, idx_out,
+                                      counts_out, stream)
+                    : select_d<bf16_t>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group, bias, idx_out,
+                                       counts_out, stream);
 }
 
 }  // namespace esg

@@ -99,6 +99,9 @@ EDGE = [
     ("k_equals_g", 120, 64, 256, 32, 8, "bf16"),
     ("empty_groups", 3, 64, 1024, 32, 2, "bf16"),
     ("f32_wide", 513, 256, 1024, 64, 4, "f32"),
+    ("d16_gs64", 77, 16, 256, 64, 2, "bf16"),
+    ("d208_gs128", 150, 208, 512, 128, 2, "bf16"),
+    ("d1040_gs64_k3", 700, 1040, 640, 64, 3, "bf16"),
 ]
 
 
