@@ -27,8 +27,12 @@ METRIC = "sparse SwiGLU fwd+bwd tokens/s and active-FLOP MFMA % of bf16 peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense MFMA (fp32: vector/MFMA fp32 peak)
 HBM_GBS = 8000.0
 
-# per-kernel algorithmic work (FLOPs) per launch, in units of T*k*gs*d
-KERNEL_FLOP_UNITS = {"fwd_grouped": 6, "bwd_dh_dx": 6, "bwd_dw": 6}
+# per-kernel algorithmic work (FLOPs) per launch, in units of (tokens of the
+# launch)*k*gs*d.  The dense backward recomputes gate/up (4 units per token in
+# dense_rec) without credit: only its dA product (2 units) is the method's.
+KERNEL_FLOP_UNITS = {"fwd_grouped": 6, "bwd_dh_dx": 6, "bwd_dw": 6,
+                     "dense_fwd": 6, "dense_rec": 2, "dense_dx": 4, "dense_dw": 6}
+DENSE_CHUNK_TOKENS = 8192   # token chunk of the dense backward (one launch each of rec/dx/dw)
 
 
 def parse():
@@ -67,18 +71,23 @@ def cpu_baseline(w, inp, seconds):
     while True:
         s0 = done % w.tokens
         xs, dys = f64(x[s0:s0 + slice_tokens]), f64(dy[s0:s0 + slice_tokens])
-        idx, _ = O.grouped_topk_select(xs, W[0], w.group_size, w.k, subn, w.spg, b)
+        if w.dense:
+            idx = np.tile(np.arange(G, dtype=np.int32), (xs.shape[0], 1))
+        else:
+            idx, _ = O.grouped_topk_select(xs, W[0], w.group_size, w.k, subn, w.spg, b)
         O.sparse_swiglu_forward(xs, *W, idx, w.group_size)
         O.sparse_swiglu_backward(dys, xs, *W, idx, w.group_size)
-        cur = O.frequency_from_counts(O.group_counts(idx, G), xs.shape[0])
-        b, ema = O.update_load_balance_bias(b, ema, cur, w.k / G, 1e-3, 0.5, 0.99)
+        if w.bias_update:
+            cur = O.frequency_from_counts(O.group_counts(idx, G), xs.shape[0])
+            b, ema = O.update_load_balance_bias(b, ema, cur, w.k / G, 1e-3, 0.5, 0.99)
         done += xs.shape[0]
         el = time.perf_counter() - t0
         if el >= seconds:
             break
     return {"value": done / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} tokens of {w.name} in slices of {slice_tokens} (fp64 dense-masked select+fwd+bwd"
-                      f"+bias update), {el:.1f} s"}
+            "sample": f"{done} tokens of {w.name} in slices of {slice_tokens} (fp64 dense-masked "
+                      f"{'fwd+bwd' if w.dense else 'select+fwd+bwd'}"
+                      f"{'+bias update' if w.bias_update else ''}), {el:.1f} s"}
 
 
 def main():
@@ -93,8 +102,6 @@ def main():
     import group_sparse_swiglu_amd as E
 
     w = I.WORKLOADS[args.workload]
-    if w.dense:
-        raise SystemExit(f"workload {w.name}: the dense path is not wired into this bench")
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     dev = torch.device("cuda", 0)
@@ -117,6 +124,11 @@ def main():
     saved = [None]
 
     def step():
+        if w.dense:   # every group active: no selection, fused dense forward, recompute backward
+            _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, None, w.group_size, workspace=ws, out=Y, saved=saved[0])
+            saved[0] = ctx.saved
+            E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
+            return
         E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, return_counts=True,
                               out=IDX, counts_out=CNT)
         _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, saved=saved[0])
@@ -130,7 +142,8 @@ def main():
     torch.cuda.synchronize()
 
     kernels = ["select", "fill", "bucket_count", "bucket_scan", "bucket_scatter", "fwd_grouped", "rowsum",
-               "bwd_dh_dx", "bwd_dw", "bias_update"]
+               "bwd_dh_dx", "bwd_dw", "bias_update", "dense_fwd", "dense_route", "dense_rec", "dense_dx",
+               "dense_dw"]
     timing = not args.no_kernel_timing
     if timing:
         E.timing_reset()
@@ -160,7 +173,9 @@ def main():
     fwd_bwd_us = None
     if per_kernel:
         dom = max((k for k in per_kernel if k in KERNEL_FLOP_UNITS), key=lambda k: per_kernel[k]["us_per_step"])
-        flops = KERNEL_FLOP_UNITS[dom] * unit_flops
+        # tokens one launch processes (the dense backward runs once per token chunk)
+        launch_tokens = w.tokens / per_kernel[dom]["launches_per_step"]
+        flops = KERNEL_FLOP_UNITS[dom] * launch_tokens * w.k * w.group_size * w.d_model
         achieved = flops / (per_kernel[dom]["avg_us"] * 1e-6) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
@@ -168,6 +183,9 @@ def main():
         # forward + backward kernels only (the counts fill belongs to the selection call)
         fwd_bwd_us = sum(v["us_per_step"] for k, v in per_kernel.items()
                          if k not in ("select", "fill", "bias_update"))
+        line_kernel_flops = {k: KERNEL_FLOP_UNITS[k] * (w.tokens / v["launches_per_step"]) * w.k * w.group_size
+                             * w.d_model / (v["avg_us"] * 1e-6) / 1e12
+                             for k, v in per_kernel.items() if k in KERNEL_FLOP_UNITS}
 
     line = {
         "metric": METRIC,
@@ -185,7 +203,8 @@ def main():
         "config": {"workload": w.name, "tokens": w.tokens, "d_model": w.d_model, "d_ff": w.d_ff,
                    "group_size": w.group_size, "groups": G, "k": w.k, "samples_per_group": w.spg,
                    "bias": w.bias, "bias_update": w.bias_update,
-                   "step": "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else "")},
+                   "step": ("dense fwd+bwd (recompute)" if w.dense else
+                            "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else ""))},
         "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
         "active_mfma_frac": round(active / (elapsed / args.steps) / 1e12 / peak, 4),
         "roofline": roofline,
@@ -196,6 +215,7 @@ def main():
         line["fwd_bwd_active_mfma_frac"] = round(active / (fwd_bwd_us * 1e-6) / 1e12 / peak, 4)
     if per_kernel:
         line["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in per_kernel.items()}
+        line["kernels_algorithmic_tflops"] = {k: round(v, 1) for k, v in line_kernel_flops.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, host_inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)

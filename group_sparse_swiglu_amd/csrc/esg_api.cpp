@@ -160,7 +160,15 @@ int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int grou
                                      size_t* saved_bytes, size_t* fwd_scratch_bytes, size_t* bwd_scratch_bytes) {
   int st = check_shape(dtype, tokens, d_model, d_ff, group_size, k);
   if (st != ESG_OK) return st;
-  if (dense) return ESG_ERR_UNSUPPORTED;
+  if (dense) {
+    const FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
+    if (k != s.groups()) return ESG_ERR_INVALID_ARG;
+    if (!dense_supported(s)) return ESG_ERR_UNSUPPORTED;
+    if (saved_bytes) *saved_bytes = 0;
+    if (fwd_scratch_bytes) *fwd_scratch_bytes = 0;
+    if (bwd_scratch_bytes) *bwd_scratch_bytes = dense_bwd_layout(tokens, d_model, d_ff).bytes;
+    return ESG_OK;
+  }
   if (k > kMaxK) return ESG_ERR_UNSUPPORTED;
   const Layout L = make_layout(FfnShape{dtype, tokens, d_model, d_ff, group_size, k});
   if (saved_bytes) *saved_bytes = L.saved;
@@ -175,10 +183,18 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
                           void* stream) {
   int st = check_shape(dtype, tokens, d_model, d_ff, group_size, k);
   if (st != ESG_OK) return st;
-  if (w_gate == nullptr || w_up == nullptr || w_down == nullptr || saved == nullptr || scratch == nullptr)
-    return ESG_ERR_INVALID_ARG;
-  if (tokens == 0) return ESG_OK;                  // nothing to route or compute
-  if (idx == nullptr) return ESG_ERR_UNSUPPORTED;  // dense path not in this entry yet
+  if (w_gate == nullptr || w_up == nullptr || w_down == nullptr) return ESG_ERR_INVALID_ARG;
+  if (tokens == 0) return ESG_OK;  // nothing to route or compute (an empty idx may be NULL)
+  if (idx == nullptr) {            // dense limit: every group active, nothing saved
+    const FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
+    if (k != s.groups()) return ESG_ERR_INVALID_ARG;
+    if (!dense_supported(s)) return ESG_ERR_UNSUPPORTED;
+    if (x == nullptr || y == nullptr) return ESG_ERR_INVALID_ARG;
+    for (const void* p : {x, w_gate, w_up, w_down, (const void*)y})
+      if (!aligned16(p)) return ESG_ERR_INVALID_ARG;
+    return hip_status(launch_dense_fwd(s, x, w_gate, w_up, w_down, y, (hipStream_t)stream));
+  }
+  if (saved == nullptr || scratch == nullptr) return ESG_ERR_INVALID_ARG;
   if (k > kMaxK) return ESG_ERR_UNSUPPORTED;
   if (tokens > 0 && (x == nullptr || y == nullptr)) return ESG_ERR_INVALID_ARG;
   for (const void* p : {x, w_gate, w_up, w_down, (const void*)y, (const void*)idx, (const void*)saved,
@@ -209,10 +225,31 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
                           void* dw_down, void* scratch, size_t scratch_bytes, void* stream) {
   int st = check_shape(dtype, tokens, d_model, d_ff, group_size, k);
   if (st != ESG_OK) return st;
-  if (w_gate == nullptr || w_up == nullptr || w_down == nullptr || saved == nullptr || scratch == nullptr ||
-      dw_gate == nullptr || dw_up == nullptr || dw_down == nullptr)
+  if (w_gate == nullptr || w_up == nullptr || w_down == nullptr || scratch == nullptr || dw_gate == nullptr ||
+      dw_up == nullptr || dw_down == nullptr)
     return ESG_ERR_INVALID_ARG;
-  if (tokens > 0 && idx == nullptr) return ESG_ERR_UNSUPPORTED;
+  if (tokens == 0) {  // no token: every weight gradient is zero (an empty idx may be NULL)
+    hipStream_t stream_h = (hipStream_t)stream;
+    const size_t wbytes = (size_t)d_ff * d_model * (dtype == ESG_BF16 ? 2 : 4);
+    hipError_t e = zero_bytes(dw_gate, wbytes, stream_h);
+    if (e == hipSuccess) e = zero_bytes(dw_up, wbytes, stream_h);
+    if (e == hipSuccess) e = zero_bytes(dw_down, wbytes, stream_h);
+    return hip_status(e);
+  }
+  if (idx == nullptr) {  // dense limit: gate/up recomputed, nothing saved
+    const FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
+    if (k != s.groups()) return ESG_ERR_INVALID_ARG;
+    if (!dense_supported(s)) return ESG_ERR_UNSUPPORTED;
+    hipStream_t stream_h = (hipStream_t)stream;
+    if (x == nullptr || dy == nullptr || dx == nullptr) return ESG_ERR_INVALID_ARG;
+    for (const void* p : {dy, x, w_gate, w_up, w_down, (const void*)dx, (const void*)dw_gate, (const void*)dw_up,
+                          (const void*)dw_down, (const void*)scratch})
+      if (!aligned16(p)) return ESG_ERR_INVALID_ARG;
+    if (scratch_bytes < dense_bwd_layout(tokens, d_model, d_ff).bytes) return ESG_ERR_WORKSPACE;
+    return hip_status(
+        launch_dense_bwd(s, dy, x, w_gate, w_up, w_down, dx, dw_gate, dw_up, dw_down, scratch, stream_h));
+  }
+  if (saved == nullptr) return ESG_ERR_INVALID_ARG;
   if (k > kMaxK) return ESG_ERR_UNSUPPORTED;
   if (tokens > 0 && (x == nullptr || dy == nullptr || dx == nullptr)) return ESG_ERR_INVALID_ARG;
   for (const void* p : {dy, x, w_gate, w_up, w_down, saved, (const void*)dx, (const void*)dw_gate,
@@ -222,13 +259,6 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
   const Layout L = make_layout(s);
   if (saved_bytes < L.saved || scratch_bytes < L.bwd) return ESG_ERR_WORKSPACE;
   hipStream_t stream_h = (hipStream_t)stream;
-  const size_t wbytes = (size_t)d_ff * d_model * s.elem_bytes();
-  if (tokens == 0) {
-    hipError_t e = zero_bytes(dw_gate, wbytes, stream_h);
-    if (e == hipSuccess) e = zero_bytes(dw_up, wbytes, stream_h);
-    if (e == hipSuccess) e = zero_bytes(dw_down, wbytes, stream_h);
-    return hip_status(e);
-  }
   const int32_t* tile_group = at<int32_t>(saved, L.tile_group);
   const int32_t* tile_off = at<int32_t>(saved, L.tile_off);
   const int32_t* ptoken = at<int32_t>(saved, L.ptoken);

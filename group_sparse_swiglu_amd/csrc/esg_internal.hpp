@@ -83,6 +83,20 @@ hipError_t launch_dw2(const FfnShape& s, const void* x, const void* dy, const in
                       int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
                       hipStream_t stream);
 
+// ---- dense limit (all groups active) ----------------------------------------------
+constexpr int kDenseChunkTokens = 8192;  // backward token chunk (recompute workspace)
+struct DenseBwdLayout {
+  int tc = 0, chunks = 0, nblk = 0;      // chunk tokens (padded to 128), chunk count, 128-neuron blocks
+  size_t ptoken = 0, dg = 0, du = 0, act = 0, fg = 0, fu = 0, fd = 0, bytes = 0;
+};
+DenseBwdLayout dense_bwd_layout(int tokens, int d_model, int d_ff);
+bool dense_supported(const FfnShape& s);
+hipError_t launch_dense_fwd(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd, void* y,
+                            hipStream_t stream);
+hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, const void* wg, const void* wu,
+                            const void* wd, void* dx, void* dwg, void* dwu, void* dwd, void* scratch,
+                            hipStream_t stream);
+
 // ---- bias update / fills -------------------------------------------------------
 hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts,
                               int tokens, float target, float gamma, float bias_max, float momentum,

@@ -62,10 +62,12 @@ __device__ __forceinline__ DmaSrc make_dma_src(const void* base, uint32_t bytes)
 // orders them with explicit vmcnt waits and barriers (wait_vmcnt, barrier).
 __device__ __forceinline__ void dma16(const DmaSrc& s, ESG_LDS char* wave_base, uint32_t voff) {
   const int m = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m), "v"(voff), "s"(s.d)
-               : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(s.d), "{m0}"(m) : "memory");
+}
+// The same with 4 bytes per lane (one wavefront instruction fills 256 bytes).
+__device__ __forceinline__ void dma4(const DmaSrc& s, ESG_LDS char* wave_base, uint32_t voff) {
+  const int m = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)wave_base);
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(s.d), "{m0}"(m) : "memory");
 }
 
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)

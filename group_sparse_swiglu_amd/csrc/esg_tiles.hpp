@@ -1,0 +1,457 @@
+// Tile building blocks of the pipelined bf16 kernels (esg_ffn_bf16.hip,
+// esg_dense.hip): the direct-to-LDS pipelines, the per-tile phase-1 loops of
+// the forward (gate/up) and backward (dA) GEMMs, and the weight-gradient body.
+#pragma once
+
+#include "esg_internal.hpp"
+#include "esg_pipe.hpp"
+
+namespace esg {
+namespace tiles {
+
+constexpr int NT = 256;
+constexpr int BM = kTileRows;  // bucket positions per tile
+constexpr int DB = 128;        // d rows per forward phase-2 block
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store8(rsrc_t r, uint32_t voff, const float (&v)[4]) {
+  const v2i32 q = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(q, r, voff, 0, 0);
+}
+
+// Pipeline depth: 3 stages for 128-neuron blocks (one workgroup per CU), 2 for
+// 64-neuron blocks so that two workgroups share a CU.
+template <int GSB>
+constexpr int stages_for() {
+  return GSB >= 128 ? 3 : 2;
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS K loop with NS stages (2 or 3): tile t lands in stage t % NS
+// and NS-1 tiles are in flight ahead of the one consumed.
+//   issue(stage, t)    enqueues tile t's loads (L per lane; called once per
+//                      tile, in order);
+//   compute(stage, t)  consumes a landed tile and may end with S global stores
+//                      per lane (S > 0 only with NS = 2).
+// Step t waits for tile t with the exact vmcnt the issue order implies
+// (vector loads and stores retire in order): younger than tile t are the
+// loads of the tiles issued ahead of it and the stores of step t-1.  The
+// direct-to-LDS loads are invisible to the compiler (esg_pipe.hpp), so these
+// explicit waits are the only ones that order them, and the loop can stay a
+// plain rolled loop: the accumulators then stay in place across steps.
+// ---------------------------------------------------------------------------
+template <int NS, int L, int S, class Issue, class Compute>
+__device__ __forceinline__ void kloop(int nk, ESG_LDS char* s0, ESG_LDS char* s1, ESG_LDS char* s2, Issue&& issue,
+                                      Compute&& compute) {
+  static_assert(NS == 2 || NS == 3, "two or three stages");
+  static_assert(NS == 2 || S == 0, "stores inside the loop only with two stages");
+  auto stage = [&](int i) __attribute__((always_inline)) { return i == 0 ? s0 : (i == 1 ? s1 : s2); };
+  if (nk <= 0) return;
+  issue(s0, 0);
+  if (NS == 3 && nk > 1) issue(s1, 1);
+  int cur = 0;                   // t % NS
+  int nxt = NS - 1;              // (t + NS - 1) % NS
+  for (int t = 0; t < nk; ++t) {
+    if constexpr (NS == 3) {
+      if (t + 1 < nk)
+        wait_vmcnt<L>();
+      else
+        wait_vmcnt<0>();
+    } else {
+      if (t == 0)
+        wait_vmcnt<0>();
+      else
+        wait_vmcnt<S>();
+    }
+    wait_lgkm0();
+    barrier();
+    if (t + NS - 1 < nk) issue(stage(nxt), t + NS - 1);
+    compute(stage(cur), t);
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    nxt = nxt + 1 == NS ? 0 : nxt + 1;
+  }
+}
+
+
+// ===========================================================================
+// Forward
+// ===========================================================================
+template <int GSB>
+struct Fwd2 {
+  static constexpr int RA = 2 * GSB;           // weight rows per tile (gate, then up)
+  static constexpr int A_BYTES = RA * 128;     // one 64-wide K stage
+  static constexpr int B_BYTES = BM * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int IA = RA / 32;           // DMA instructions per lane per stage (A)
+  static constexpr int IB = BM / 32;           // (B)
+  static constexpr int L = IA + IB;
+  static constexpr int FMP = GSB / 32;         // gate/up fragment pairs per wave
+  static constexpr int FN = 4;                 // 64 positions per wave
+  static constexpr int KSUB = GSB / 64;        // 64-wide K sub-tiles of the group width
+  static constexpr int ACT_BYTES = KSUB * BM * 128;
+  static constexpr int W2_BYTES = KSUB * DB * 128;
+  static constexpr int FM2 = 4, FN2 = 4;       // phase-2 wave tile 64 d x 64 positions
+  static constexpr int STORES2 = FM2 * FN2;    // buffer stores per lane per d-block
+  static_assert(ACT_BYTES <= STAGE && W2_BYTES <= STAGE, "phase-2 tiles reuse the stages");
+};
+
+// Phase 1 of a forward tile: [hg; hu]^T for the GSB neurons from nb0 (gate
+// rows, then up rows) against the 128 bucket positions from prow0, whose token
+// ids come from ptoken (-1 = padding, reads zeros).  K = d in 64-wide stages.
+// acc[p][j] (p < FMP: gate, p >= FMP: up) follows the wave mapping below.
+template <int GSB, int NS>
+__device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                                            const bf16_t* __restrict__ wu, int tokens, int d, int F, int nb0,
+                                            const int32_t* __restrict__ ptoken, uint32_t prow0, ESG_LDS char* st0,
+                                            ESG_LDS char* st1, ESG_LDS char* st2,
+                                            f32x4 (&acc)[2 * Fwd2<GSB>::FMP][Fwd2<GSB>::FN]) {
+  using C = Fwd2<GSB>;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const uint32_t kbytes = (uint32_t)d * 2;
+  const DmaSrc rx = make_dma_src(x, (uint32_t)tokens * kbytes);
+  const DmaSrc rg = make_dma_src(wg, (uint32_t)F * kbytes);
+  const DmaSrc ru = make_dma_src(wu, (uint32_t)F * kbytes);
+
+  // ---- DMA addressing: lane (row = lane/8 of an 8-row group, slot = lane%8) ----
+  const int c_lane = (lane & 7) ^ (lane >> 3);  // logical chunk this lane moves
+  uint32_t voffA[C::IA];
+#pragma unroll
+  for (int i = 0; i < C::IA; ++i) {
+    const int r = (w * C::IA + i) * 8 + (lane >> 3);
+    const int grow = nb0 + (r < GSB ? r : r - GSB);
+    voffA[i] = grow < F ? (uint32_t)grow * kbytes + c_lane * 16 : kOOB;
+  }
+  uint32_t voffB[C::IB];
+#pragma unroll
+  for (int i = 0; i < C::IB; ++i) {
+    const int r = (w * C::IB + i) * 8 + (lane >> 3);
+    const int t = ptoken[prow0 + r];
+    voffB[i] = t >= 0 ? (uint32_t)t * kbytes + c_lane * 16 : kOOB;
+  }
+  auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
+    const uint32_t kb = (uint32_t)kt * 128;
+    const bool kin = kb + c_lane * 16 < kbytes;
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i) {
+      const bool gate = (w * C::IA + i) * 8 < GSB;  // wave-uniform
+      dma16(gate ? rg : ru, st + (w * C::IA + i) * 1024, (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+      dma16(rx, st + C::A_BYTES + (w * C::IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
+  };
+
+  // MFMA: wave (wm, wn) owns neurons [wm*GSB/2, +GSB/2) of gate and up, positions [wn*64, +64) ----
+  const int wm = w & 1, wn = w >> 1;
+  int arow[2 * C::FMP], brow[C::FN];
+#pragma unroll
+  for (int p = 0; p < C::FMP; ++p) {
+    arow[p] = wm * (GSB / 2) + p * 16 + (lane & 15);
+    arow[C::FMP + p] = GSB + arow[p];
+  }
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
+  zero_acc(acc);
+  auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int c = kb * 4 + (lane >> 4);
+      uint4 a[2 * C::FMP], b[C::FN];
+#pragma unroll
+      for (int i = 0; i < 2 * C::FMP; ++i) a[i] = frag_krow(st, arow[i], c);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) b[j] = frag_krow(st + C::A_BYTES, brow[j], c);
+#pragma unroll
+      for (int i = 0; i < 2 * C::FMP; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) mma_bf16(acc[i][j], a[i], b[j]);
+    }
+  };
+  kloop<NS, C::L, 0>((int)((kbytes + 127) / 128), st0, st1, st2, issue, compute);
+}
+
+// ===========================================================================
+// Backward dh (+ SiLU' epilogue) and dx partials.
+//   phase 1  dA^T = W_down[:, group cols]^T . dY_tile^T   (K = d); W_down comes
+//            in as an N-row tile (rows = d, columns = neurons)
+//   epilogue dg = dA*hu*SiLU'(hg), du = dA*SiLU(hg), a = SiLU(hg)*hu, stored
+//            row-major [pos][gsb] for the dW kernel; [dg du] to an LDS K-row tile
+//   phase 2  Q^T = [W_gate; W_up]^T[d-block] . [dg du]^T  (K = 2*gsb); the
+//            weights come in as N-row tiles (rows = neurons, columns = d)
+// ===========================================================================
+template <int GSB>
+struct Dh2 {
+  static constexpr int NCH = GSB / 8;            // 16-byte chunks per neuron row segment
+  static constexpr int A_BYTES = 64 * GSB * 2;   // N-row: 64 d rows x GSB neurons
+  static constexpr int B_BYTES = BM * 128;       // K-row: BM positions x 64 d
+  static constexpr int STAGE1 = A_BYTES + B_BYTES;
+  static constexpr int IA = NCH / 4;
+  static constexpr int IB = BM / 32;
+  static constexpr int L = IA + IB;
+  static constexpr int FM = GSB / 32, FN = 4;    // wave tile GSB/2 neurons x 64 positions
+  static constexpr int KSUB2 = 2 * GSB / 64;
+  static constexpr int DGU_BYTES = KSUB2 * BM * 128;
+  static constexpr int DB2 = 64;
+  static constexpr int W2_BYTES = 2 * GSB * DB2 * 2;  // N-row: 2*GSB neuron rows x 64 d
+  static constexpr int IW = 2 * GSB / 32;
+  static constexpr int FM2 = 2, FN2 = 4;         // wave tile 32 d x 64 positions
+  static constexpr int STORES2 = FM2 * FN2;
+  static constexpr int STAGE = STAGE1 > W2_BYTES ? STAGE1 : W2_BYTES;
+};
+
+// Phase 1 of a backward tile: dA^T = W_down[:, nb0 .. nb0+GSB)^T . dY_tile^T
+// (K = d) for the 128 bucket positions from prow0 (token ids from ptoken).
+template <int GSB, int NS>
+__device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf16_t* __restrict__ wd, int tokens,
+                                        int d, int F, int nb0, const int32_t* __restrict__ ptoken, uint32_t prow0,
+                                        ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2,
+                                        f32x4 (&acc)[Dh2<GSB>::FM][Dh2<GSB>::FN]) {
+  using C = Dh2<GSB>;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const uint32_t kbytes = (uint32_t)d * 2;
+  const DmaSrc ry = make_dma_src(dy, (uint32_t)tokens * kbytes);
+  const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
+
+  // phase-1 DMA: A = W_down N-row tile, B = dY K-row tile
+  uint32_t voffA[C::IA];
+  int rowA[C::IA];
+#pragma unroll
+  for (int i = 0; i < C::IA; ++i) {
+    const int row = (w * C::IA + i) * (64 / C::NCH) + lane / C::NCH;
+    const int j = (lane % C::NCH) ^ mn_swz<C::NCH>(row);
+    rowA[i] = nb0 + j * 8 < F ? row : 0x40000000;  // columns past F: never in range
+    voffA[i] = (uint32_t)row * F * 2 + (uint32_t)nb0 * 2 + j * 16;
+  }
+  const int c_lane = (lane & 7) ^ (lane >> 3);
+  uint32_t voffB[C::IB];
+#pragma unroll
+  for (int i = 0; i < C::IB; ++i) {
+    const int r = (w * C::IB + i) * 8 + (lane >> 3);
+    const int t = ptoken[prow0 + r];
+    voffB[i] = t >= 0 ? (uint32_t)t * kbytes + c_lane * 16 : kOOB;
+  }
+  auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
+    const uint32_t k0 = (uint32_t)kt * 64;
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i)
+      dma16(rd, st + (w * C::IA + i) * 1024, k0 + rowA[i] < (uint32_t)d ? voffA[i] + k0 * F * 2 : kOOB);
+    const uint32_t kb = k0 * 2;
+    const bool kin = kb + c_lane * 16 < kbytes;
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+      dma16(ry, st + C::A_BYTES + (w * C::IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
+  };
+  const int wm = w & 1, wn = w >> 1;
+  int brow[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
+  zero_acc(acc);
+  auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
+    uint4 a[2][C::FM], b[2][C::FN];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int c = kb * 4 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) a[kb][i] = frag_nrow<C::NCH>(st, kb, wm * (GSB / 2) + i * 16, lane);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) b[kb][j] = frag_krow(st + C::A_BYTES, brow[j], c);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) mma_bf16(acc[i][j], a[kb][i], b[kb][j]);
+  };
+  kloop<NS, C::L, 0>((d + 63) / 64, st0, st1, st2, issue, compute);
+}
+
+// ===========================================================================
+// Backward weight gradients, one workgroup per (group sub-block, 128-wide
+// d-block, kind) with K = the group's padded positions:
+//   kind 0: dW_gate|up[rows of g]^T[d-block] = X^T . [dg | du]
+//   kind 1: dW_down[d-block, cols of g]^T   = a^T . dY
+// Every operand comes in as an N-row tile (rows = positions).  Within a stage
+// LDS row R holds position perm(R) (two 2-bit fields of R swapped) so each
+// lane's four gathered rows are four consecutive positions whose token ids
+// come from one 16-byte load; both operands use the same row order, which
+// only permutes the K summation.
+// ===========================================================================
+template <int GSB>
+struct Dw2 {
+  static constexpr int NCHP = GSB / 8;           // chunks per position row of dg/du/a
+  static constexpr int X_BYTES = 64 * 256;       // N-row: 64 positions x 128 d
+  static constexpr int P_BYTES = 64 * GSB * 2;   // N-row: 64 positions x GSB neurons
+  static constexpr int STAGE = X_BYTES + 2 * P_BYTES;
+  static constexpr int IX = 4;
+  static constexpr int IP = NCHP / 4;
+  static constexpr int L0 = IX + 2 * IP, L1 = IX + IP;
+  static constexpr int FM0 = 4, FN0 = GSB / 16;  // kind 0 wave tile: 64 d x GSB neurons
+  static constexpr int FM1 = GSB / 32, FN1 = 4;  // kind 1 wave tile: GSB/2 neurons x 64 d
+};
+
+template <int MODE>
+__device__ __forceinline__ void store_dw(bf16_t* out, float* acc32, float (&v)[4]) {
+  if constexpr (MODE >= 2) {
+    float o[4];
+    Quad<float>::load(acc32, o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += o[e];
+  }
+  if constexpr (MODE == 0 || MODE == 3)
+    Quad<bf16_t>::store(out, v);
+  else
+    Quad<float>::store(acc32, v);
+}
+
+__device__ __forceinline__ int dw_perm(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// MODE: 0 stores bf16; 1 stores the fp32 sums to f0/f1; 2 adds them to
+// f0/f1; 3 adds f0/f1 and stores bf16 (K split over consecutive launches, in
+// a fixed order).  Ids of the K positions come from ptoken[pid0 ..], their
+// packed dg/du/a rows start at row p0; np positions (a multiple of 64).
+template <int GSB, int KIND, int NS, int MODE = 0>
+__device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tokens, int d, int F, int nb0,
+                                         const int32_t* __restrict__ ptoken, int pid0, int p0, int np,
+                                         size_t sub_el, float* __restrict__ f0, float* __restrict__ f1,
+                                         const bf16_t* __restrict__ pa, const bf16_t* __restrict__ pb,
+                                         uint32_t pbytes, bf16_t* __restrict__ out0, bf16_t* __restrict__ out1,
+                                         int db0, ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2) {
+  using C = Dw2<GSB>;
+  constexpr int NP = KIND == 0 ? 2 : 1;  // packed operand tiles per stage
+  constexpr int L = KIND == 0 ? C::L0 : C::L1;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const uint32_t kbytes = (uint32_t)d * 2;
+  const DmaSrc rz = make_dma_src(src, (uint32_t)tokens * kbytes);
+  const DmaSrc rpa = make_dma_src(pa, pbytes);
+  const DmaSrc rpb = make_dma_src(pb, pbytes);
+  const int nk = np / 64;
+
+  // gathered tile (x or dY): instruction i of wave w fills LDS rows
+  // (w*4 + i)*4 + q, q = lane/16, holding positions 16w + 4q + i
+  const int q = lane >> 4;
+  int jz[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) jz[i] = (lane & 15) ^ mn_swz<16>((w * 4 + i) * 4 + q);
+  // packed tiles (dg / du / a rows of positions)
+  uint32_t voffP[C::IP];
+#pragma unroll
+  for (int i = 0; i < C::IP; ++i) {
+    const int R = (w * C::IP + i) * (64 / C::NCHP) + lane / C::NCHP;
+    const int j = (lane % C::NCHP) ^ mn_swz<C::NCHP>(R);
+    voffP[i] = (uint32_t)((sub_el + (size_t)(p0 + dw_perm(R)) * GSB) * 2) + j * 16;
+  }
+  // The wave's 16 token ids of a tile come through the scalar unit (constant
+  // address space: ptoken is not written while this kernel runs), so that
+  // their wait is an lgkmcnt one, which every pipeline step performs anyway;
+  // a vector load would make the compiler wait for every load in flight.
+  // Lane group q takes ids 4q .. 4q+3.
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) i32x4 cint4;
+  struct IdBlock {
+    i32x4 v[4];
+  };
+  auto load_ids = [&](int kt) __attribute__((always_inline)) {
+    const cint4* src = (const cint4*)(ptoken + pid0 + kt * 64 + w * 16);
+    IdBlock r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = src[i];
+    return r;
+  };
+  IdBlock next_ids;  // ids of the next tile to issue, loaded one issue ahead
+  if (nk > 0) next_ids = load_ids(0);
+  auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
+    const IdBlock r = next_ids;
+    if (kt + 1 < nk) next_ids = load_ids(kt + 1);
+    int tk[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // branch-free pick of r.v[q][c]
+      const int lo = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[1][c] : r.v[0][c];
+      const int hi = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[3][c] : r.v[2][c];
+      tk[c] = q >= 2 ? hi : lo;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = tk[i] >= 0 && db0 + jz[i] * 8 < d;
+      dma16(rz, st + (w * 4 + i) * 1024, ok ? (uint32_t)tk[i] * kbytes + (uint32_t)db0 * 2 + jz[i] * 16 : kOOB);
+    }
+    const uint32_t kofs = (uint32_t)kt * 64 * GSB * 2;
+#pragma unroll
+    for (int i = 0; i < C::IP; ++i) dma16(rpa, st + C::X_BYTES + (w * C::IP + i) * 1024, voffP[i] + kofs);
+    if constexpr (NP == 2) {
+#pragma unroll
+      for (int i = 0; i < C::IP; ++i)
+        dma16(rpb, st + C::X_BYTES + C::P_BYTES + (w * C::IP + i) * 1024, voffP[i] + kofs);
+    }
+  };
+
+  const int wm = w & 1, wn = w >> 1;
+  constexpr int FM = KIND == 0 ? C::FM0 : C::FM1;
+  constexpr int FN = KIND == 0 ? C::FN0 : C::FN1;
+  f32x4 acc[FM][FN];
+  zero_acc(acc);
+  auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
+    uint4 a[2][FM], b[2][FN];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (KIND == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[kb][i] = frag_nrow<16>(st, kb, wm * 64 + i * 16, lane);
+        const ESG_LDS char* tb = st + C::X_BYTES + wn * C::P_BYTES;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[kb][j] = frag_nrow<C::NCHP>(tb, kb, j * 16, lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          a[kb][i] = frag_nrow<C::NCHP>(st + C::X_BYTES, kb, wm * (GSB / 2) + i * 16, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[kb][j] = frag_nrow<16>(st, kb, wn * 64 + j * 16, lane);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma_bf16(acc[i][j], a[kb][i], b[kb][j]);
+  };
+  kloop<NS, L, 0>(nk, st0, st1, st2, issue, compute);
+
+  if constexpr (KIND == 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int dd = db0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+      if (dd >= d) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = j * 16 + (lane & 15);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+        if (nb0 + n >= F) continue;
+        const size_t o = (size_t)(nb0 + n) * d + dd;
+        store_dw<MODE>((wn == 0 ? out0 : out1) + o, (wn == 0 ? f0 : f1) + o, v);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int n = wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int dd = db0 + wn * 64 + j * 16 + (lane & 15);
+        if (dd >= d) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
+        if (nb0 + n >= F) continue;
+        const size_t o = (size_t)dd * F + nb0 + n;
+        store_dw<MODE>(out0 + o, f0 + o, v);
+      }
+    }
+  }
+}
+
+}  // namespace tiles
+}  // namespace esg

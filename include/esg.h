@@ -120,7 +120,12 @@ int esg_bucket_by_group(const int32_t* idx, int tokens, int k, int groups, int32
  * the backward of the same call pair (routing in CSR form and the compact
  * gate/up pre-activations of the selected groups); it must not change in
  * between.  `fwd_scratch` and `bwd_scratch` are free between calls.  dense=1
- * sizes the all-groups-active path (idx = NULL).
+ * sizes the all-groups-active path (idx = NULL, k must equal G): it saves
+ * nothing and its forward needs no scratch; its backward scratch holds the
+ * recomputed dg, du, a of one chunk of at most 8192 tokens (3 * 2 bytes per
+ * neuron per token) plus, when there is more than one chunk, float32
+ * accumulators for the three weight gradients.  Errors: as for the forward;
+ * ESG_ERR_UNSUPPORTED for a dense shape the dense kernels do not cover.
  */
 int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int group_size, int k,
                                      int dtype, int dense, size_t* saved_bytes,
@@ -131,10 +136,16 @@ int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int grou
  *   y[t] = sum over g in idx[t] of (SiLU(x[t] W_gate[g]^T) * (x[t] W_up[g]^T)) W_down[:,g]^T
  * x: [tokens, d_model]; idx: device int32 [tokens, k] (distinct ids per token;
  * see esg_bucket_by_group for what happens otherwise); y: [tokens, d_model]
- * overwritten.  idx = NULL with k = G is the dense SwiGLU (every group
- * active).  The gated activation of a group never leaves the chip; the k
+ * overwritten.  The gated activation of a group never leaves the chip; the k
  * per-token contributions are summed in slot order without atomics, so the
  * result is bitwise reproducible.  status_dev: as in esg_bucket_by_group.
+ *
+ * Dense limit: idx = NULL with k = G means every group is active, i.e. the
+ * plain SwiGLU block (the README's layer with all groups selected).  It runs
+ * a fused kernel in which the [tokens, d_ff] intermediate never exists in
+ * device memory; saved and scratch are unused (may be NULL).  Supported for
+ * bf16 with d_model <= 2048; other dense shapes return ESG_ERR_UNSUPPORTED,
+ * and k != G with idx = NULL returns ESG_ERR_INVALID_ARG.
  */
 int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, const void* w_down,
                           int dtype, int tokens, int d_model, int d_ff, int group_size, int k,
@@ -152,6 +163,10 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
  * [d_model, d_ff]; all overwritten (not accumulated).  Rows/columns of groups
  * that no token selected are written as exact zeros.  `saved` and `idx` must
  * be those of the matching forward call.  No atomics: bitwise reproducible.
+ * Dense limit (idx = NULL, k = G): the gate/up pre-activations are recomputed
+ * per token chunk (the forward saved nothing; `saved` is unused and may be
+ * NULL); the weight gradients are summed over chunks in float32 in chunk
+ * order.  Same support rules as the dense forward.
  */
 int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, const void* w_up,
                           const void* w_down, int dtype, int tokens, int d_model, int d_ff,

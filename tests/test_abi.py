@@ -69,6 +69,12 @@ def test_workspace_sizes_and_shape_rules():
     assert _sizes(8192, 768, 2048, 64, 8, 7, 0)[0] == 2                # dtype
     assert _sizes(2**28, 768, 2048, 64, 8, E.ESG_BF16, 0)[0] == 2      # tokens*k >= 2^31
     assert _sizes(-1, 768, 2048, 64, 8, E.ESG_BF16, 0)[0] == 1
+    # dense limit (idx = NULL): nothing saved, no forward scratch, a chunked backward workspace
+    st, sv, fw, bw = _sizes(65536, 2048, 5504, 128, 43, E.ESG_BF16, 1)
+    assert st == 0 and sv == 0 and fw == 0 and bw >= 3 * 43 * 128 * 8192 * 2
+    assert _sizes(65536, 2048, 5504, 128, 42, E.ESG_BF16, 1)[0] == 1   # dense needs k == G
+    assert _sizes(256, 128, 512, 32, 16, E.ESG_F32, 1)[0] == 2         # dense kernels are bf16
+    assert _sizes(256, 2064, 512, 32, 16, E.ESG_BF16, 1)[0] == 2       # d_model above 2048
 
 
 def test_entry_points_reject_bad_arguments_before_launch():
@@ -83,6 +89,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
                                      None, None) == 1
     assert lib.esg_sparse_swiglu_bwd(32, 32, 32, 32, 32, 1, 16, 64, 128, 32, 2, 64, 64, 0, 64, 64, 64, 64, 64, 0,
                                      None) == 3
+    # dense (idx NULL): k must equal G; fp32 dense is not provided
+    assert lib.esg_sparse_swiglu_fwd(32, 32, 32, 32, 1, 16, 64, 128, 32, 2, None, 64, None, 0, None, 0, None,
+                                     None) == 1
+    assert lib.esg_sparse_swiglu_fwd(32, 32, 32, 32, 0, 16, 64, 128, 32, 4, None, 64, None, 0, None, 0, None,
+                                     None) == 2
+    assert lib.esg_sparse_swiglu_bwd(32, 32, 32, 32, 32, 1, 16, 64, 128, 32, 4, None, None, 0, 64, 64, 64, 64, 64,
+                                     16, None) == 3   # dense backward scratch too small
     assert lib.esg_update_load_balance_bias(None, 64, 64, 0.25, 1e-3, 0.5, 0.99, 4, None) == 1
     assert lib.esg_update_load_balance_bias_from_counts(64, 64, 64, 0, 0.25, 1e-3, 0.5, 0.99, 4, None) == 1
     need = ctypes.c_size_t()
