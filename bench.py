@@ -9,7 +9,9 @@ dW) and the load-balance bias update from the step's counts.
 Prints ONE JSON line.  ``value`` is tokens per second of the whole step.  The
 ``roofline`` object describes the kernel that takes the most time in the step:
 algorithmic FLOPs per launch divided by its average duration, measured with
-HIP events on its launch stream over the timed region.  ``cpu_baseline`` is
+HIP events on its launch stream over a second timed region of the same number
+of eagerly launched steps (the headline steps replay one captured HIP graph).
+``cpu_baseline`` is
 the CPU oracle timed on this host's cores on a bounded slice of the same
 workload.
 
@@ -44,7 +46,50 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel HIP events")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replaying the step as one HIP graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB (reference for the HBM counters)")
     return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources: traffic counters apply only to the code they were taken on."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_sparse_swiglu_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(root)):
+        with open(os.path.join(root, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/hbm_traffic_<workload>.md (FETCH_SIZE + WRITE_SIZE
+    per dispatch, scaled by the copy-kernel calibration), or None when absent or taken on other sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_source_digest()
+    for line in open(path):
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 5 and cells[0] == kernel and cells[1] == digest:
+            try:
+                return float(cells[4])
+            except ValueError:
+                return None
+    return None
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
 def cpu_baseline(w, inp, seconds):
@@ -92,6 +137,9 @@ def cpu_baseline(w, inp, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU leg.",
               file=sys.stderr)
@@ -141,19 +189,45 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Headline: the step's launches captured once as a HIP graph and replayed (the library enqueues
+    # kernels only: no host synchronisation, allocation or memset inside a step).
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Per-kernel durations: the same steps launched eagerly, each kernel bracketed by HIP events on its stream.
     kernels = ["select", "fill", "bucket_count", "bucket_scan", "bucket_scatter", "fwd_grouped", "rowsum",
                "bwd_dh_dx", "bwd_dw", "bias_update", "dense_fwd", "dense_route", "dense_rec", "dense_dx",
                "dense_dw"]
     timing = not args.no_kernel_timing
+    eager_ms = None
     if timing:
         E.timing_reset()
         E.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        te = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        eager_ms = 1e3 * (time.perf_counter() - te) / args.steps
     per_kernel = {}
     if timing:
         for k in kernels:
@@ -177,9 +251,12 @@ def main():
         launch_tokens = w.tokens / per_kernel[dom]["launches_per_step"]
         flops = KERNEL_FLOP_UNITS[dom] * launch_tokens * w.k * w.group_size * w.d_model
         achieved = flops / (per_kernel[dom]["avg_us"] * 1e-6) / 1e12
+        traffic = recorded_traffic(w.name, dom)
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                     "flops_per_launch": flops, "avg_launch_us": round(per_kernel[dom]["avg_us"], 2)}
+        if traffic:
+            roofline["traffic_gbs"] = round(traffic / (per_kernel[dom]["avg_us"] * 1e-6) / 1e9, 1)
         # forward + backward kernels only (the counts fill belongs to the selection call)
         fwd_bwd_us = sum(v["us_per_step"] for k, v in per_kernel.items()
                          if k not in ("select", "fill", "bias_update"))
@@ -205,10 +282,13 @@ def main():
                    "bias": w.bias, "bias_update": w.bias_update,
                    "step": ("dense fwd+bwd (recompute)" if w.dense else
                             "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else ""))},
+        "launch": "hip_graph_replay" if graph is not None else "eager",
         "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
         "active_mfma_frac": round(active / (elapsed / args.steps) / 1e12 / peak, 4),
         "roofline": roofline,
     }
+    if eager_ms is not None:
+        line["eager_ms_per_step_with_kernel_events"] = round(eager_ms, 4)
     if fwd_bwd_us:
         line["fwd_bwd_kernel_us"] = round(fwd_bwd_us, 2)
         line["fwd_bwd_tokens_per_s"] = round(w.tokens / (fwd_bwd_us * 1e-6), 1)

@@ -402,11 +402,13 @@ __global__ __launch_bounds__(NT, 1) void dense_dw_kernel(const bf16_t* __restric
   ESG_LDS char* st0 = (ESG_LDS char*)st0_;
   ESG_LDS char* st1 = (ESG_LDS char*)st1_;
   ESG_LDS char* st2 = (ESG_LDS char*)st2_;
-  const int blk = blockIdx.x, db0 = blockIdx.y * 128;
   const int nblk = (F + NB - 1) / NB;
+  DwWork wk;
+  if (!dw_work(blockIdx.x, 2 * nblk, (d + 127) / 128, wk)) return;
+  const int blk = wk.unit >> 1, db0 = wk.db * 128;
   const uint32_t pbytes = (uint32_t)((size_t)nblk * tc_pad * NB * 2);
   const int p0 = blk * tc_pad;
-  if (blockIdx.z == 0)
+  if ((wk.unit & 1) == 0)
     dw2_body<NB, 0, 3, MODE>(x, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fg, fu, dg, du, pbytes, dwg, dwu,
                              db0, st0, st1, st2);
   else
@@ -496,7 +498,7 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
     }
     {
       LaunchTimer timer("dense_dw", stream);
-      const dim3 grid(L.nblk, (d + 127) / 128, 2);
+      const dim3 grid(dw_grid(2 * L.nblk, (d + 127) / 128));  // order: dw_work
       const int mode = L.chunks == 1 ? 0 : (c == 0 ? 1 : (c == L.chunks - 1 ? 3 : 2));
 #define ESG_DW(M)                                                                                                  \
   hipLaunchKernelGGL(dense_dw_kernel<M>, grid, dim3(NT), 0, stream, (const bf16_t*)x, (const bf16_t*)dy, s.tokens, \

@@ -296,8 +296,10 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
   using C = Dw2<GSB>;
   constexpr int NS = stages_for<GSB>();
   __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE], st2_[NS == 3 ? C::STAGE : 16];
-  const int g = blockIdx.x / nsub, s = blockIdx.x % nsub;
-  const int db0 = blockIdx.y * 128;
+  DwWork wk;
+  if (!dw_work(blockIdx.x, 2 * (F / gs) * nsub, (d + 127) / 128, wk)) return;
+  const int g = (wk.unit >> 1) / nsub, s = (wk.unit >> 1) % nsub;
+  const int db0 = wk.db * 128;
   const int nb0 = g * gs + s * GSB;
   const int p0 = tile_off[g] * BM, p1 = tile_off[g + 1] * BM;
   const size_t sub_el = (size_t)s * rows_total * GSB;
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
   ESG_LDS char* st0 = (ESG_LDS char*)st0_;
   ESG_LDS char* st1 = (ESG_LDS char*)st1_;
   ESG_LDS char* st2 = (ESG_LDS char*)st2_;
-  if (blockIdx.z == 0)
+  if ((wk.unit & 1) == 0)
     dw2_body<GSB, 0, NS>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du, pbytes,
                          dwg, dwu, db0, st0, st1, st2);
   else
@@ -345,7 +347,7 @@ hipError_t dw2_t(const FfnShape& s, const void* x, const void* dy, const int32_t
                  int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
                  hipStream_t stream) {
   LaunchTimer timer("bwd_dw", stream);
-  const dim3 grid(s.groups() * s.nsub(), (s.d_model + 127) / 128, 2);
+  const dim3 grid(dw_grid(2 * s.groups() * s.nsub(), (s.d_model + 127) / 128));  // order: dw_work
   hipLaunchKernelGGL((dw2_kernel<GSB>), grid, dim3(NT), 0, stream, (const bf16_t*)x, (const bf16_t*)dy, s.tokens,
                      s.d_model, s.d_ff, s.group_size, s.nsub(), tile_off, ptoken, (uint32_t)rows_total,
                      (const bf16_t*)dg, (const bf16_t*)du, (const bf16_t*)act, (bf16_t*)dwg, (bf16_t*)dwu,

@@ -100,15 +100,20 @@ __device__ __forceinline__ void lds_write8(ESG_LDS char* p, uint32_t lo, uint32_
 }
 
 // ---- N-row tiles -----------------------------------------------------------
+// The transposing read of frag_nrow touches, per 16 lanes, rows 4a..4a+3 of
+// one 8-row group and two neighbouring chunks (per 32 lanes: two 8-row groups
+// of one 16-row half).  The swizzles below send those (row, chunk) pairs to
+// distinct bank groups: rows 0..3 of a group and the group bit 3 select
+// distinct even chunk offsets, so the chunk pair stays disjoint too.
 template <int NCH>
 __device__ __forceinline__ int mn_swz(int k);
 template <>
-__device__ __forceinline__ int mn_swz<16>(int k) {
-  return ((k >> 3) & 3) | ((k & 3) << 2);
+__device__ __forceinline__ int mn_swz<16>(int k) {  // 256-byte rows
+  return ((k & 3) << 1) | (((k >> 3) & 1) << 3) | ((k >> 4) & 1);
 }
 template <>
-__device__ __forceinline__ int mn_swz<8>(int k) {
-  return ((k >> 3) & 3) | (((k >> 1) & 1) << 2);
+__device__ __forceinline__ int mn_swz<8>(int k) {  // 128-byte rows: row parity picks the bank half
+  return (((k & 1) ^ ((k >> 3) & 1)) << 1) | (((k >> 1) & 1) << 2) | ((k >> 4) & 1);
 }
 template <int NCH>
 __device__ __forceinline__ int mnrow_off(int k, int j) {

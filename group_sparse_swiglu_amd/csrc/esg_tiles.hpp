@@ -291,6 +291,25 @@ struct Dw2 {
   static constexpr int FM1 = GSB / 32, FN1 = 4;  // kind 1 wave tile: GSB/2 neurons x 64 d
 };
 
+// Order of the weight-gradient workgroups.  A "unit" is one (neuron block,
+// kind) pair; its ndb d-blocks read the same packed dg/du/a rows.  Workgroup L
+// takes neuron block L % GB, then d-block, then kind (GB = units / 2), so the
+// workgroups in flight together spread over all neuron blocks.  (Keeping one
+// unit's d-blocks together on one XCD measured slower on the 1.3B shapes.)
+// Returns false for workgroups past the last unit.
+struct DwWork {
+  int unit, db;
+};
+__device__ __forceinline__ bool dw_work(int L, int units, int ndb, DwWork& w) {
+  const int GB = units / 2;
+  if (L >= units * ndb) return false;
+  const int gb = L % GB, rest = L / GB;
+  w.db = rest % ndb;
+  w.unit = gb * 2 + rest / ndb;
+  return true;
+}
+inline int dw_grid(int units, int ndb) { return units * ndb; }
+
 template <int MODE>
 __device__ __forceinline__ void store_dw(bf16_t* out, float* acc32, float (&v)[4]) {
   if constexpr (MODE >= 2) {
