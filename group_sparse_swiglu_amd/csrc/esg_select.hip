@@ -11,8 +11,11 @@
 // fewer than k beat it, and its output slot is its rank among the selected ids
 // (a ballot prefix).  Every token's result depends only on its own row: batch
 // invariant and bitwise reproducible.
+#include <type_traits>
+
 #include "esg_device.hpp"
 #include "esg_internal.hpp"
+#include "esg_tiles.hpp"
 
 namespace esg {
 namespace {
@@ -23,28 +26,63 @@ constexpr int KC = 4;  // chunks per K stage
 // BM tokens per workgroup; each wave owns FNW 16-column fragments of a
 // super-chunk of 4*FNW*16 sampled rows, interleaved across the waves, so the
 // x tile is read once per super-chunk.
-template <typename T, int BM, int FNW>
+// bf16 with BM = 32 streams both operands by direct-to-LDS loads into K-row
+// tiles (64 K per stage, DMA_NS stages); other cases stage through registers.
+template <typename T, int BM, int FNW, bool USE_DMA = true>
 struct SelCfg {
   static constexpr int NSC = 4 * FNW * 16;  // sampled rows per super-chunk
   static constexpr int FM = BM / 16;
+  // (with only two stages of the wider super-chunks the staged loop measured faster)
+  static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && BM == 32 && FNW <= 4;
   static constexpr int PA = Plane<BM>::BYTES;
   static constexpr int PB = Plane<NSC>::BYTES;
-  static constexpr int A_BYTES = KC * PA;
-  static constexpr int B_BYTES = KC * PB;
-  static constexpr int STAGES = 2 * (A_BYTES + B_BYTES);
+  static constexpr int A_BYTES = DMA ? BM * 128 : KC * PA;
+  static constexpr int B_BYTES = DMA ? NSC * 128 : KC * PB;
+  static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES) <= 112 * 1024 ? 3 : 2;
+  static constexpr int DMA_L = 1 + NSC / 32;  // loads per lane per stage
+  static constexpr int STAGES = (DMA ? DMA_NS : 2) * (A_BYTES + B_BYTES);
   static constexpr int S_STRIDE = NSC + 1;  // odd float stride: conflict-free column walks
   static constexpr int S_BYTES = BM * S_STRIDE * 4;
   static constexpr int FIXED = STAGES > S_BYTES ? STAGES : S_BYTES;
 };
 
-template <typename T, int BM, int FNW>
+// |SiLU| of one super-chunk's accumulators into S, then per (token, group)
+// sums over the super-chunk's columns, in column order, added to E.
+template <class C, int FM, int FNW>
+__device__ __forceinline__ void select_energy(const f32x4 (&acc)[FM][FNW], float* S, float* E, int ES, int n0,
+                                              int ncols, int rpg, int groups, int lane, const int (&brow)[FNW]) {
+  constexpr int BM = FM * 16;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FNW; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + (lane >> 4) * 4 + e;
+        const float h = acc[i][j][e];
+        S[r * C::S_STRIDE + brow[j]] = fabsf(h * sigmoid_f(h));
+      }
+  __syncthreads();
+  const int g_lo = n0 / rpg;
+  const int g_hi = min(groups - 1, (min(n0 + C::NSC, ncols) - 1) / rpg);
+  const int ng = g_hi - g_lo + 1;
+  for (int p = threadIdx.x; p < BM * ng; p += NT) {
+    const int r = p % BM, g = g_lo + p / BM;
+    const int c0 = max(n0, g * rpg) - n0, c1 = min(n0 + C::NSC, (g + 1) * rpg) - n0;
+    float sum = E[r * ES + g];
+    for (int c = c0; c < c1; ++c) sum += S[r * C::S_STRIDE + c];
+    E[r * ES + g] = sum;
+  }
+}
+
+template <typename T, int BM, int FNW, bool USE_DMA>
 __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, const T* __restrict__ wg,
-                                                     int tokens, int d_model, int groups, int k,
+                                                     int tokens, int d_model, int d_ff, int groups, int k,
                                                      const int32_t* __restrict__ sub, int rpg,
                                                      const float* __restrict__ bias,
                                                      int32_t* __restrict__ idx_out,
                                                      int32_t* __restrict__ counts) {
-  using C = SelCfg<T, BM, FNW>;
+  using C = SelCfg<T, BM, FNW, USE_DMA>;
   extern __shared__ __align__(16) char smem[];
   auto la = [&](int i_) -> char* { return smem + i_ * C::A_BYTES; };
   auto lb = [&](int i_) -> char* { return smem + 2 * C::A_BYTES + i_ * C::B_BYTES; };
@@ -65,17 +103,68 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   }
   for (int i = tid; i < groups; i += NT) cnt[i] = 0;
 
-  RowKLoader<BM, KC, NT> ldA;
-  ldA.init(tid, [&](int r) -> const char* {
-    const int t = t0 + r;
-    return t < tokens ? (const char*)(x + (size_t)t * d_model) : nullptr;
-  });
   int arow[C::FM], brow[FNW];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) arow[i] = i * 16 + (lane & 15);
 #pragma unroll
   for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + wave) * 16 + (lane & 15);
 
+  if constexpr (C::DMA) {
+    ESG_LDS char* st0 = (ESG_LDS char*)smem;
+    const DmaSrc rx = make_dma_src(x, (uint32_t)tokens * kbytes);
+    const DmaSrc rwg = make_dma_src(wg, (uint32_t)d_ff * kbytes);
+    const int w = wave_id();
+    const int c_lane = (lane & 7) ^ (lane >> 3);
+    const int xr = w * 8 + (lane >> 3);
+    const uint32_t voffA = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
+    constexpr int IB = C::NSC / 32;
+    for (int n0 = 0; n0 < ncols; n0 += C::NSC) {
+      uint32_t voffB[IB];
+#pragma unroll
+      for (int i = 0; i < IB; ++i) {
+        const int col = n0 + (w * IB + i) * 8 + (lane >> 3);
+        const int row = col < ncols ? (sub ? sub[col] : col) : -1;
+        voffB[i] = row >= 0 ? (uint32_t)row * kbytes + c_lane * 16 : kOOB;
+      }
+      auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
+        const uint32_t kb = (uint32_t)kt * 128;
+        const bool kin = kb + c_lane * 16 < (uint32_t)kbytes;
+        dma16(rx, st + w * 1024, (kin && voffA != kOOB) ? voffA + kb : kOOB);
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+          dma16(rwg, st + C::A_BYTES + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
+      };
+      f32x4 acc[C::FM][FNW];
+      zero_acc(acc);
+      auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int cc = kb * 4 + (lane >> 4);
+          uint4 a[C::FM], b[FNW];
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i) a[i] = frag_krow(st, arow[i], cc);
+#pragma unroll
+          for (int j = 0; j < FNW; ++j) b[j] = frag_krow(st + C::A_BYTES, brow[j], cc);
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FNW; ++j) mma_bf16(acc[i][j], a[i], b[j]);
+        }
+      };
+      wait_lgkm0();
+      barrier();  // the previous super-chunk's S reads (S aliases the stages) are done
+      constexpr int SB = C::A_BYTES + C::B_BYTES;
+      tiles::kloop<C::DMA_NS, C::DMA_L, 0>((kbytes + 127) / 128, st0, st0 + SB, st0 + 2 * SB, issue, compute);
+      wait_lgkm0();
+      barrier();  // every wave is done with the stages before S overwrites them
+      select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
+    }
+  } else {
+  RowKLoader<BM, KC, NT> ldA;
+  ldA.init(tid, [&](int r) -> const char* {
+    const int t = t0 + r;
+    return t < tokens ? (const char*)(x + (size_t)t * d_model) : nullptr;
+  });
   for (int n0 = 0; n0 < ncols; n0 += C::NSC) {
     RowKLoader<C::NSC, KC, NT> ldB;
     ldB.init(tid, [&](int r) -> const char* {
@@ -104,30 +193,9 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
       }
       __syncthreads();
     }
-    // |SiLU| of the super-chunk into S
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FNW; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = i * 16 + (lane >> 4) * 4 + e;
-          const float h = acc[i][j][e];
-          S[r * C::S_STRIDE + brow[j]] = fabsf(h * sigmoid_f(h));
-        }
-    __syncthreads();
-    // per (token, group) sums over this super-chunk's columns, in column order
-    const int g_lo = n0 / rpg;
-    const int g_hi = min(groups - 1, (min(n0 + C::NSC, ncols) - 1) / rpg);
-    const int ng = g_hi - g_lo + 1;
-    for (int p = tid; p < BM * ng; p += NT) {
-      const int r = p % BM, g = g_lo + p / BM;
-      const int c0 = max(n0, g * rpg) - n0, c1 = min(n0 + C::NSC, (g + 1) * rpg) - n0;
-      float sum = E[r * ES + g];
-      for (int c = c0; c < c1; ++c) sum += S[r * C::S_STRIDE + c];
-      E[r * ES + g] = sum;
-    }
+    select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
     // the next super-chunk's first __syncthreads orders these before S is reused
+  }
   }
   __syncthreads();
 
@@ -184,20 +252,33 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   }
 }
 
-template <typename T, int BM, int FNW>
-hipError_t launch_select_t(const void* x, const void* wg, int tokens, int d_model, int groups, int k,
-                           const int32_t* sub, int rpg, const float* bias, int32_t* idx,
-                           int32_t* counts, hipStream_t stream) {
-  using C = SelCfg<T, BM, FNW>;
+template <typename T, int BM, int FNW, bool USE_DMA>
+hipError_t launch_select_v(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
+                           const int32_t* sub, int rpg, const float* bias, int32_t* idx, int32_t* counts,
+                           hipStream_t stream) {
+  using C = SelCfg<T, BM, FNW, USE_DMA>;
   const size_t smem = C::FIXED + (size_t)BM * (groups | 1) * 4 + (size_t)groups * 4;
-  static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW, USE_DMA>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
   const int blocks = (tokens + BM - 1) / BM;
   LaunchTimer timer("select", stream);
-  hipLaunchKernelGGL((select_kernel<T, BM, FNW>), dim3(blocks), dim3(NT), smem, stream, (const T*)x,
-                     (const T*)wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts);
+  hipLaunchKernelGGL((select_kernel<T, BM, FNW, USE_DMA>), dim3(blocks), dim3(NT), smem, stream, (const T*)x,
+                     (const T*)wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts);
   return hipGetLastError();
+}
+
+// The direct-to-LDS path addresses x and w_gate through 32-bit buffer offsets.
+template <typename T, int BM, int FNW>
+hipError_t launch_select_t(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
+                           const int32_t* sub, int rpg, const float* bias, int32_t* idx, int32_t* counts,
+                           hipStream_t stream) {
+  const unsigned long long kb = (unsigned long long)d_model * sizeof(T);
+  if ((unsigned long long)tokens * kb < (1ull << 31) && (unsigned long long)d_ff * kb < (1ull << 31))
+    return launch_select_v<T, BM, FNW, true>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts,
+                                             stream);
+  return launch_select_v<T, BM, FNW, false>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts,
+                                            stream);
 }
 
 // Fragments per wave: the choice with the least padded MFMA work (ties: wider).
@@ -216,15 +297,16 @@ int pick_fnw(int ncols) {
 }
 
 template <typename T>
-hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int groups, int k, const int32_t* sub,
+hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
+                    const int32_t* sub,
                     int rpg, const float* bias, int32_t* idx, int32_t* counts, hipStream_t st) {
   if (groups > 256)
-    return launch_select_t<T, 16, 8>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+    return launch_select_t<T, 16, 8>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
   switch (pick_fnw(groups * rpg)) {
-    case 2: return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
-    case 4: return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
-    case 6: return launch_select_t<T, 32, 6>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
-    default: return launch_select_t<T, 32, 8>(x, wg, tokens, d_model, groups, k, sub, rpg, bias, idx, counts, st);
+    case 2: return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+    case 4: return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+    case 6: return launch_select_t<T, 32, 6>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+    default: return launch_select_t<T, 32, 8>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
   }
 }
 
@@ -233,16 +315,16 @@ hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int 
 hipError_t launch_select(int dtype, const void* x, const void* w_gate, int tokens, int d_model,
                          int groups, int k, const int32_t* sub, int rows_per_group, int group_size,
                          const float* bias, int32_t* idx_out, int32_t* counts_out, hipStream_t stream) {
-  (void)group_size;
   if (counts_out) {
     hipError_t e = launch_fill_i32(counts_out, 0, (size_t)groups, stream);
     if (e != hipSuccess) return e;
   }
   if (tokens == 0) return hipSuccess;
-  return dtype == 0 ? select_d<float>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group, bias, idx_out,
-                                      counts_out, stream)
-                    : select_d<bf16_t>(x, w_gate, tokens, d_model, groups, k, sub, rows_per_group, bias, idx_out,
-                                       counts_out, stream);
+  const int d_ff = groups * group_size;
+  return dtype == 0 ? select_d<float>(x, w_gate, tokens, d_model, d_ff, groups, k, sub, rows_per_group, bias,
+                                      idx_out, counts_out, stream)
+                    : select_d<bf16_t>(x, w_gate, tokens, d_model, d_ff, groups, k, sub, rows_per_group, bias,
+                                       idx_out, counts_out, stream);
 }
 
 }  // namespace esg
