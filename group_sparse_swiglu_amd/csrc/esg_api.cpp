@@ -1,6 +1,6 @@
 // The C ABI (include/esg.h): argument validation, workspace layout and the
 // launch sequence of each entry point.  No device memory is allocated here.
-#include "../../include/esg.h"
+#include "esg.h"
 
 #include <hip/hip_runtime.h>
 

@@ -109,14 +109,20 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
       }
   };
   int arow2[C::FM2], brow2[C::FN2];
-  uint32_t pbase[C::FN2];
 #pragma unroll
   for (int i = 0; i < C::FM2; ++i) arow2[i] = wm * 64 + i * 16 + (lane & 15);
 #pragma unroll
-  for (int j = 0; j < C::FN2; ++j) {
-    brow2[j] = wn * 64 + j * 16 + (lane & 15);
-    pbase[j] = ptoken[prow0 + brow2[j]] >= 0 ? psub + (prow0 + brow2[j]) * (uint32_t)d * 2 : kOOB;
+  for (int j = 0; j < C::FN2; ++j) brow2[j] = wn * 64 + j * 16 + (lane & 15);
+  using RS = RowStore<DB>;
+  uint32_t row_off[RS::IT];
+#pragma unroll
+  for (int it = 0; it < RS::IT; ++it) {
+    const int r = RS::row(it, threadIdx.x);
+    row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
   }
+  // staging of the output block: stage tails the W_down tiles and the act tile leave free
+  ESG_LDS char* out0 = NS == 3 ? st1 + C::W2_BYTES : st0 + C::ACT_BYTES;
+  ESG_LDS char* out1 = NS == 3 ? st2 + C::W2_BYTES : st1 + C::W2_BYTES;
   auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
     f32x4 acc2[C::FM2][C::FN2];
     zero_acc(acc2);
@@ -133,18 +139,18 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
 #pragma unroll
         for (int j = 0; j < C::FN2; ++j) mma_bf16(acc2[i][j], a[i], b[j]);
     }
-    const int db0 = blk * DB;
 #pragma unroll
-    for (int i = 0; i < C::FM2; ++i) {
-      const int dd = db0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+    for (int i = 0; i < C::FM2; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN2; ++j) {
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
-        store8(rp, (pbase[j] != kOOB && dd < d) ? pbase[j] + dd * 2 : kOOB, v);
+        RS::put(out0, out1, brow2[j], wm * 64 + i * 16 + (lane >> 4) * 4, v);
       }
-    }
+    wait_lgkm0();
+    barrier();  // the whole block is staged
+    RS::flush(out0, out1, rp, row_off, blk * DB, d);
   };
   // st1 and st2 are free (the barrier above); the first step's full wait
   // covers the epilogue stores, and its barrier publishes the act tile
@@ -242,10 +248,16 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
             db0 + jW[i] * 8 < (uint32_t)d ? voffW[i] + db0 * 2 : kOOB);
     }
   };
-  uint32_t pbase[C::FN2];
+  using RS = RowStore<C::DB2>;
+  uint32_t row_off[RS::IT];
 #pragma unroll
-  for (int j = 0; j < C::FN2; ++j)
-    pbase[j] = ptoken[prow0 + brow[j]] >= 0 ? psub + (prow0 + brow[j]) * (uint32_t)d * 2 : kOOB;
+  for (int it = 0; it < RS::IT; ++it) {
+    const int r = RS::row(it, threadIdx.x);
+    row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
+  }
+  // staging of the output block: st0 when the weight tiles use st1/st2, else the stage tails
+  ESG_LDS char* out0 = NS == 3 ? st0 : st0 + C::W2_BYTES;
+  ESG_LDS char* out1 = NS == 3 ? st0 + 64 * RS::RB : st1 + C::W2_BYTES;
   auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
     constexpr int KB = 2 * GSB / 32;
     uint4 a[KB][C::FM2];
@@ -266,18 +278,18 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
 #pragma unroll
         for (int j = 0; j < C::FN2; ++j) mma_bf16(acc2[i][j], a[kb][i], b[j]);
     }
-    const int db0 = blk * C::DB2;
 #pragma unroll
-    for (int i = 0; i < C::FM2; ++i) {
-      const int dd = db0 + wm * 32 + i * 16 + (lane >> 4) * 4;
+    for (int i = 0; i < C::FM2; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN2; ++j) {
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
-        store8(rp, (pbase[j] != kOOB && dd < d) ? pbase[j] + dd * 2 : kOOB, v);
+        RS::put(out0, out1, brow[j], wm * 32 + i * 16 + (lane >> 4) * 4, v);
       }
-    }
+    wait_lgkm0();
+    barrier();  // the whole block is staged
+    RS::flush(out0, out1, rp, row_off, blk * C::DB2, d);
   };
   wait_lgkm0();
   barrier();  // all waves are done with the phase-1 stages

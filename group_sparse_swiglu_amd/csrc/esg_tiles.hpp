@@ -14,11 +14,48 @@ constexpr int BM = kTileRows;  // bucket positions per tile
 constexpr int DB = 128;        // d rows per forward phase-2 block
 
 typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef int v4i32 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void store8(rsrc_t r, uint32_t voff, const float (&v)[4]) {
   const v2i32 q = {(int)pack_bf16x2(v[0], v[1]), (int)pack_bf16x2(v[2], v[3])};
   __builtin_amdgcn_raw_buffer_store_b64(q, r, voff, 0, 0);
 }
+
+// A [128 positions][DW d] bf16 block held as MFMA accumulators (lane: four
+// consecutive d of one position) is written to row-major partial rows through
+// LDS, so that every store instruction writes whole rows (16 bytes per lane,
+// DW*2 bytes per row) instead of 32-byte pieces of 16 rows.  Rows 0..63 are
+// staged in lds0, rows 64..127 in lds1 (DW*2*64 bytes each); 16-byte chunks
+// are XOR-swizzled by row.  row_off[it]: byte offset of the partial row this
+// thread stores at iteration it (kOOB for padding rows).
+template <int DW>
+struct RowStore {
+  static constexpr int RB = DW * 2;       // bytes per staged row
+  static constexpr int NCHK = RB / 16;    // 16-byte chunks per row
+  static constexpr int IT = 128 * NCHK / 256;  // 16-byte stores per thread
+  static __device__ __forceinline__ int row(int it, int tid) { return (it * 256 + tid) / NCHK; }
+  static __device__ __forceinline__ int chunk(int it, int tid) { return (it * 256 + tid) % NCHK; }
+  static __device__ __forceinline__ int off(int rr, int c) { return rr * RB + ((c ^ (rr & (NCHK - 1))) << 4); }
+  // acc value e of a lane: d = dl + e (dl % 4 == 0, dl < DW), position r (0..127)
+  static __device__ __forceinline__ void put(ESG_LDS char* lds0, ESG_LDS char* lds1, int r, int dl,
+                                             const float (&v)[4]) {
+    ESG_LDS char* h = r < 64 ? lds0 : lds1;
+    lds_write8(h + off(r & 63, dl >> 3) + (dl & 7) * 2, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+  // after a barrier: every thread stores IT chunks of 16 bytes
+  static __device__ __forceinline__ void flush(const ESG_LDS char* lds0, const ESG_LDS char* lds1, rsrc_t rp,
+                                               const uint32_t (&row_off)[IT], int db0, int d) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = row(it, tid), c = chunk(it, tid);
+      const u32x4_t q = *(const ESG_LDS u32x4_t*)((r < 64 ? lds0 : lds1) + off(r & 63, c));
+      const int dd = db0 + c * 8;
+      const uint32_t o = (row_off[it] != kOOB && dd < d) ? row_off[it] + dd * 2 : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32, q), rp, o, 0, 0);
+    }
+  }
+};
 
 // Pipeline depth: 3 stages for 128-neuron blocks (one workgroup per CU), 2 for
 // 64-neuron blocks so that two workgroups share a CU.
@@ -92,7 +129,7 @@ struct Fwd2 {
   static constexpr int ACT_BYTES = KSUB * BM * 128;
   static constexpr int W2_BYTES = KSUB * DB * 128;
   static constexpr int FM2 = 4, FN2 = 4;       // phase-2 wave tile 64 d x 64 positions
-  static constexpr int STORES2 = FM2 * FN2;    // buffer stores per lane per d-block
+  static constexpr int STORES2 = RowStore<DB>::IT;  // buffer stores per lane per d-block
   static_assert(ACT_BYTES <= STAGE && W2_BYTES <= STAGE, "phase-2 tiles reuse the stages");
 };
 
@@ -196,7 +233,7 @@ struct Dh2 {
   static constexpr int W2_BYTES = 2 * GSB * DB2 * 2;  // N-row: 2*GSB neuron rows x 64 d
   static constexpr int IW = 2 * GSB / 32;
   static constexpr int FM2 = 2, FN2 = 4;         // wave tile 32 d x 64 positions
-  static constexpr int STORES2 = FM2 * FN2;
+  static constexpr int STORES2 = RowStore<DB2>::IT;
   static constexpr int STAGE = STAGE1 > W2_BYTES ? STAGE1 : W2_BYTES;
 };
 
