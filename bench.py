@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as one HIP graph")
+    ap.add_argument("--inference", action="store_true",
+                    help="forward only (selection + forward, nothing saved): tokens/s of serving steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (reference for the HBM counters)")
     return ap.parse_args()
@@ -172,6 +174,13 @@ def main():
     saved = [None]
 
     def step():
+        if args.inference:
+            if w.dense:
+                E.sparse_swiglu_fwd(X, WG, WU, WD, None, w.group_size, workspace=ws, out=Y, for_backward=False)
+                return
+            E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, out=IDX)
+            E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, for_backward=False)
+            return
         if w.dense:   # every group active: no selection, fused dense forward, recompute backward
             _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, None, w.group_size, workspace=ws, out=Y, saved=saved[0])
             saved[0] = ctx.saved
@@ -241,7 +250,7 @@ def main():
     ms_step = 1e3 * elapsed / args.steps
     tokens_per_s = w.tokens / (elapsed / args.steps)
     unit_flops = float(w.tokens) * w.k * w.group_size * w.d_model
-    active = 18.0 * unit_flops
+    active = (6.0 if args.inference else 18.0) * unit_flops
     peak = PEAK_TFLOPS[w.dtype]
     roofline = None
     fwd_bwd_us = None
@@ -265,7 +274,7 @@ def main():
                              for k, v in per_kernel.items() if k in KERNEL_FLOP_UNITS}
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not args.inference else "sparse SwiGLU forward-only (inference) tokens/s",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -280,7 +289,8 @@ def main():
         "config": {"workload": w.name, "tokens": w.tokens, "d_model": w.d_model, "d_ff": w.d_ff,
                    "group_size": w.group_size, "groups": G, "k": w.k, "samples_per_group": w.spg,
                    "bias": w.bias, "bias_update": w.bias_update,
-                   "step": ("dense fwd+bwd (recompute)" if w.dense else
+                   "step": (("dense fwd" if w.dense else "select+bucket+fwd") + " (inference)" if args.inference
+                            else "dense fwd+bwd (recompute)" if w.dense else
                             "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else ""))},
         "launch": "hip_graph_replay" if graph is not None else "eager",
         "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
@@ -296,7 +306,7 @@ def main():
     if per_kernel:
         line["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in per_kernel.items()}
         line["kernels_algorithmic_tflops"] = {k: round(v, 1) for k, v in line_kernel_flops.items()}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.inference:
         line["cpu_baseline"] = cpu_baseline(w, host_inputs, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

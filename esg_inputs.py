@@ -57,6 +57,9 @@ WORKLOADS = {
     "s1p3b_bf16": Workload("s1p3b_bf16", "bf16", 32768, 2048, 5504, 128, 11, 16, True, False),
     "dense1p3b_bf16": Workload("dense1p3b_bf16", "bf16", 65536, 2048, 5504, 128, 43, None, False, False,
                                dense=True),
+    # forward-only (inference) shapes: one decode step of a batch of 64 sequences, and a 4096-token prefill
+    "decode1p3b_bf16": Workload("decode1p3b_bf16", "bf16", 64, 2048, 5504, 128, 11, 16, True, False),
+    "prefill1p3b_bf16": Workload("prefill1p3b_bf16", "bf16", 4096, 2048, 5504, 128, 11, 16, True, False),
 }
 
 

@@ -195,10 +195,12 @@ def _ws(nbytes: int, dev, cache: Optional[dict], key: str) -> torch.Tensor:
 
 
 def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, status=None, workspace=None,
-                      out=None, saved=None):
+                      out=None, saved=None, for_backward: bool = True):
     """Forward -> (y [T, d], FfnContext).  group_idx None = every group active.
 
-    ``workspace``: optional dict reused across calls to hold scratch buffers."""
+    ``workspace``: optional dict reused across calls to hold scratch buffers.
+    ``for_backward=False``: inference, nothing is saved (the context then cannot
+    be passed to the backward)."""
     T, d = x.shape
     F = w_gate.shape[0]
     code = _dtype_code(x)
@@ -208,13 +210,16 @@ def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, statu
     k = group_idx.shape[1] if group_idx is not None else F // group_size
     sv, fw, _ = workspace_size(T, d, F, group_size, k, code, group_idx is None)
     dev = x.device
-    if saved is None or saved.numel() < sv:
+    if not for_backward:
+        saved = None
+    elif saved is None or saved.numel() < sv:
         saved = torch.empty(max(sv, 256), dtype=torch.uint8, device=dev)
     scratch = _ws(fw, dev, workspace, "fwd")
     y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=dev)
     _check(lib().esg_sparse_swiglu_fwd(
         _dev(x, "x"), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"), code, T, d, F,
-        group_size, k, _dev(group_idx, "group_idx", torch.int32), _dev(y, "y"), _dev(saved, "saved"), saved.numel(),
+        group_size, k, _dev(group_idx, "group_idx", torch.int32), _dev(y, "y"), _dev(saved, "saved"),
+        saved.numel() if saved is not None else 0,
         _dev(scratch, "scratch"), scratch.numel(), _dev(status, "status", torch.int32), _stream(dev)),
         "sparse_swiglu_fwd")
     return y, FfnContext(saved, group_idx, group_size, k)
@@ -222,6 +227,8 @@ def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, statu
 
 def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=None, outs=None):
     """Backward -> (dx, dW_gate, dW_up, dW_down), all overwritten."""
+    if ctx.saved is None and ctx.idx is not None:
+        raise EsgError("the forward ran with for_backward=False: nothing was saved for a backward")
     T, d = x.shape
     F = w_gate.shape[0]
     code = _dtype_code(x)
@@ -236,7 +243,7 @@ def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=No
     _check(lib().esg_sparse_swiglu_bwd(
         _dev(dy, "dy"), _dev(x, "x"), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"), code, T,
         d, F, ctx.group_size, ctx.k, _dev(ctx.idx, "group_idx", torch.int32), _dev(ctx.saved, "saved"),
-        ctx.saved.numel(), _dev(dx, "dx"), _dev(dwg, "dw_gate"), _dev(dwu, "dw_up"), _dev(dwd, "dw_down"),
+        ctx.saved.numel() if ctx.saved is not None else 0, _dev(dx, "dx"), _dev(dwg, "dw_gate"), _dev(dwu, "dw_up"), _dev(dwd, "dw_down"),
         _dev(scratch, "scratch"), scratch.numel(), _stream(dev)), "sparse_swiglu_bwd")
     return dx, dwg, dwu, dwd
 

@@ -47,7 +47,7 @@ struct Layout {
   int mt = 0;            // maximum tiles
   size_t rows = 0;       // padded positions
   size_t offsets = 0, tile_off = 0, tile_group = 0, ptoken = 0, pinv = 0, hg = 0, hu = 0, saved = 0;
-  size_t f_bucket = 0, f_part = 0, fwd = 0;
+  size_t f_bucket = 0, f_part = 0, f_route = 0, fwd = 0;
   size_t b_dg = 0, b_du = 0, b_act = 0, b_part = 0, bwd = 0;
 };
 
@@ -71,6 +71,7 @@ Layout make_layout(const FfnShape& s) {
   o = 0;
   L.f_bucket = o;   o = align256(o + bucket_scratch_bytes(s.tokens, G));
   L.f_part = o;     o = align256(o + part_bytes);
+  L.f_route = o;    o = align256(o + L.hg);  // the routing arrays of `saved`, for saved = NULL (inference)
   L.fwd = o;
   o = 0;
   L.b_dg = o;       o = align256(o + act_bytes);
@@ -194,7 +195,7 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
       if (!aligned16(p)) return ESG_ERR_INVALID_ARG;
     return hip_status(launch_dense_fwd(s, x, w_gate, w_up, w_down, y, (hipStream_t)stream));
   }
-  if (saved == nullptr || scratch == nullptr) return ESG_ERR_INVALID_ARG;
+  if (scratch == nullptr) return ESG_ERR_INVALID_ARG;
   if (k > kMaxK) return ESG_ERR_UNSUPPORTED;
   if (tokens > 0 && (x == nullptr || y == nullptr)) return ESG_ERR_INVALID_ARG;
   for (const void* p : {x, w_gate, w_up, w_down, (const void*)y, (const void*)idx, (const void*)saved,
@@ -202,18 +203,22 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
     if (!aligned16(p)) return ESG_ERR_INVALID_ARG;
   const FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
   const Layout L = make_layout(s);
-  if (saved_bytes < L.saved || scratch_bytes < L.fwd) return ESG_ERR_WORKSPACE;
+  const bool train = saved != nullptr;  // NULL: forward only, the routing lives in the scratch
+  if ((train && saved_bytes < L.saved) || scratch_bytes < L.fwd) return ESG_ERR_WORKSPACE;
+  void* route = train ? saved : at<char>(scratch, L.f_route);
   hipStream_t stream_h = (hipStream_t)stream;
-  BucketOut out{at<int32_t>(saved, L.offsets), nullptr, nullptr, at<int32_t>(saved, L.tile_off),
-                at<int32_t>(saved, L.tile_group), at<int32_t>(saved, L.ptoken), at<int32_t>(saved, L.pinv),
+  BucketOut out{at<int32_t>(route, L.offsets), nullptr, nullptr, at<int32_t>(route, L.tile_off),
+                at<int32_t>(route, L.tile_group), at<int32_t>(route, L.ptoken), at<int32_t>(route, L.pinv),
                 status_dev};
   hipError_t e = launch_bucket(idx, tokens, k, s.groups(), kTileRows, out, at<char>(scratch, L.f_bucket), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
+  char* hg = train ? at<char>(saved, L.hg) : nullptr;
+  char* hu = train ? at<char>(saved, L.hu) : nullptr;
   e = bf16_pipelined(s, L.mt)
-          ? launch_fwd2(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, at<char>(saved, L.hg),
-                        at<char>(saved, L.hu), at<char>(scratch, L.f_part), stream_h)
-          : launch_fwd_grouped(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, at<char>(saved, L.hg),
-                               at<char>(saved, L.hu), at<char>(scratch, L.f_part), stream_h);
+          ? launch_fwd2(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, hg, hu,
+                        at<char>(scratch, L.f_part), stream_h)
+          : launch_fwd_grouped(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, hg, hu,
+                               at<char>(scratch, L.f_part), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
   e = launch_rowsum(s, at<char>(scratch, L.f_part), L.rows, out.pinv, y, stream_h);
   return hip_status(e);

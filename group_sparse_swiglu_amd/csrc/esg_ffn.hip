@@ -157,8 +157,10 @@ __global__ __launch_bounds__(NT) void fwd_grouped_kernel(
         hu[e] = acc[i][C::FP1 + p][e];
       }
       const size_t q = sub_off + packed_index<T>(prow0 + r0, n, GSB);
-      Quad<T>::store(hg_saved + q, hg);
-      Quad<T>::store(hu_saved + q, hu);
+      if (hg_saved != nullptr) {  // NULL: inference, nothing kept for a backward
+        Quad<T>::store(hg_saved + q, hg);
+        Quad<T>::store(hu_saved + q, hu);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a = hg[e] * sigmoid_f(hg[e]) * hu[e];

@@ -79,8 +79,10 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
         a[e] = hg[e] * sigmoid_f(hg[e]) * hu[e];
       }
       const uint32_t so = sub_off + ((prow0 + r) * GSB + n) * 2;
-      store8(rsv_g, so, hg);
-      store8(rsv_u, so, hu);
+      if (hg_saved != nullptr) {  // NULL: inference, nothing kept for a backward
+        store8(rsv_g, so, hg);
+        store8(rsv_u, so, hu);
+      }
       lds_write8(act + (n >> 6) * BM * 128 + krow_off(r, (n & 63) >> 3) + (n & 7) * 2, pack_bf16x2(a[0], a[1]),
                  pack_bf16x2(a[2], a[3]));
     }

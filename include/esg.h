@@ -139,6 +139,9 @@ int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int grou
  * overwritten.  The gated activation of a group never leaves the chip; the k
  * per-token contributions are summed in slot order without atomics, so the
  * result is bitwise reproducible.  status_dev: as in esg_bucket_by_group.
+ * saved = NULL selects inference (forward only): nothing is kept for a
+ * backward, the routing is held in the scratch instead (fwd_scratch_bytes
+ * covers it), and y is bitwise the same as with saved given.
  *
  * Dense limit: idx = NULL with k = G means every group is active, i.e. the
  * plain SwiGLU block (the README's layer with all groups selected).  It runs
