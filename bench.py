@@ -50,6 +50,8 @@ def parse():
                     help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--inference", action="store_true",
                     help="forward only (selection + forward, nothing saved): tokens/s of serving steps")
+    ap.add_argument("--routing", default=None, metavar="WORKLOAD",
+                    help="time sigmoid top-k routing on a routing workload (route_e256_k8, route_e43_k11) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (reference for the HBM counters)")
     return ap.parse_args()
@@ -137,6 +139,107 @@ def cpu_baseline(w, inp, seconds):
                       f"{'+bias update' if w.bias_update else ''}), {el:.1f} s"}
 
 
+def routing_cpu_baseline(logits, bias, k, scaling, seconds):
+    """The routing oracle (as it stands: a Python loop over rows, one core)
+    on consecutive rows of the same logits until `seconds` have passed."""
+    from oracle import routing_oracle as R
+    ln, bn = logits.numpy(), bias.numpy()
+    rows, done, t0 = 256, 0, time.perf_counter()
+    while True:
+        s0 = done % ln.shape[0]
+        R.sigmoid_topk_routing(ln[s0:s0 + rows], bn, k, scaling)
+        done += min(rows, ln.shape[0] - s0)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows of the same logits in slices of {rows}, {el:.1f} s"}
+
+
+def routing_main(args):
+    """Sigmoid top-k routing alone: one launch per step over [tokens, experts]
+    fp32 logits resident in HBM."""
+    import torch
+    import esg_inputs as I
+    import group_sparse_swiglu_amd as E
+
+    w = I.ROUTING_WORKLOADS[args.routing]
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    E.lib()
+    logits, bias = I.make_routing_inputs(w.tokens, w.experts, seed=0)
+    L, B = logits.to(dev), bias.to(dev)
+    P = torch.empty(w.tokens, w.k, dtype=torch.float32, device=dev)
+    IX = torch.empty(w.tokens, w.k, dtype=torch.int64, device=dev)
+
+    def step():
+        E.sigmoid_topk_routing(L, B, w.k, w.scaling, out=(P, IX))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay() if graph is not None else step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+
+    roofline = None
+    if not args.no_kernel_timing:
+        E.timing_reset()
+        E.timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms, n = E.timing_read("sigmoid_topk")
+        E.timing_enable(False)
+        E.timing_reset()
+        avg_us = 1e3 * ms / n
+        # algorithmic bytes: read the logits and the bias, write fp32 weights and int64 indices
+        nbytes = w.tokens * (w.experts * 4 + w.k * 12) + w.experts * 4
+        achieved = nbytes / (avg_us * 1e-6) / 1e9
+        roofline = {"kernel": "sigmoid_topk", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4),
+                    "traffic": recorded_traffic(w.name, "sigmoid_topk"), "bytes_per_launch": nbytes,
+                    "avg_launch_us": round(avg_us, 2)}
+    line = {
+        "metric": "sigmoid top-k routing tokens/s",
+        "value": round(w.tokens / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "experts": w.experts, "k": w.k,
+                   "scaling_factor": w.scaling, "step": "sigmoid top-k routing"},
+        "launch": "hip_graph_replay" if graph is not None else "eager",
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = routing_cpu_baseline(logits, bias, w.k, w.scaling, min(args.cpu_seconds, 10.0))
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -146,6 +249,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU leg.",
               file=sys.stderr)
         sys.exit(2)
+    if args.routing:
+        routing_main(args)
+        return
 
     import torch
     import esg_inputs as I

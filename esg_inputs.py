@@ -110,3 +110,43 @@ def random_group_idx(tokens: int, groups: int, k: int, seed: int = 0) -> torch.T
     scores = torch.rand(tokens, groups, generator=g)
     idx = torch.topk(scores, k, dim=1).indices
     return torch.sort(idx, dim=1).values.to(torch.int32)
+
+
+# ---------------------------------------------------------------------------
+# Router logits for sigmoid top-k routing.  Recipe: one CPU generator seeded
+# with ``seed``; logits ~ N(0, 1) * scale drawn first, then the expert bias
+# ~ U(-0.1, 0.1), both fp32.  ``levels`` > 0 instead draws integer logits in
+# [0, levels) (many exact ties), and ``saturate`` adds +-30 to half the logits
+# (scores that round to 0 or 1 in fp32, more ties).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class RoutingWorkload:
+    name: str
+    tokens: int
+    experts: int
+    k: int
+    scaling: Optional[float]
+
+
+ROUTING_WORKLOADS = {
+    # DeepSeek-V3-style expert-bias routing: 256 experts, 8 active, scaling 2.5
+    "route_e256_k8": RoutingWorkload("route_e256_k8", 65536, 256, 8, 2.5),
+    # the 1.3B group shape of the sparse layer: 43 groups, 11 active
+    "route_e43_k11": RoutingWorkload("route_e43_k11", 32768, 43, 11, None),
+}
+
+
+def make_routing_inputs(tokens: int, experts: int, seed: int = 0, scale: float = 1.0, levels: int = 0,
+                        saturate: bool = False):
+    g = torch.Generator().manual_seed(seed)
+    if levels > 0:
+        logits = torch.randint(0, levels, (tokens, experts), generator=g).float()
+    else:
+        logits = torch.randn(tokens, experts, generator=g) * scale
+    bias = torch.rand(experts, generator=g) * 0.2 - 0.1
+    if saturate:
+        sign = torch.randint(0, 2, (tokens, experts), generator=g).float() * 2 - 1
+        half = torch.rand(tokens, experts, generator=g) < 0.5
+        logits = torch.where(half, logits + 30.0 * sign, logits)
+    return logits.contiguous(), bias.contiguous()

@@ -7,7 +7,8 @@ or no GPU is present, the calls raise.
 
 Names follow the eugen_sparse README ("What it does"): make_subsample_index,
 grouped_topk_select, sparse_swiglu_ffn (forward + backward),
-update_load_balance_bias.
+update_load_balance_bias; and, from the Megatron-Core developer guide page
+"core.inference.moe.sigmoid_topk", sigmoid_topk_routing.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ __all__ = [
     "ESG_F32", "ESG_BF16", "EsgError", "lib", "library_path", "make_subsample_index", "grouped_topk_select",
     "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn", "update_load_balance_bias",
     "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
-    "FfnContext", "EXPORTED_SYMBOLS",
+    "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
 ]
 
 ESG_F32 = 0
@@ -57,6 +58,9 @@ _SIGNATURES = {
     "esg_update_load_balance_bias": (_c_int, [_c_vp, _c_vp, _c_vp, _c_f, _c_f, _c_f, _c_f, _c_int, _c_vp]),
     "esg_update_load_balance_bias_from_counts": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_f, _c_f, _c_f, _c_f,
                                                           _c_int, _c_vp]),
+    "esg_sigmoid_topk_supported": (_c_int, [_c_int, _c_int]),
+    "esg_sigmoid_topk_routing": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_vp, _c_vp,
+                                          _c_vp]),
     "esg_timing_enable": (_c_int, [_c_int]),
     "esg_timing_reset": (_c_int, []),
     "esg_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]),
@@ -286,6 +290,41 @@ def update_load_balance_bias_from_counts(bias, freq_ema, counts, tokens: int, ta
         _dev(bias, "bias", torch.float32), _dev(freq_ema, "freq_ema", torch.float32),
         _dev(counts, "counts", torch.int32), tokens, target_freq, gamma, bias_max, momentum, G,
         _stream(bias.device)), "update_load_balance_bias_from_counts")
+
+
+def sigmoid_topk_supported(num_experts: int, topk: int) -> bool:
+    """Whether the routing kernel takes this shape (1 <= topk <= min(32, E), E <= 2048)."""
+    return bool(lib().esg_sigmoid_topk_supported(num_experts, topk))
+
+
+def sigmoid_topk_routing(logits, expert_bias, topk: int, scaling_factor: Optional[float] = None, out=None):
+    """Top-k of sigmoid(logits) + bias per row; weights from sigmoid(logits),
+    normalised by their left-folded sum (+1e-20) and optionally scaled.
+
+    logits: float32 [T, E] contiguous GPU tensor; expert_bias: float32 [E]
+    (a strided view is accepted).  Returns (probs float32 [T, k], indices
+    int64 [T, k]); ``out`` may supply both."""
+    if logits.dim() != 2:
+        raise EsgError("logits must be [tokens, num_experts]")
+    T, E = logits.shape
+    if expert_bias.dim() != 1 or expert_bias.shape[0] != E or expert_bias.dtype != torch.float32:
+        raise EsgError("expert_bias must be float32 [num_experts]")
+    if not expert_bias.is_cuda or expert_bias.device != logits.device:
+        raise EsgError("expert_bias must be on the logits' GPU")
+    stride = expert_bias.stride(0) if E > 1 else 1
+    if stride < 1:
+        raise EsgError("expert_bias must have a positive stride")
+    if out is None:
+        probs = torch.empty(T, topk, dtype=torch.float32, device=logits.device)
+        indices = torch.empty(T, topk, dtype=torch.int64, device=logits.device)
+    else:
+        probs, indices = out
+    _check(lib().esg_sigmoid_topk_routing(
+        _dev(logits, "logits", torch.float32), expert_bias.data_ptr(), stride, T, E, topk,
+        1.0 if scaling_factor is None else float(scaling_factor), int(scaling_factor is not None),
+        _dev(probs, "probs", torch.float32), _dev(indices, "indices", torch.int64), _stream(logits.device)),
+        "sigmoid_topk_routing")
+    return probs, indices
 
 
 def timing_enable(on: bool = True) -> None:

@@ -301,6 +301,22 @@ int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const
                                        momentum, groups, (hipStream_t)stream));
 }
 
+int esg_sigmoid_topk_supported(int num_experts, int topk) { return sigmoid_topk_supported(num_experts, topk) ? 1 : 0; }
+
+int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int bias_stride, int tokens,
+                             int num_experts, int topk, float scaling_factor, int apply_scaling, float* probs,
+                             int64_t* indices, void* stream) {
+  if (tokens < 0 || bias_stride < 1) return ESG_ERR_INVALID_ARG;
+  if (!sigmoid_topk_supported(num_experts, topk)) return ESG_ERR_UNSUPPORTED;
+  if ((size_t)tokens * topk >= (1ull << 31) || (size_t)tokens * num_experts >= (1ull << 40))
+    return ESG_ERR_UNSUPPORTED;
+  if (tokens == 0) return ESG_OK;
+  if (logits == nullptr || expert_bias == nullptr || probs == nullptr || indices == nullptr)
+    return ESG_ERR_INVALID_ARG;
+  return hip_status(launch_sigmoid_topk(logits, expert_bias, bias_stride, tokens, num_experts, topk, scaling_factor,
+                                        apply_scaling, probs, indices, (hipStream_t)stream));
+}
+
 int esg_timing_enable(int on) {
   timing_set(on != 0);
   return ESG_OK;

@@ -103,4 +103,12 @@ hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const 
                               int groups, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stream);
 
+// ---- sigmoid top-k routing (esg_route.hip) ------------------------------------
+constexpr int kRouteMaxExperts = 2048;  // 32 experts per lane of one wavefront
+constexpr int kRouteMaxK = 32;
+bool sigmoid_topk_supported(int num_experts, int topk);
+hipError_t launch_sigmoid_topk(const float* logits, const float* bias, int bias_stride, int tokens, int E, int k,
+                               float scaling, int apply_scaling, float* probs, int64_t* indices,
+                               hipStream_t stream);
+
 }  // namespace esg

@@ -198,6 +198,39 @@ int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const
                                              void* stream);
 
 /*
+ * Sigmoid top-k routing with an expert bias (Megatron-Core developer guide,
+ * "core.inference.moe.sigmoid_topk": the description of _sigmoid_topk_kernel
+ * and the API of sigmoid_topk_routing).  Per token row t and expert e:
+ *   s[t,e]   = sigmoid(logits[t,e]), the fp64 value rounded once to fp32;
+ *   key[t,e] = s[t,e] + expert_bias[e * bias_stride]   (one fp32 addition).
+ * The row's k-th largest key is taken in the total order of fp32 values
+ * (-0.0 below +0.0); indices[t] lists the experts whose key is above it in
+ * ascending expert order, then the experts whose key equals it in ascending
+ * order, k in all.  The weights use the unbiased scores:
+ *   probs[t,j] = s[t,i_j] / ((((s_0 + s_1) + s_2) + ...) + 1e-20f),
+ * the sum folded left in output order, then times scaling_factor if
+ * apply_scaling != 0; every operation is a separately rounded fp32 one.
+ * The bias serves the selection only.  Rows are independent and the launch
+ * does not depend on `tokens`, so each row's result is independent of the
+ * batch (bitwise).
+ *
+ * logits: device float [tokens, num_experts] row-major (finite values);
+ * expert_bias: device float, element e at expert_bias[e * bias_stride]
+ * (bias_stride >= 1; finite values); probs: device float [tokens, topk];
+ * indices: device int64 [tokens, topk].  Both outputs are overwritten.
+ * tokens == 0 enqueues nothing.
+ * Errors: ESG_ERR_INVALID_ARG (null pointer with tokens > 0, tokens < 0,
+ * bias_stride < 1), ESG_ERR_UNSUPPORTED (shape outside
+ * esg_sigmoid_topk_supported, or tokens * topk >= 2^31).
+ * esg_sigmoid_topk_supported returns 1 when 1 <= topk <= min(32,
+ * num_experts) and num_experts <= 2048, else 0.
+ */
+int esg_sigmoid_topk_supported(int num_experts, int topk);
+int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int bias_stride, int tokens,
+                             int num_experts, int topk, float scaling_factor, int apply_scaling, float* probs,
+                             int64_t* indices, void* stream);
+
+/*
  * Kernel timing (instrumentation, off by default).  When enabled, every
  * kernel the library launches is bracketed by HIP events recorded on the
  * launch stream.  esg_timing_read synchronises on the recorded events and

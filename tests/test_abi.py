@@ -110,3 +110,19 @@ def test_timing_api_without_launches():
     E.timing_enable(True)
     assert E.timing_read("fwd_grouped") == (0.0, 0)
     E.timing_enable(False)
+
+
+def test_sigmoid_topk_argument_checks():
+    lib = E.lib()
+    assert lib.esg_sigmoid_topk_supported(256, 8) == 1
+    assert lib.esg_sigmoid_topk_supported(2048, 32) == 1
+    assert lib.esg_sigmoid_topk_supported(43, 11) == 1
+    for e, k in ((2049, 8), (8, 33), (4, 5), (4, 0), (0, 1)):
+        assert lib.esg_sigmoid_topk_supported(e, k) == 0
+    null = None
+    # tokens == 0 enqueues nothing and needs no buffers
+    assert lib.esg_sigmoid_topk_routing(null, null, 1, 0, 256, 8, 1.0, 0, null, null, null) == 0
+    assert lib.esg_sigmoid_topk_routing(null, null, 1, -1, 256, 8, 1.0, 0, null, null, null) == 1
+    assert lib.esg_sigmoid_topk_routing(null, null, 0, 4, 256, 8, 1.0, 0, null, null, null) == 1
+    assert lib.esg_sigmoid_topk_routing(null, null, 1, 4, 256, 40, 1.0, 0, null, null, null) == 2
+    assert lib.esg_sigmoid_topk_routing(null, null, 1, 4, 256, 8, 1.0, 0, null, null, null) == 1
