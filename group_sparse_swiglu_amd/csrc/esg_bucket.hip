@@ -62,22 +62,46 @@ __global__ __launch_bounds__(TB) void bucket_count_kernel(const int32_t* __restr
   for (int g = threadIdx.x; g < groups; g += TB) bc[(size_t)blockIdx.x * groups + g] = hist[g];
 }
 
-// Block-wide exclusive scan of one int per thread (NTS threads).
-template <int NTS>
-__device__ int block_exclusive_scan(int v, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < NTS; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+// Inclusive prefix sum across a wavefront (64 lanes).
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
   }
-  const int incl = buf[tid];
-  *total = buf[NTS - 1];
+  return v;
+}
+
+// Block-wide exclusive scans of two ints per thread (NTS threads, a multiple
+// of 64): wavefront scans, then a scan of the wavefront totals by wavefront 0.
+// Two barriers.
+template <int NTS>
+__device__ void block_exclusive_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb, int* wsum) {
+  constexpr int NW = NTS / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ia = wave_inclusive_scan(a, lane), ib = wave_inclusive_scan(b, lane);
+  if (lane == 63) {
+    wsum[w] = ia;
+    wsum[NW + w] = ib;
+  }
   __syncthreads();
-  return incl - v;
+  if (w == 0) {
+    const int va = lane < NW ? wsum[lane] : 0, vb = lane < NW ? wsum[NW + lane] : 0;
+    const int sa = wave_inclusive_scan(va, lane), sb = wave_inclusive_scan(vb, lane);
+    if (lane < NW) {
+      wsum[2 * NW + lane] = sa - va;  // exclusive wavefront bases
+      wsum[3 * NW + lane] = sb - vb;
+    }
+    if (lane == NW - 1) {
+      wsum[4 * NW] = sa;
+      wsum[4 * NW + 1] = sb;
+    }
+  }
+  __syncthreads();
+  ea = wsum[2 * NW + w] + ia - a;
+  eb = wsum[3 * NW + w] + ib - b;
+  ta = wsum[4 * NW];
+  tb = wsum[4 * NW + 1];
 }
 
 constexpr int SCAN_NT = 1024;
@@ -92,7 +116,7 @@ __global__ __launch_bounds__(SCAN_NT) void bucket_scan_kernel(int nblocks, int g
                                                               int32_t* __restrict__ pbase,
                                                               int32_t* offsets, int32_t* tile_off,
                                                               int32_t* tile_group, int32_t* ptoken) {
-  __shared__ int buf[SCAN_NT];
+  __shared__ int wsum[4 * (SCAN_NT / 64) + 2];
   __shared__ int part[SCAN_NT];     // [slice][group] sums, then exclusive prefix over slices
   __shared__ int g_off[SCAN_NT + 1], g_toff[SCAN_NT + 1];
   const int tid = threadIdx.x;
@@ -115,10 +139,9 @@ __global__ __launch_bounds__(SCAN_NT) void bucket_scan_kernel(int nblocks, int g
     }
   }
   __syncthreads();
-  int total = 0, total_tiles = 0;
-  const int off = block_exclusive_scan<SCAN_NT>(tid < groups ? n : 0, buf, &total);
+  int total = 0, total_tiles = 0, off = 0, toff = 0;
   const int nt = tid < groups ? (n + tile_rows - 1) / tile_rows : 0;
-  const int toff = block_exclusive_scan<SCAN_NT>(nt, buf, &total_tiles);
+  block_exclusive_scan2<SCAN_NT>(tid < groups ? n : 0, nt, off, toff, total, total_tiles, wsum);
   if (tid < groups) {
     g_off[tid] = off;
     g_toff[tid] = toff;
@@ -180,7 +203,14 @@ __global__ __launch_bounds__(TB) void bucket_scatter_kernel(const int32_t* __res
   uint32_t* mask = sm + lane * gw;
   int* rk = (int*)(sm + TB * gw) + lane * k;  // rank of this token among the block's
                                               // tokens of its i-th smallest group
+  int* sbase = (int*)(sm + TB * gw) + TB * k;  // the block's bases: [G] CSR, then [G] padded
   for (int i = 0; i < gw; ++i) mask[i] = 0;
+  const size_t brow = (size_t)blockIdx.x * groups;
+  for (int g = lane; g < groups; g += TB) {
+    sbase[g] = base[brow + g];
+    sbase[groups + g] = pbase[brow + g];
+  }
+  __syncthreads();
   const int t = blockIdx.x * TB + lane;
   const int32_t* row = idx + (size_t)t * k;
   int bits = 0;
@@ -197,7 +227,6 @@ __global__ __launch_bounds__(TB) void bucket_scatter_kernel(const int32_t* __res
   if (t >= tokens) return;
   // outputs per slot; a slot is valid when it is the first occurrence of an
   // in-range id (the same rule as the count pass)
-  const size_t brow = (size_t)blockIdx.x * groups;
   for (int j = 0; j < k; ++j) {
     const int g = row[j];
     bool valid = g >= 0 && g < groups;
@@ -214,8 +243,8 @@ __global__ __launch_bounds__(TB) void bucket_scatter_kernel(const int32_t* __res
       continue;
     }
     const int r = rk[order];
-    const int pos = base[brow + g] + r;
-    const int ppos = pbase[brow + g] + r;
+    const int pos = sbase[g] + r;
+    const int ppos = sbase[groups + g] + r;
     if (perm_token) perm_token[pos] = t;
     if (inv) inv[o] = pos;
     if (ptoken) ptoken[ppos] = t;
@@ -260,7 +289,7 @@ hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int 
   }
   if (nb > 0) {
     LaunchTimer timer("bucket_scatter", stream);
-    const size_t smem = (size_t)TB * gw * 4 + (size_t)TB * k * 4;
+    const size_t smem = (size_t)TB * gw * 4 + (size_t)TB * k * 4 + (size_t)groups * 8;
     hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nb), dim3(TB), smem, stream, idx, tokens, k, groups, base,
                        pbase, out.perm_token, out.inv, out.ptoken, out.pinv);
     hipError_t e = hipGetLastError();
