@@ -150,3 +150,36 @@ def make_routing_inputs(tokens: int, experts: int, seed: int = 0, scale: float =
         half = torch.rand(tokens, experts, generator=g) < 0.5
         logits = torch.where(half, logits + 30.0 * sign, logits)
     return logits.contiguous(), bias.contiguous()
+
+
+# ---------------------------------------------------------------------------
+# LeakyReLU(0.5)-squared MLP.  Recipe: one CPU generator seeded with ``seed``;
+# fp32 draws in the order x ~ N(0, 1), W_up ~ N(0, 1/d_model),
+# W_down ~ N(0, 1/d_ff), dy ~ N(0, 1); then cast to bf16.
+# The shape follows the parameter-golf pull request 1105 architecture table
+# (d_model 512, MLP 3.5x = 1792); the token count is chosen so that one bf16
+# [tokens, 1792] intermediate is about the 302 MB that page quotes
+# (86016 = 42 sequences of 2048 tokens: 308 MB).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MlpWorkload:
+    name: str
+    tokens: int
+    d_model: int
+    d_ff: int
+
+
+MLP_WORKLOADS = {
+    "leaky_mlp_d512": MlpWorkload("leaky_mlp_d512", 86016, 512, 1792),
+}
+
+
+def make_mlp_inputs(tokens: int, d_model: int, d_ff: int, seed: int = 0, dtype: str = "bf16"):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(tokens, d_model, generator=g)
+    w_up = torch.randn(d_ff, d_model, generator=g) / d_model ** 0.5
+    w_down = torch.randn(d_model, d_ff, generator=g) / d_ff ** 0.5
+    dy = torch.randn(tokens, d_model, generator=g)
+    td = torch_dtype(dtype)
+    return tuple(t.to(td).contiguous() for t in (x, w_up, w_down, dy))
