@@ -52,6 +52,8 @@ def parse():
                     help="forward only (selection + forward, nothing saved): tokens/s of serving steps")
     ap.add_argument("--routing", default=None, metavar="WORKLOAD",
                     help="time sigmoid top-k routing on a routing workload (route_e256_k8, route_e43_k11) instead")
+    ap.add_argument("--mlp", default=None, metavar="WORKLOAD",
+                    help="time the LeakyReLU(0.5)^2 MLP fwd+bwd on an MLP workload (leaky_mlp_d512) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (reference for the HBM counters)")
     return ap.parse_args()
@@ -240,6 +242,132 @@ def routing_main(args):
     print(json.dumps(line), flush=True)
 
 
+MLP_KERNELS = ("mlp_up_act", "mlp_down", "mlp_dpre", "mlp_dx", "mlp_dw_down", "mlp_dw_up", "mlp_dw_reduce")
+
+
+def mlp_cpu_baseline(x, wu, wd, dy, seconds):
+    """The MLP oracle (fp64 numpy, as it stands) on consecutive token slices
+    of the same inputs until `seconds` have passed: forward and backward."""
+    import numpy as np
+    from oracle import mlp_oracle as M
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 0) for p in threadpool_info()] or [0]) or os.cpu_count()
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    W = (f64(wu), f64(wd))
+    rows, done, t0 = 512, 0, time.perf_counter()
+    while True:
+        s0 = done % x.shape[0]
+        xs, dys = f64(x[s0:s0 + rows]), f64(dy[s0:s0 + rows])
+        _, post, ag = M.mlp_forward(xs, *W)
+        M.mlp_backward(dys, xs, *W, post, ag)
+        done += xs.shape[0]
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done / el, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} tokens in slices of {rows} (fp64 fwd+bwd), {el:.1f} s"}
+
+
+def mlp_main(args):
+    """LeakyReLU(0.5)^2 MLP: forward (fused up projection + activation, down
+    projection) and backward (fused dpre, dx, both weight gradients) per step."""
+    import torch
+    import esg_inputs as I
+    import group_sparse_swiglu_amd as E
+
+    w = I.MLP_WORKLOADS[args.mlp]
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    E.lib()
+    x, wu, wd, dy = I.make_mlp_inputs(w.tokens, w.d_model, w.d_ff, seed=0)
+    X, WU, WD, DY = (t.to(dev) for t in (x, wu, wd, dy))
+    sv, _ = E.leaky_mlp_workspace_size(w.tokens, w.d_model, w.d_ff)
+    SAVED = torch.empty(sv, dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(X)
+    GR = (torch.empty_like(X), torch.empty_like(WU), torch.empty_like(WD))
+    ws = {}
+
+    def step():
+        E.leaky_mlp_fwd(X, WU, WD, out=Y, saved=SAVED)
+        E.leaky_mlp_bwd(DY, X, WU, WD, SAVED, workspace=ws, outs=GR)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay() if graph is not None else step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+    gemm_flops = 2.0 * w.tokens * w.d_model * w.d_ff
+    active = 6 * gemm_flops
+    peak = PEAK_TFLOPS["bf16"]
+    per_kernel, roofline = {}, None
+    if not args.no_kernel_timing:
+        E.timing_reset()
+        E.timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        for k in MLP_KERNELS:
+            ms, n = E.timing_read(k)
+            if n:
+                per_kernel[k] = {"avg_us": 1e3 * ms / n, "us_per_step": 1e3 * ms / args.steps}
+        E.timing_enable(False)
+        E.timing_reset()
+        gemms = [k for k in per_kernel if k != "mlp_dw_reduce"]
+        dom = max(gemms, key=lambda k: per_kernel[k]["us_per_step"])
+        achieved = gemm_flops / (per_kernel[dom]["avg_us"] * 1e-6) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": recorded_traffic(w.name, dom),
+                    "flops_per_launch": gemm_flops, "avg_launch_us": round(per_kernel[dom]["avg_us"], 2)}
+    line = {
+        "metric": "LeakyReLU(0.5)^2 MLP fwd+bwd tokens/s",
+        "value": round(w.tokens / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "d_model": w.d_model, "d_ff": w.d_ff,
+                   "step": "up+act, down, dpre, dx, dW_down, dW_up"},
+        "launch": "hip_graph_replay" if graph is not None else "eager",
+        "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
+        "active_mfma_frac": round(active / (elapsed / args.steps) / 1e12 / peak, 4),
+        "roofline": roofline,
+    }
+    if per_kernel:
+        line["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in per_kernel.items()}
+        line["kernels_algorithmic_tflops"] = {k: round(gemm_flops / (v["avg_us"] * 1e-6) / 1e12, 1)
+                                              for k, v in per_kernel.items() if k != "mlp_dw_reduce"}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = mlp_cpu_baseline(x, wu, wd, dy, min(args.cpu_seconds, 10.0))
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -251,6 +379,9 @@ def main():
         sys.exit(2)
     if args.routing:
         routing_main(args)
+        return
+    if args.mlp:
+        mlp_main(args)
         return
 
     import torch

@@ -8,7 +8,9 @@ or no GPU is present, the calls raise.
 Names follow the eugen_sparse README ("What it does"): make_subsample_index,
 grouped_topk_select, sparse_swiglu_ffn (forward + backward),
 update_load_balance_bias; and, from the Megatron-Core developer guide page
-"core.inference.moe.sigmoid_topk", sigmoid_topk_routing.
+"core.inference.moe.sigmoid_topk", sigmoid_topk_routing; and, from the
+parameter-golf pull request 1105 page, the LeakyReLU(0.5)^2 MLP with a stored
+activation gradient (leaky_mlp_fwd / leaky_mlp_bwd).
 """
 from __future__ import annotations
 
@@ -24,6 +26,7 @@ __all__ = [
     "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn", "update_load_balance_bias",
     "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
     "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
+    "leaky_mlp_workspace_size", "leaky_mlp_fwd", "leaky_mlp_bwd", "leaky_mlp_saved_views",
 ]
 
 ESG_F32 = 0
@@ -58,6 +61,11 @@ _SIGNATURES = {
     "esg_update_load_balance_bias": (_c_int, [_c_vp, _c_vp, _c_vp, _c_f, _c_f, _c_f, _c_f, _c_int, _c_vp]),
     "esg_update_load_balance_bias_from_counts": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_f, _c_f, _c_f, _c_f,
                                                           _c_int, _c_vp]),
+    "esg_leaky_mlp_workspace_size": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size),
+                                              ctypes.POINTER(_c_size)]),
+    "esg_leaky_mlp_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_size, _c_vp]),
+    "esg_leaky_mlp_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                   _c_vp, _c_size, _c_vp]),
     "esg_sigmoid_topk_supported": (_c_int, [_c_int, _c_int]),
     "esg_sigmoid_topk_routing": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_vp, _c_vp,
                                           _c_vp]),
@@ -290,6 +298,58 @@ def update_load_balance_bias_from_counts(bias, freq_ema, counts, tokens: int, ta
         _dev(bias, "bias", torch.float32), _dev(freq_ema, "freq_ema", torch.float32),
         _dev(counts, "counts", torch.int32), tokens, target_freq, gamma, bias_max, momentum, G,
         _stream(bias.device)), "update_load_balance_bias_from_counts")
+
+
+def leaky_mlp_workspace_size(tokens: int, d_model: int, d_ff: int):
+    """(saved_bytes, scratch_bytes) of the LeakyReLU(0.5)^2 MLP."""
+    sv, sc = _c_size(), _c_size()
+    _check(lib().esg_leaky_mlp_workspace_size(tokens, d_model, d_ff, ctypes.byref(sv), ctypes.byref(sc)),
+           "leaky_mlp_workspace_size")
+    return sv.value, sc.value
+
+
+def leaky_mlp_saved_views(saved: torch.Tensor, tokens: int, d_ff: int):
+    """(post, act_grad) bf16 [tokens, d_ff] views of a forward's saved buffer."""
+    n = tokens * d_ff
+    off = (n * 2 + 255) // 256 * 256
+    post = saved[: n * 2].view(torch.bfloat16).view(tokens, d_ff)
+    act = saved[off: off + n * 2].view(torch.bfloat16).view(tokens, d_ff)
+    return post, act
+
+
+def leaky_mlp_fwd(x, w_up, w_down, out=None, saved=None):
+    """y = LeakyReLU(0.5)(x W_up^T)^2 W_down^T (bf16).  Returns (y, saved): saved
+    holds post and act_grad for leaky_mlp_bwd."""
+    T, d = x.shape
+    F = w_up.shape[0]
+    if w_up.shape != (F, d) or w_down.shape != (d, F):
+        raise EsgError("w_up must be [d_ff, d_model] and w_down [d_model, d_ff]")
+    sv, _ = leaky_mlp_workspace_size(T, d, F)
+    y = torch.empty_like(x) if out is None else out
+    if saved is None or saved.numel() < sv:
+        saved = torch.empty(max(sv, 1), dtype=torch.uint8, device=x.device)
+    bf = torch.bfloat16
+    _check(lib().esg_leaky_mlp_fwd(_dev(x, "x", bf), _dev(w_up, "w_up", bf), _dev(w_down, "w_down", bf), T, d, F,
+                                   _dev(y, "y", bf), _dev(saved, "saved"), saved.numel(), _stream(x.device)),
+           "leaky_mlp_fwd")
+    return y, saved
+
+
+def leaky_mlp_bwd(dy, x, w_up, w_down, saved, workspace: Optional[dict] = None, outs=None):
+    """(dx, dW_up, dW_down) of the LeakyReLU(0.5)^2 MLP (overwritten)."""
+    T, d = x.shape
+    F = w_up.shape[0]
+    _, sc = leaky_mlp_workspace_size(T, d, F)
+    if outs is None:
+        outs = (torch.empty_like(x), torch.empty_like(w_up), torch.empty_like(w_down))
+    dx, dwu, dwd = outs
+    scratch = _ws(sc, x.device, workspace, "mlp_scratch")
+    bf = torch.bfloat16
+    _check(lib().esg_leaky_mlp_bwd(_dev(dy, "dy", bf), _dev(x, "x", bf), _dev(w_up, "w_up", bf),
+                                   _dev(w_down, "w_down", bf), T, d, F, _dev(saved, "saved"), _dev(dx, "dx", bf),
+                                   _dev(dwu, "dw_up", bf), _dev(dwd, "dw_down", bf), _dev(scratch, "scratch"),
+                                   scratch.numel(), _stream(x.device)), "leaky_mlp_bwd")
+    return dx, dwu, dwd
 
 
 def sigmoid_topk_supported(num_experts: int, topk: int) -> bool:

@@ -301,6 +301,66 @@ int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const
                                        momentum, groups, (hipStream_t)stream));
 }
 
+namespace {
+int mlp_shape(int tokens, int d_model, int d_ff) {
+  if (tokens < 0 || d_model <= 0 || d_ff <= 0) return ESG_ERR_INVALID_ARG;
+  if (d_model % 8 || d_ff % 8) return ESG_ERR_UNSUPPORTED;
+  const long long wide = d_model > d_ff ? d_model : d_ff;
+  if ((long long)tokens * wide * 2 >= (1ll << 31) || (long long)d_model * d_ff * 2 >= (1ll << 31))
+    return ESG_ERR_UNSUPPORTED;
+  return ESG_OK;
+}
+}  // namespace
+
+int esg_leaky_mlp_workspace_size(int tokens, int d_model, int d_ff, size_t* saved_bytes, size_t* scratch_bytes) {
+  if (saved_bytes == nullptr || scratch_bytes == nullptr) return ESG_ERR_INVALID_ARG;
+  const int e = mlp_shape(tokens, d_model, d_ff);
+  if (e != ESG_OK) return e;
+  const size_t tf = (size_t)tokens * d_ff * 2;
+  *saved_bytes = 2 * align256(tf);
+  *scratch_bytes = align256(tf) + align256(mlp_partial_bytes(tokens, d_model, d_ff));
+  return ESG_OK;
+}
+
+int esg_leaky_mlp_fwd(const void* x, const void* w_up, const void* w_down, int tokens, int d_model, int d_ff,
+                      void* y, void* saved, size_t saved_bytes, void* stream) {
+  size_t need_saved, need_scratch;
+  int e = esg_leaky_mlp_workspace_size(tokens, d_model, d_ff, &need_saved, &need_scratch);
+  if (e != ESG_OK) return e;
+  if (tokens == 0) return ESG_OK;
+  if (x == nullptr || w_up == nullptr || w_down == nullptr || y == nullptr || saved == nullptr)
+    return ESG_ERR_INVALID_ARG;
+  if (saved_bytes < need_saved) return ESG_ERR_WORKSPACE;
+  void* post = saved;
+  void* act = (char*)saved + align256((size_t)tokens * d_ff * 2);
+  return hip_status(launch_mlp_fwd(x, w_up, w_down, tokens, d_model, d_ff, y, post, act, (hipStream_t)stream));
+}
+
+int esg_leaky_mlp_bwd(const void* dy, const void* x, const void* w_up, const void* w_down, int tokens, int d_model,
+                      int d_ff, const void* saved, void* dx, void* dw_up, void* dw_down, void* scratch,
+                      size_t scratch_bytes, void* stream) {
+  size_t need_saved, need_scratch;
+  int e = esg_leaky_mlp_workspace_size(tokens, d_model, d_ff, &need_saved, &need_scratch);
+  if (e != ESG_OK) return e;
+  if (w_up == nullptr || w_down == nullptr || dw_up == nullptr || dw_down == nullptr) return ESG_ERR_INVALID_ARG;
+  if (tokens > 0 && (dy == nullptr || x == nullptr || saved == nullptr || dx == nullptr || scratch == nullptr))
+    return ESG_ERR_INVALID_ARG;
+  if (tokens > 0 && scratch_bytes < need_scratch) return ESG_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (tokens == 0) {  // no tokens: the weight gradients are zero
+    e = hip_status(launch_fill_i32((int32_t*)dw_up, 0, (size_t)d_ff * d_model / 2, st));
+    if (e != ESG_OK) return e;
+    return hip_status(launch_fill_i32((int32_t*)dw_down, 0, (size_t)d_ff * d_model / 2, st));
+  }
+  const size_t tf = align256((size_t)tokens * d_ff * 2);
+  const void* post = saved;
+  const void* act = (const char*)saved + tf;
+  void* dpre = scratch;
+  float* part = (float*)((char*)scratch + tf);
+  return hip_status(launch_mlp_bwd(dy, x, w_up, w_down, tokens, d_model, d_ff, post, act, dx, dw_up, dw_down, dpre,
+                                   part, st));
+}
+
 int esg_sigmoid_topk_supported(int num_experts, int topk) { return sigmoid_topk_supported(num_experts, topk) ? 1 : 0; }
 
 int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int bias_stride, int tokens,

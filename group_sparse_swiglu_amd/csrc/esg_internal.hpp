@@ -103,6 +103,15 @@ hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const 
                               int groups, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stream);
 
+// ---- LeakyReLU(0.5)^2 MLP (esg_mlp.hip), bf16 ------------------------------------
+size_t mlp_partial_bytes(int tokens, int d_model, int d_ff);
+// bf16 buffers as void pointers (the bf16 type lives with the device code)
+hipError_t launch_mlp_fwd(const void* x, const void* w_up, const void* w_down, int tokens, int d, int F, void* y,
+                          void* post, void* act_grad, hipStream_t stream);
+hipError_t launch_mlp_bwd(const void* dy, const void* x, const void* w_up, const void* w_down, int tokens, int d,
+                          int F, const void* post, const void* act_grad, void* dx, void* dw_up, void* dw_down,
+                          void* dpre, float* part, hipStream_t stream);
+
 // ---- sigmoid top-k routing (esg_route.hip) ------------------------------------
 constexpr int kRouteMaxExperts = 2048;  // 32 experts per lane of one wavefront
 constexpr int kRouteMaxK = 32;

@@ -198,6 +198,39 @@ int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const
                                              void* stream);
 
 /*
+ * LeakyReLU(0.5)-squared MLP with a stored activation gradient (parameter-golf
+ * pull request 1105, "1. Fused MLP Kernels"; architecture table A.7: d_model
+ * 512, width 3.5 x 512 = 1792).  bf16 tensors, fp32 accumulation:
+ *   forward   pre = x . W_up^T (not stored);
+ *             act_grad = 2*pre if pre > 0 else 0.5*pre;
+ *             post = 0.5 * act_grad * pre     (= LeakyReLU(0.5)(pre)^2);
+ *             y = post . W_down^T
+ *   backward  dpre = (dy . W_down) * act_grad  (the product fused into the
+ *             GEMM epilogue); dx = dpre . W_up; dW_up = dpre^T . x;
+ *             dW_down = dy^T . post
+ * post and act_grad are computed from the fp32 pre and rounded once to bf16;
+ * dpre is rounded to bf16 before its two products.  The weight gradients are
+ * deterministic: token splits add their fp32 partials in a fixed order.
+ *
+ * x, y, dy, dx: device bf16 [tokens, d_model]; w_up, dw_up: [d_ff, d_model];
+ * w_down, dw_down: [d_model, d_ff] (nn.Linear layout).  The gradients are
+ * overwritten (tokens == 0 writes zero weight gradients).
+ * saved: device buffer of saved_bytes holding post then act_grad ([tokens,
+ * d_ff] bf16 each, 256-byte aligned), written by the forward for the backward.
+ * scratch: device buffer of scratch_bytes for the backward (dpre and the fp32
+ * partials of the weight gradients).
+ * Errors: ESG_ERR_INVALID_ARG (null pointer, negative size),
+ * ESG_ERR_UNSUPPORTED (d_model or d_ff not a multiple of 8, or a tensor of
+ * 2^31 bytes or more), ESG_ERR_WORKSPACE (a buffer below its size).
+ */
+int esg_leaky_mlp_workspace_size(int tokens, int d_model, int d_ff, size_t* saved_bytes, size_t* scratch_bytes);
+int esg_leaky_mlp_fwd(const void* x, const void* w_up, const void* w_down, int tokens, int d_model, int d_ff,
+                      void* y, void* saved, size_t saved_bytes, void* stream);
+int esg_leaky_mlp_bwd(const void* dy, const void* x, const void* w_up, const void* w_down, int tokens, int d_model,
+                      int d_ff, const void* saved, void* dx, void* dw_up, void* dw_down, void* scratch,
+                      size_t scratch_bytes, void* stream);
+
+/*
  * Sigmoid top-k routing with an expert bias (Megatron-Core developer guide,
  * "core.inference.moe.sigmoid_topk": the description of _sigmoid_topk_kernel
  * and the API of sigmoid_topk_routing).  Per token row t and expert e:

@@ -126,3 +126,18 @@ def test_sigmoid_topk_argument_checks():
     assert lib.esg_sigmoid_topk_routing(null, null, 0, 4, 256, 8, 1.0, 0, null, null, null) == 1
     assert lib.esg_sigmoid_topk_routing(null, null, 1, 4, 256, 40, 1.0, 0, null, null, null) == 2
     assert lib.esg_sigmoid_topk_routing(null, null, 1, 4, 256, 8, 1.0, 0, null, null, null) == 1
+
+
+def test_leaky_mlp_sizes_and_argument_checks():
+    lib = E.lib()
+    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.esg_leaky_mlp_workspace_size(0, 512, 1792, ctypes.byref(sv), ctypes.byref(sc)) == 0
+    assert sv.value == 0
+    assert lib.esg_leaky_mlp_workspace_size(1000, 136, 456, ctypes.byref(sv), ctypes.byref(sc)) == 0
+    assert sv.value >= 2 * 1000 * 456 * 2 and sc.value >= 1000 * 456 * 2
+    assert lib.esg_leaky_mlp_workspace_size(10, 100, 64, ctypes.byref(sv), ctypes.byref(sc)) == 2   # d % 8
+    assert lib.esg_leaky_mlp_workspace_size(-1, 64, 64, ctypes.byref(sv), ctypes.byref(sc)) == 1
+    assert lib.esg_leaky_mlp_workspace_size(2 ** 20, 2048, 2048, ctypes.byref(sv), ctypes.byref(sc)) == 2
+    null = None
+    assert lib.esg_leaky_mlp_fwd(null, null, null, 0, 64, 64, null, null, 0, null) == 0
+    assert lib.esg_leaky_mlp_fwd(null, null, null, 4, 64, 64, null, null, 0, null) == 1
