@@ -34,21 +34,32 @@ using namespace tiles;
 enum { KROW = 0, NROW = 1 };
 enum { EPI_STORE = 0, EPI_ACT = 1, EPI_MUL = 2, EPI_PARTIAL = 3 };
 
-constexpr int GQ = 256, GP = 128, GK = 64;
-constexpr int A_BYTES = GQ * 128;  // 32 KB: K-row 256 x 128 B, or N-row 2 x (64 x 256 B)
+constexpr int GP = 128, GK = 64;
 constexpr int B_BYTES = GP * 128;  // 16 KB: K-row 128 x 128 B, or N-row 64 x 256 B
-constexpr int STAGE = A_BYTES + B_BYTES;
-constexpr int IA = A_BYTES / 1024 / 4;  // 1 KB DMA instructions per wave per stage
-constexpr int IB = B_BYTES / 1024 / 4;
-constexpr int LDMA = IA + IB;
+
+// Output tile TQ (256 or 128) columns x 128 rows.  256: three 48 KB stages,
+// one workgroup per compute unit, waves of 128 x 64.  128: two 32 KB stages,
+// two workgroups per compute unit (one's epilogue overlaps the other's
+// loop), waves of 64 x 64.
+template <int TQ>
+struct TileCfg {
+  static constexpr int NS = TQ == 256 ? 3 : 2;
+  static constexpr int OCC = TQ == 256 ? 1 : 2;
+  static constexpr int A_BYTES = TQ * 128;  // K-row TQ x 128 B, or N-row TQ/128 x (64 x 256 B)
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDMA = STAGE / 1024 / 4;  // 1 KB DMA instructions per wave per stage
+  static constexpr int FM = TQ / 32;             // 16-wide q fragments per wave
+};
 
 struct GemmArgs {
   const bf16_t* a;  // KROW: [Q][K] (row stride lda); NROW: [K][Q]
   const bf16_t* b;  // KROW: [P][K]; NROW: [K][P]
   int lda, ldb;
   int Q, P, K;
-  int k_split;      // K extent of one split (multiple of 64); blockIdx.z = split
-  int nq;           // q blocks
+  int k_split;      // K extent of one split (multiple of 64)
+  int nq, np;       // q and p blocks
+  int splits;       // K splits
+  int nitems;       // work items of the persistent loop (tiles, plus empty ones for the XCD order)
   bf16_t* c0;       // [P][ldc] outputs (q contiguous)
   bf16_t* c1;
   int ldc;
@@ -112,28 +123,27 @@ __device__ __forceinline__ uint4 frag(const ESG_LDS char* t, int rowbase, int kb
   }
 }
 
-template <int AL, int BL, int EPI>
-__global__ __launch_bounds__(NT, 1) void mlp_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) char st0_[STAGE], st1_[STAGE], st2_[STAGE];
-  ESG_LDS char* st0 = (ESG_LDS char*)st0_;
-  ESG_LDS char* st1 = (ESG_LDS char*)st1_;
-  ESG_LDS char* st2 = (ESG_LDS char*)st2_;
+// One output tile (q block qb, p block pb, K split z).  Leaves the stages free
+// for the next tile (all LDS reads done, every wave past a barrier).
+template <int TQ, int AL, int BL, int EPI>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int qb, int pb, int z, ESG_LDS char* st0,
+                                          ESG_LDS char* st1, ESG_LDS char* st2) {
+  using C = TileCfg<TQ>;
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int qb = blockIdx.x % g.nq, pb = blockIdx.x / g.nq;
-  const int q0 = qb * GQ, p0 = pb * GP;
-  const int kbeg = blockIdx.z * g.k_split;
+  const int q0 = qb * TQ, p0 = pb * GP;
+  const int kbeg = z * g.k_split;
   const int kend = min(g.K, kbeg + g.k_split);
   const int nk = (kend - kbeg + GK - 1) / GK;
 
   const DmaSrc ra = make_dma_src(g.a, AL == KROW ? (uint32_t)g.Q * g.lda * 2 : (uint32_t)g.K * g.lda * 2);
   const DmaSrc rb = make_dma_src(g.b, BL == KROW ? (uint32_t)g.P * g.ldb * 2 : (uint32_t)g.K * g.ldb * 2);
-  OperandDma<AL, GQ> da;
+  OperandDma<AL, TQ> da;
   OperandDma<BL, GP> db;
   da.init(w, lane, q0, g.Q, g.lda, kbeg);
   db.init(w, lane, p0, g.P, g.ldb, kbeg);
 
-  const int wm = w & 1, wn = w >> 1;  // wave: q [wm*128, +128), p [wn*64, +64)
-  constexpr int FM = 8, FN = 4;
+  const int wm = w & 1, wn = w >> 1;  // wave: q [wm*TQ/2, +TQ/2), p [wn*64, +64)
+  constexpr int FM = C::FM, FN = 4, HQ = TQ / 2;
 
   // EPI_MUL: the act_grad values of this lane's outputs, loaded before the K
   // loop (the first pipeline wait covers them)
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int q = q0 + wm * 128 + i * 16 + (lane >> 4) * 4;
+        const int q = q0 + wm * HQ + i * 16 + (lane >> 4) * 4;
         const int p = p0 + wn * 64 + j * 16 + (lane & 15);
         const uint32_t o = (q < g.Q && p < g.P) ? ((uint32_t)p * g.ldc + q) * 2 : kOOB;
         const v2i32 v = __builtin_amdgcn_raw_buffer_load_b64(rx, o, 0, 0);
@@ -156,40 +166,39 @@ __global__ __launch_bounds__(NT, 1) void mlp_gemm_kernel(GemmArgs g) {
   zero_acc(acc);
   auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
     da.issue(ra, st, w, kt, kbeg, kend);
-    db.issue(rb, st + A_BYTES, w, kt, kbeg, kend);
+    db.issue(rb, st + C::A_BYTES, w, kt, kbeg, kend);
   };
   auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       uint4 a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = frag<AL>(st, wm * 128 + i * 16, kb, lane);
+      for (int i = 0; i < FM; ++i) a[i] = frag<AL>(st, wm * HQ + i * 16, kb, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = frag<BL>(st + A_BYTES, wn * 64 + j * 16, kb, lane);
+      for (int j = 0; j < FN; ++j) b[j] = frag<BL>(st + C::A_BYTES, wn * 64 + j * 16, kb, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) mma_bf16(acc[i][j], a[i], b[j]);
     }
   };
-  kloop<3, LDMA, 0>(nk, st0, st1, st2, issue, compute);
+  kloop<C::NS, C::LDMA, 0>(nk, st0, st1, st2, issue, compute);
   wait_lgkm0();
   barrier();  // every wave is done with the stages
 
   if constexpr (EPI == EPI_PARTIAL) {
-    float* out = g.part + (size_t)blockIdx.z * g.P * g.Q;
+    float* out = g.part + (size_t)z * g.P * g.Q;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int q = q0 + wm * 128 + i * 16 + (lane >> 4) * 4;
+        const int q = q0 + wm * HQ + i * 16 + (lane >> 4) * 4;
         const int p = p0 + wn * 64 + j * 16 + (lane & 15);
         if (q < g.Q && p < g.P)
           *(float4*)(out + (size_t)p * g.Q + q) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       }
-    return;
   } else {
-    using RS = RowStore<GQ>;
+    using RS = RowStore<TQ>;
     const rsrc_t rc0 = make_rsrc(g.c0, (uint32_t)g.P * g.ldc * 2);
     uint32_t row_off[RS::IT];
 #pragma unroll
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_gemm_kernel(GemmArgs g) {
       const int p = p0 + RS::row(it, threadIdx.x);
       row_off[it] = p < g.P ? (uint32_t)p * g.ldc * 2 : kOOB;
     }
-    ESG_LDS char* out0 = st0;  // rows 0..63 (32 KB)
+    ESG_LDS char* out0 = st0;  // rows 0..63 (TQ/4 KB)
     ESG_LDS char* out1 = st1;  // rows 64..127
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(NT, 1) void mlp_gemm_kernel(GemmArgs g) {
             v[e] = x;
           }
         }
-        RS::put(out0, out1, wn * 64 + j * 16 + (lane & 15), wm * 128 + i * 16 + (lane >> 4) * 4, v);
+        RS::put(out0, out1, wn * 64 + j * 16 + (lane & 15), wm * HQ + i * 16 + (lane >> 4) * 4, v);
       }
     wait_lgkm0();
     barrier();
@@ -236,12 +245,44 @@ __global__ __launch_bounds__(NT, 1) void mlp_gemm_kernel(GemmArgs g) {
             const float x = acc[i][j][e];
             v[e] = x > 0.0f ? 2.0f * x : 0.5f * x;  // act_grad
           }
-          RS::put(out0, out1, wn * 64 + j * 16 + (lane & 15), wm * 128 + i * 16 + (lane >> 4) * 4, v);
+          RS::put(out0, out1, wn * 64 + j * 16 + (lane & 15), wm * HQ + i * 16 + (lane >> 4) * 4, v);
         }
       wait_lgkm0();
       barrier();
       RS::flush(out0, out1, rc1, row_off, q0, g.Q);
     }
+  }
+  wait_lgkm0();
+  barrier();  // staged output read by every wave: the stages are free again
+}
+
+// Persistent: each workgroup takes work items blockIdx.x, + gridDim.x, ... so
+// that a tile's output stores drain while the next tile's operands stream in.
+// Workgroups go to the 8 XCDs round-robin (and gridDim.x is a multiple of 8),
+// so item t runs on XCD t % 8.  The order keeps operands that several tiles
+// read in one XCD's L2: without splits, item t takes p block
+// 8 * (t / 8 / nq) + t % 8 and q block (t / 8) % nq, so the nq tiles of one p
+// block (same token rows) share an XCD; with splits, item t takes split
+// t % splits, so with 8 splits each split's token range is read by one XCD.
+template <int TQ, int AL, int BL, int EPI>
+__global__ __launch_bounds__(NT, TileCfg<TQ>::OCC) void mlp_gemm_kernel(GemmArgs g) {
+  using C = TileCfg<TQ>;
+  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE], st2_[C::NS == 3 ? C::STAGE : 16];
+  for (int t = blockIdx.x; t < g.nitems; t += gridDim.x) {
+    int qb, pb, z;
+    if (g.splits > 1) {
+      z = t % g.splits;
+      const int r = t / g.splits;
+      qb = r % g.nq;
+      pb = r / g.nq;
+    } else {
+      z = 0;
+      const int r = t >> 3;
+      qb = r % g.nq;
+      pb = (r / g.nq) * 8 + (t & 7);
+      if (pb >= g.np) continue;
+    }
+    gemm_tile<TQ, AL, BL, EPI>(g, qb, pb, z, (ESG_LDS char*)st0_, (ESG_LDS char*)st1_, (ESG_LDS char*)st2_);
   }
 }
 
@@ -260,11 +301,29 @@ __global__ void mlp_reduce_kernel(const float* __restrict__ part, int splits, si
   }
 }
 
-template <int AL, int BL, int EPI>
-hipError_t launch_gemm(const char* name, const GemmArgs& a, int splits, hipStream_t stream) {
-  const int np = (a.P + GP - 1) / GP;
+int compute_units() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int TQ, int AL, int BL, int EPI>
+hipError_t launch_gemm(const char* name, GemmArgs a, int splits, hipStream_t stream) {
+  a.nq = (a.Q + TQ - 1) / TQ;
+  a.np = (a.P + GP - 1) / GP;
+  a.splits = splits;
+  a.nitems = splits > 1 ? a.nq * a.np * splits : a.nq * 8 * ((a.np + 7) / 8);
+  // TileCfg::OCC workgroups per compute unit, a multiple of 8
+  const int slots = compute_units() * TileCfg<TQ>::OCC;
+  const int blocks = std::min((a.nitems + 7) / 8 * 8, slots / 8 * 8);
   LaunchTimer timer(name, stream);
-  hipLaunchKernelGGL((mlp_gemm_kernel<AL, BL, EPI>), dim3(a.nq * np, 1, splits), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((mlp_gemm_kernel<TQ, AL, BL, EPI>), dim3(blocks), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -278,33 +337,35 @@ GemmArgs args(const bf16_t* A, int lda, const bf16_t* B, int ldb, int Q, int P, 
   g.P = P;
   g.K = K;
   g.k_split = K;
-  g.nq = (Q + GQ - 1) / GQ;
   return g;
 }
 
-// Token splits of a weight-gradient product: enough workgroups for two per
-// compute unit, each split a whole number of 64-token steps.
-int dw_splits(int tokens, int tiles, int* k_split) {
+// Token splits of a weight-gradient product: as many as keep every compute
+// unit busy in one round of tiles (tiles * splits <= CUs, at most kMaxSplits),
+// each split a whole number of 64-token steps.
+constexpr int kMaxSplits = 16;
+int dw_splits(int tokens, int tiles, int cus, int* k_split) {
   const int steps = (tokens + GK - 1) / GK;
   if (steps == 0) {  // no tokens: nothing to split
     *k_split = GK;
     return 1;
   }
-  int s = (512 + tiles - 1) / tiles;
+  // one split per XCD when a split's tiles fit in one XCD, else fill the CUs
+  int s = tiles <= cus / 8 ? 8 : std::min(kMaxSplits, std::max(1, cus / tiles));
   if (s > steps) s = steps;
-  if (s < 1) s = 1;
   const int per = (steps + s - 1) / s;
   *k_split = per * GK;
   return (steps + per - 1) / per;
 }
 
+template <int TQ>
 hipError_t weight_grad(const char* name, const bf16_t* A, int lda, const bf16_t* B, int ldb, int Q, int P,
                        int tokens, float* part, bf16_t* out, hipStream_t stream) {
   GemmArgs g = args(A, lda, B, ldb, Q, P, tokens);
-  const int tiles = g.nq * ((P + GP - 1) / GP);
-  const int splits = dw_splits(tokens, tiles, &g.k_split);
+  const int tiles = ((Q + TQ - 1) / TQ) * ((P + GP - 1) / GP);
+  const int splits = dw_splits(tokens, tiles, compute_units() * TileCfg<TQ>::OCC, &g.k_split);
   g.part = part;
-  hipError_t e = launch_gemm<NROW, NROW, EPI_PARTIAL>(name, g, splits, stream);
+  hipError_t e = launch_gemm<TQ, NROW, NROW, EPI_PARTIAL>(name, g, splits, stream);
   if (e != hipSuccess) return e;
   const size_t n4 = (size_t)P * Q / 4;
   LaunchTimer timer("mlp_dw_reduce", stream);
@@ -315,16 +376,14 @@ hipError_t weight_grad(const char* name, const bf16_t* A, int lda, const bf16_t*
 
 }  // namespace
 
+// tile width per product (measured on the 86016 x 512 x 1792 workload)
+constexpr int kUpTQ = 128, kDownTQ = 256, kDpreTQ = 128, kDxTQ = 256, kDwTQ = 128;
+
 size_t mlp_partial_bytes(int tokens, int d_model, int d_ff) {
-  size_t worst = 0;
-  for (int w = 0; w < 2; ++w) {
-    const int Q = w ? d_model : d_ff, P = w ? d_ff : d_model;
-    const int tiles = ((Q + GQ - 1) / GQ) * ((P + GP - 1) / GP);
-    int ks;
-    const int s = dw_splits(tokens, tiles, &ks);
-    worst = std::max(worst, (size_t)s * P * Q * 4);
-  }
-  return worst;
+  // any device and tile width: at most kMaxSplits splits, each a whole 64-token step
+  const size_t steps = ((size_t)tokens + GK - 1) / GK;
+  const size_t splits = std::max<size_t>(1, std::min<size_t>(kMaxSplits, steps));
+  return splits * d_model * d_ff * 4;
 }
 
 hipError_t launch_mlp_fwd(const void* xv, const void* w_upv, const void* w_downv, int tokens, int d, int F, void* yv,
@@ -337,13 +396,13 @@ hipError_t launch_mlp_fwd(const void* xv, const void* w_upv, const void* w_downv
   g.c0 = post;
   g.c1 = act_grad;
   g.ldc = F;
-  hipError_t e = launch_gemm<KROW, KROW, EPI_ACT>("mlp_up_act", g, 1, stream);
+  hipError_t e = launch_gemm<kUpTQ, KROW, KROW, EPI_ACT>("mlp_up_act", g, 1, stream);
   if (e != hipSuccess) return e;
   // y^T = W_down . post^T: q = d, p = token, K = F
   GemmArgs h = args(w_down, F, post, F, d, tokens, F);
   h.c0 = y;
   h.ldc = d;
-  return launch_gemm<KROW, KROW, EPI_STORE>("mlp_down", h, 1, stream);
+  return launch_gemm<kDownTQ, KROW, KROW, EPI_STORE>("mlp_down", h, 1, stream);
 }
 
 hipError_t launch_mlp_bwd(const void* dyv, const void* xv, const void* w_upv, const void* w_downv, int tokens, int d,
@@ -358,20 +417,20 @@ hipError_t launch_mlp_bwd(const void* dyv, const void* xv, const void* w_upv, co
     g.c0 = dpre;
     g.ldc = F;
     g.aux = act_grad;
-    hipError_t e = launch_gemm<NROW, KROW, EPI_MUL>("mlp_dpre", g, 1, stream);
+    hipError_t e = launch_gemm<kDpreTQ, NROW, KROW, EPI_MUL>("mlp_dpre", g, 1, stream);
     if (e != hipSuccess) return e;
     // dx^T = W_up^T . dpre^T: q = d (W_up read along neurons), p = token, K = F
     GemmArgs h = args(w_up, d, dpre, F, d, tokens, F);
     h.c0 = dx;
     h.ldc = d;
-    e = launch_gemm<NROW, KROW, EPI_STORE>("mlp_dx", h, 1, stream);
+    e = launch_gemm<kDxTQ, NROW, KROW, EPI_STORE>("mlp_dx", h, 1, stream);
     if (e != hipSuccess) return e;
   }
   // dW_down [d][F] = dy^T . post: q = neuron, p = d, K = tokens (both token-major)
-  hipError_t e = weight_grad("mlp_dw_down", post, F, dy, d, F, d, tokens, part, dw_down, stream);
+  hipError_t e = weight_grad<kDwTQ>("mlp_dw_down", post, F, dy, d, F, d, tokens, part, dw_down, stream);
   if (e != hipSuccess) return e;
   // dW_up [F][d] = dpre^T . x: q = d, p = neuron, K = tokens
-  return weight_grad("mlp_dw_up", x, d, dpre, F, d, F, tokens, part, dw_up, stream);
+  return weight_grad<kDwTQ>("mlp_dw_up", x, d, dpre, F, d, F, tokens, part, dw_up, stream);
 }
 
 }  // namespace esg
