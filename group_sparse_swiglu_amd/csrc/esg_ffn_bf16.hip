@@ -171,11 +171,13 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
     bf16_t* __restrict__ act_out, bf16_t* __restrict__ partials) {
   using C = Dh2<GSB>;
   constexpr int NS = stages_for<GSB>();
-  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE], st2_[NS == 3 ? C::STAGE : 16];
+  // NS stages in one array (with two stages nothing uses st2; no placeholder
+  // array, so that two workgroups fit in a compute unit's LDS)
+  __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE];
   __shared__ __attribute__((aligned(1024))) char dgu_[C::DGU_BYTES];
-  ESG_LDS char* st0 = (ESG_LDS char*)st0_;
-  ESG_LDS char* st1 = (ESG_LDS char*)st1_;
-  ESG_LDS char* st2 = (ESG_LDS char*)st2_;
+  ESG_LDS char* st0 = (ESG_LDS char*)stages_;
+  ESG_LDS char* st1 = st0 + C::STAGE;
+  ESG_LDS char* st2 = NS == 3 ? st1 + C::STAGE : st0;
   ESG_LDS char* dgu = (ESG_LDS char*)dgu_;
 
   const int tile = blockIdx.x;
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
     bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu, bf16_t* __restrict__ dwd) {
   using C = Dw2<GSB>;
   constexpr int NS = stages_for<GSB>();
-  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE], st2_[NS == 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE];  // no placeholder for a third stage
   DwWork wk;
   if (!dw_work(blockIdx.x, 2 * (F / gs) * nsub, (d + 127) / 128, wk)) return;
   const int g = (wk.unit >> 1) / nsub, s = (wk.unit >> 1) % nsub;
@@ -318,9 +320,9 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
   const int p0 = tile_off[g] * BM, p1 = tile_off[g + 1] * BM;
   const size_t sub_el = (size_t)s * rows_total * GSB;
   const uint32_t pbytes = (uint32_t)(nsub * rows_total * GSB * 2);
-  ESG_LDS char* st0 = (ESG_LDS char*)st0_;
-  ESG_LDS char* st1 = (ESG_LDS char*)st1_;
-  ESG_LDS char* st2 = (ESG_LDS char*)st2_;
+  ESG_LDS char* st0 = (ESG_LDS char*)stages_;
+  ESG_LDS char* st1 = st0 + C::STAGE;
+  ESG_LDS char* st2 = NS == 3 ? st1 + C::STAGE : st0;
   if ((wk.unit & 1) == 0)
     dw2_body<GSB, 0, NS>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du, pbytes,
                          dwg, dwu, db0, st0, st1, st2);

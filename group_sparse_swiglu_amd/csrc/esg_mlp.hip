@@ -267,7 +267,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int qb, int pb, int
 template <int TQ, int AL, int BL, int EPI>
 __global__ __launch_bounds__(NT, TileCfg<TQ>::OCC) void mlp_gemm_kernel(GemmArgs g) {
   using C = TileCfg<TQ>;
-  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE], st2_[C::NS == 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char stages_[C::NS * C::STAGE];
   for (int t = blockIdx.x; t < g.nitems; t += gridDim.x) {
     int qb, pb, z;
     if (g.splits > 1) {
@@ -282,7 +282,8 @@ __global__ __launch_bounds__(NT, TileCfg<TQ>::OCC) void mlp_gemm_kernel(GemmArgs
       pb = (r / g.nq) * 8 + (t & 7);
       if (pb >= g.np) continue;
     }
-    gemm_tile<TQ, AL, BL, EPI>(g, qb, pb, z, (ESG_LDS char*)st0_, (ESG_LDS char*)st1_, (ESG_LDS char*)st2_);
+    ESG_LDS char* st0 = (ESG_LDS char*)stages_;
+    gemm_tile<TQ, AL, BL, EPI>(g, qb, pb, z, st0, st0 + C::STAGE, C::NS == 3 ? st0 + 2 * C::STAGE : st0);
   }
 }
 
