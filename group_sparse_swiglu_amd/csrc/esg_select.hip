@@ -7,10 +7,11 @@
 // super-chunk's |SiLU| values are staged in LDS and summed per (token, group)
 // in column order into an fp32 energy table E[BM][G] that starts at the bias.
 // The top-k is a wavefront rank test: lane g counts the groups that beat group
-// g (higher score, or equal score and lower id); the group is selected when
-// fewer than k beat it, and its output slot is its rank among the selected ids
-// (a ballot prefix).  Every token's result depends only on its own row: batch
-// invariant and bitwise reproducible.
+// g (higher score, or equal score and lower id), reading the other scores as
+// broadcast LDS reads, for all of a wavefront's tokens in one pass; the group
+// is selected when fewer than k beat it, and its output slot is its rank among
+// the selected ids (a ballot prefix).  Every token's result depends only on
+// its own row: batch invariant and bitwise reproducible.
 #include <type_traits>
 
 #include "esg_device.hpp"
@@ -199,30 +200,45 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   }
   __syncthreads();
 
-  // rank top-k, one token per wave at a time: group g is selected when fewer
-  // than k groups beat it (higher score, or equal score and lower id)
+  // rank top-k: group g is selected when fewer than k groups beat it (higher
+  // score, or equal score and lower id); its output slot is its rank among the
+  // selected ids (a ballot prefix)
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int r = wave; r < BM; r += 4) {
-    const int t = t0 + r;
-    if (t >= tokens) break;
-    const float* row = E + r * ES;
-    int base = 0;
-    if (groups <= 64) {
-      const float sg = lane < groups ? row[lane] : 0.0f;
-      const int sbits = __float_as_int(sg);
-      int beat = 0;
-      for (int q = 0; q < groups; ++q) {
-        const float sq = __int_as_float(__builtin_amdgcn_readlane(sbits, q));
-        beat += (sq > sg) || (sq == sg && q < lane);
+  if (groups <= 64) {
+    // lane g holds group g of the wave's BM/4 tokens at once; every other
+    // group's score comes as a broadcast LDS read (same address in all lanes)
+    constexpr int TPW = BM / 4;
+    float sg[TPW];
+    int beat[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      sg[i] = lane < groups ? E[(wave + 4 * i) * ES + lane] : 0.0f;
+      beat[i] = 0;
+    }
+    for (int q = 0; q < groups; ++q) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const float sq = E[(wave + 4 * i) * ES + q];
+        beat[i] += (sq > sg[i]) || (sq == sg[i] && q < lane);
       }
-      const bool sel = lane < groups && beat < k;
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = t0 + wave + 4 * i;
+      const bool sel = lane < groups && beat[i] < k;
       const uint64_t m = __ballot(sel);
       const int pos = __popcll(m & lt);
-      if (sel && pos < k) {  // NaN scores could select more than k: never write past the row
+      if (t < tokens && sel && pos < k) {  // NaN scores could select more than k: never write past the row
         idx_out[(size_t)t * k + pos] = lane;
         if (counts) atomicAdd(&cnt[lane], 1);
       }
-    } else {
+    }
+  } else {
+    for (int r = wave; r < BM; r += 4) {
+      const int t = t0 + r;
+      if (t >= tokens) break;
+      const float* row = E + r * ES;
+      int base = 0;
       for (int g0 = 0; g0 < groups; g0 += 64) {
         const int g = g0 + lane;
         bool sel = false;
