@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "esg_internal.hpp"
 
@@ -93,6 +94,52 @@ const P* at(const void* base, size_t off) {
 
 hipError_t zero_bytes(void* p, size_t bytes, hipStream_t st) {
   return launch_fill_i32((int32_t*)p, 0, bytes / 4, st);
+}
+
+// A second stream on the current device (default priority, non-blocking) for
+// work that may run beside the caller's stream.  Created on first use, never
+// destroyed; not created while `main` is being captured into a graph (then, and
+// on any failure, nullptr: the caller runs everything on its own stream).
+hipStream_t aux_stream(hipStream_t main) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (streams[dev] == nullptr) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    streams[dev] = s;
+  }
+  return streams[dev];
+}
+
+// Runs a() on `main` and b() on a second stream, both after the work already
+// enqueued on `main`; `main` then waits for b.  Falls back to a() then b() on
+// `main` when no second stream or event is available.  Works under graph
+// capture (the event record / wait pair forks and joins the captured stream).
+template <class A, class B>
+hipError_t fork_join(hipStream_t main, A&& a, B&& b) {
+  hipStream_t aux = aux_stream(main);
+  hipEvent_t forked = nullptr, done = nullptr;
+  if (aux != nullptr && hipEventCreateWithFlags(&forked, hipEventDisableTiming) == hipSuccess) {
+    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) == hipSuccess) {
+      hipError_t e = hipEventRecord(forked, main);
+      if (e == hipSuccess) e = hipStreamWaitEvent(aux, forked, 0);
+      if (e == hipSuccess) e = b(aux);
+      if (e == hipSuccess) e = a(main);
+      if (e == hipSuccess) e = hipEventRecord(done, aux);
+      if (e == hipSuccess) e = hipStreamWaitEvent(main, done, 0);
+      (void)hipEventDestroy(forked);
+      (void)hipEventDestroy(done);
+      return e;
+    }
+    (void)hipEventDestroy(forked);
+  }
+  hipError_t e = a(main);
+  return e == hipSuccess ? b(main) : e;
 }
 
 }  // namespace
@@ -276,13 +323,16 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
                                        at<char>(saved, L.hu), at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
                                        at<char>(scratch, L.b_act), at<char>(scratch, L.b_part), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
-  e = launch_rowsum(s, at<char>(scratch, L.b_part), L.rows, pinv, dx, stream_h);
-  if (e != hipSuccess) return ESG_ERR_HIP;
-  e = v2 ? launch_dw2(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
-                      at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, stream_h)
-         : launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
-                         at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, stream_h);
-  return hip_status(e);
+  // the slot-order sum of dx and the weight gradients only read what dh+dx
+  // wrote: they run side by side
+  auto sum_dx = [&](hipStream_t st) { return launch_rowsum(s, at<char>(scratch, L.b_part), L.rows, pinv, dx, st); };
+  auto weights = [&](hipStream_t st) {
+    return v2 ? launch_dw2(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
+                           at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, st)
+              : launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
+                              at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, st);
+  };
+  return hip_status(fork_join(stream_h, sum_dx, weights));
 }
 
 int esg_update_load_balance_bias(float* bias, float* freq_ema, const float* current_freq, float target_freq,

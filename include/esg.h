@@ -19,7 +19,10 @@
  *    [g*group_size, (g+1)*group_size): rows of w_gate / w_up, columns of
  *    w_down.
  *  - The caller owns every buffer.  The library allocates no device memory and
- *    keeps no state between calls (apart from optional kernel timing); all
+ *    keeps no state between calls (apart from optional kernel timing and one
+ *    auxiliary stream per device, created by the first sparse backward call
+ *    made outside graph capture, on which that call's weight gradients run
+ *    beside the dx sum and are joined back into `stream`); all
  *    scratch comes from caller buffers whose sizes the *_workspace_size calls
  *    give.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
