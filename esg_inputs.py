@@ -183,3 +183,41 @@ def make_mlp_inputs(tokens: int, d_model: int, d_ff: int, seed: int = 0, dtype: 
     dy = torch.randn(tokens, d_model, generator=g)
     td = torch_dtype(dtype)
     return tuple(t.to(td).contiguous() for t in (x, w_up, w_down, dy))
+
+
+# ---------------------------------------------------------------------------
+# FlashFFN multi-head sub-network core.  Recipe: one CPU generator seeded with
+# ``seed``; fp32 draws in the order Q ~ N(0, 1) (unit RMS per head, as after
+# the page's per-head RMS normalisation), R ~ U(0, 2/E) (positive router
+# weights averaging 1/E), K, U ~ N(0, 1/d_h), V ~ N(0, 1/d_e), dO ~ N(0, 1);
+# Q, K, U, V, dO cast to bf16, R kept fp32.  The bench shape is the FlashFFN
+# README's 1.3B configuration (16 heads of 128, 15 sub-networks, intermediate
+# 5760 = 15 x 384 per head) at batch 8 x 2048 tokens.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MhffnWorkload:
+    name: str
+    tokens: int
+    heads: int
+    d_head: int
+    subnets: int
+    d_sub: int
+
+
+MHFFN_WORKLOADS = {
+    "mhffn1p3b": MhffnWorkload("mhffn1p3b", 16384, 16, 128, 15, 384),
+}
+
+
+def make_mhffn_inputs(tokens: int, heads: int, d_head: int, subnets: int, d_sub: int, seed: int = 0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(tokens, heads, d_head, generator=g)
+    r = torch.rand(tokens, heads, subnets, generator=g) * (2.0 / subnets)
+    k = torch.randn(heads, subnets, d_sub, d_head, generator=g) / d_head ** 0.5
+    u = torch.randn(heads, subnets, d_sub, d_head, generator=g) / d_head ** 0.5
+    v = torch.randn(heads, subnets, d_sub, d_head, generator=g) / d_sub ** 0.5
+    do = torch.randn(tokens, heads, d_head, generator=g)
+    bf = torch.bfloat16
+    return (q.to(bf).contiguous(), r.contiguous(), k.to(bf).contiguous(), u.to(bf).contiguous(),
+            v.to(bf).contiguous(), do.to(bf).contiguous())
