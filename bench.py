@@ -54,6 +54,8 @@ def parse():
                     help="time sigmoid top-k routing on a routing workload (route_e256_k8, route_e43_k11) instead")
     ap.add_argument("--mlp", default=None, metavar="WORKLOAD",
                     help="time the LeakyReLU(0.5)^2 MLP fwd+bwd on an MLP workload (leaky_mlp_d512) instead")
+    ap.add_argument("--mhffn", default=None, metavar="WORKLOAD",
+                    help="time the FlashFFN multi-head sub-network core (mhffn1p3b) instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (reference for the HBM counters)")
     return ap.parse_args()
@@ -368,6 +370,103 @@ def mlp_main(args):
     print(json.dumps(line), flush=True)
 
 
+def mhffn_cpu_baseline(q, r, k, u, v, seconds):
+    """The multi-head core oracle (fp64 numpy, as it stands) on consecutive
+    token slices until `seconds` have passed (forward only)."""
+    import numpy as np
+    from oracle import mhffn_oracle as M
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 0) for p in threadpool_info()] or [0]) or os.cpu_count()
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    W = (f64(k), f64(u), f64(v))
+    rows, done, t0 = 128, 0, time.perf_counter()
+    while True:
+        s0 = done % q.shape[0]
+        M.mhffn_forward(f64(q[s0:s0 + rows]), f64(r[s0:s0 + rows]), *W)
+        done += min(rows, q.shape[0] - s0)
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done / el, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} tokens in slices of {rows} (fp64 forward), {el:.1f} s"}
+
+
+def mhffn_main(args):
+    """FlashFFN multi-head sub-network core: one fused forward launch per step."""
+    import torch
+    import esg_inputs as I
+    import group_sparse_swiglu_amd as E
+
+    w = I.MHFFN_WORKLOADS[args.mhffn]
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    E.lib()
+    host = I.make_mhffn_inputs(w.tokens, w.heads, w.d_head, w.subnets, w.d_sub, seed=0)
+    Q, R, K, U, V, _ = (t.to(dev) for t in host)
+    O = torch.empty_like(Q)
+
+    def step():
+        E.mhffn_fwd(Q, R, K, U, V, out=O)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay() if graph is not None else step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    flops = 6.0 * w.tokens * w.heads * w.subnets * w.d_sub * w.d_head
+    peak = PEAK_TFLOPS["bf16"]
+    roofline = None
+    if not args.no_kernel_timing:
+        E.timing_reset()
+        E.timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms, n = E.timing_read("mhffn_fwd")
+        E.timing_enable(False)
+        E.timing_reset()
+        avg = 1e3 * ms / n
+        ach = flops / (avg * 1e-6) / 1e12
+        roofline = {"kernel": "mhffn_fwd", "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": recorded_traffic(w.name, "mhffn_fwd"),
+                    "flops_per_launch": flops, "avg_launch_us": round(avg, 2)}
+    sec = elapsed / args.steps
+    line = {
+        "metric": "FlashFFN multi-head sub-network FFN forward tokens/s",
+        "value": round(w.tokens / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * sec, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "d_head": w.d_head,
+                   "subnets": w.subnets, "d_sub": w.d_sub, "step": "fused forward"},
+        "launch": "hip_graph_replay" if graph is not None else "eager",
+        "active_tflops": round(flops / sec / 1e12, 2), "active_mfma_frac": round(flops / sec / 1e12 / peak, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = mhffn_cpu_baseline(*host[:5], min(args.cpu_seconds, 10.0))
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -382,6 +481,9 @@ def main():
         return
     if args.mlp:
         mlp_main(args)
+        return
+    if args.mhffn:
+        mhffn_main(args)
         return
 
     import torch

@@ -10,7 +10,8 @@ grouped_topk_select, sparse_swiglu_ffn (forward + backward),
 update_load_balance_bias; and, from the Megatron-Core developer guide page
 "core.inference.moe.sigmoid_topk", sigmoid_topk_routing; and, from the
 parameter-golf pull request 1105 page, the LeakyReLU(0.5)^2 MLP with a stored
-activation gradient (leaky_mlp_fwd / leaky_mlp_bwd).
+activation gradient (leaky_mlp_fwd / leaky_mlp_bwd); and, from the FlashFFN
+README, the multi-head sub-network FFN core (mhffn_fwd).
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ __all__ = [
     "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
     "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
     "leaky_mlp_workspace_size", "leaky_mlp_fwd", "leaky_mlp_bwd", "leaky_mlp_saved_views",
+    "mhffn_supported", "mhffn_fwd",
 ]
 
 ESG_F32 = 0
@@ -66,6 +68,8 @@ _SIGNATURES = {
     "esg_leaky_mlp_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_size, _c_vp]),
     "esg_leaky_mlp_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                    _c_vp, _c_size, _c_vp]),
+    "esg_mhffn_supported": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "esg_mhffn_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
     "esg_sigmoid_topk_supported": (_c_int, [_c_int, _c_int]),
     "esg_sigmoid_topk_routing": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_vp, _c_vp,
                                           _c_vp]),
@@ -350,6 +354,25 @@ def leaky_mlp_bwd(dy, x, w_up, w_down, saved, workspace: Optional[dict] = None, 
                                    _dev(dwu, "dw_up", bf), _dev(dwd, "dw_down", bf), _dev(scratch, "scratch"),
                                    scratch.numel(), _stream(x.device)), "leaky_mlp_bwd")
     return dx, dwu, dwd
+
+
+def mhffn_supported(tokens: int, heads: int, d_head: int, subnets: int, d_sub: int) -> bool:
+    return bool(lib().esg_mhffn_supported(tokens, heads, d_head, subnets, d_sub))
+
+
+def mhffn_fwd(q, r, k, u, v, out=None):
+    """O[t,h] = sum_e R[t,h,e] ((SiLU(Q K_e^T) * (Q U_e^T)) V_e) per head.
+    q: bf16 [T, H, d_h]; r: float32 [T, H, E]; k, u, v: bf16 [H, E, d_e, d_h]."""
+    T, H, dh = q.shape
+    _, E, de, _ = k.shape
+    if r.shape != (T, H, E) or u.shape != k.shape or v.shape != k.shape or k.shape[0] != H or k.shape[3] != dh:
+        raise EsgError("shapes: q [T,H,d_h], r [T,H,E], k/u/v [H,E,d_e,d_h]")
+    o = torch.empty_like(q) if out is None else out
+    bf = torch.bfloat16
+    _check(lib().esg_mhffn_fwd(_dev(q, "q", bf), _dev(r, "r", torch.float32), _dev(k, "k", bf), _dev(u, "u", bf),
+                               _dev(v, "v", bf), T, H, dh, E, de, _dev(o, "out", bf), _stream(q.device)),
+           "mhffn_fwd")
+    return o
 
 
 def sigmoid_topk_supported(num_experts: int, topk: int) -> bool:

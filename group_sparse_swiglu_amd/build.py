@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libesg.so")
-SOURCES = ["esg_select.hip", "esg_bucket.hip", "esg_ffn.hip", "esg_ffn_bf16.hip", "esg_dense.hip", "esg_misc.hip", "esg_route.hip", "esg_mlp.hip", "esg_host.cpp",
+SOURCES = ["esg_select.hip", "esg_bucket.hip", "esg_ffn.hip", "esg_ffn_bf16.hip", "esg_dense.hip", "esg_misc.hip", "esg_route.hip", "esg_mlp.hip", "esg_mhffn.hip", "esg_host.cpp",
            "esg_api.cpp"]
 ARCH = os.environ.get("ESG_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -411,6 +411,20 @@ int esg_leaky_mlp_bwd(const void* dy, const void* x, const void* w_up, const voi
                                    part, st));
 }
 
+int esg_mhffn_supported(int tokens, int heads, int d_head, int subnets, int d_sub) {
+  return mhffn_supported(tokens, heads, d_head, subnets, d_sub) ? 1 : 0;
+}
+
+int esg_mhffn_fwd(const void* q, const float* r, const void* k, const void* u, const void* v, int tokens, int heads,
+                  int d_head, int subnets, int d_sub, void* out, void* stream) {
+  if (tokens < 0 || heads <= 0 || subnets <= 0 || d_sub <= 0) return ESG_ERR_INVALID_ARG;
+  if (!mhffn_supported(tokens, heads, d_head, subnets, d_sub)) return ESG_ERR_UNSUPPORTED;
+  if (tokens == 0) return ESG_OK;
+  for (const void* p : {q, (const void*)r, k, u, v, (const void*)out})
+    if (p == nullptr || !aligned16(p)) return ESG_ERR_INVALID_ARG;
+  return hip_status(launch_mhffn_fwd(q, r, k, u, v, tokens, heads, subnets, d_sub, out, (hipStream_t)stream));
+}
+
 int esg_sigmoid_topk_supported(int num_experts, int topk) { return sigmoid_topk_supported(num_experts, topk) ? 1 : 0; }
 
 int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int bias_stride, int tokens,

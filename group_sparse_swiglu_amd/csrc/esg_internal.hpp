@@ -112,6 +112,11 @@ hipError_t launch_mlp_bwd(const void* dy, const void* x, const void* w_up, const
                           int F, const void* post, const void* act_grad, void* dx, void* dw_up, void* dw_down,
                           void* dpre, float* part, hipStream_t stream);
 
+// ---- FlashFFN multi-head sub-network core (esg_mhffn.hip), bf16 ----------------
+bool mhffn_supported(int tokens, int heads, int d_head, int subnets, int d_sub);
+hipError_t launch_mhffn_fwd(const void* q, const float* r, const void* k, const void* u, const void* v, int tokens,
+                            int heads, int subnets, int d_sub, void* out, hipStream_t stream);
+
 // ---- sigmoid top-k routing (esg_route.hip) ------------------------------------
 constexpr int kRouteMaxExperts = 2048;  // 32 experts per lane of one wavefront
 constexpr int kRouteMaxK = 32;

@@ -234,6 +234,28 @@ int esg_leaky_mlp_bwd(const void* dy, const void* x, const void* w_up, const voi
                       size_t scratch_bytes, void* stream);
 
 /*
+ * Multi-head sub-network FFN core of FlashFFN (FlashFFN README, "Overview" and
+ * "Model configurations"): for every token t and head h,
+ *   O[t,h] = sum_e R[t,h,e] * ((SiLU(Q[t,h] K[h,e]^T) * (Q[t,h] U[h,e]^T)) V[h,e])
+ * with per-head sub-networks K, U, V of shape [d_sub, d_head] each.  The fused
+ * forward keeps the [d_sub] intermediate and the fp32 [d_head] output
+ * accumulator on chip; the intermediate, scaled by R, is rounded to bf16
+ * before its product with V.
+ * q, out: device bf16 [tokens, heads, d_head]; r: device float [tokens, heads,
+ * subnets]; k, u, v: device bf16 [heads, subnets, d_sub, d_head].  Q is the
+ * caller's (normalised) head input and R its router weights; producing them,
+ * and the projections around the core, are not part of this call.
+ * out is overwritten; tokens == 0 enqueues nothing.
+ * esg_mhffn_supported returns 1 when d_head == 128, d_sub is a multiple of 8,
+ * subnets <= 32 and every tensor is below 2^31 bytes, else 0.
+ * Errors: ESG_ERR_INVALID_ARG (null or misaligned pointer, negative size),
+ * ESG_ERR_UNSUPPORTED (shape outside esg_mhffn_supported).
+ */
+int esg_mhffn_supported(int tokens, int heads, int d_head, int subnets, int d_sub);
+int esg_mhffn_fwd(const void* q, const float* r, const void* k, const void* u, const void* v, int tokens, int heads,
+                  int d_head, int subnets, int d_sub, void* out, void* stream);
+
+/*
  * Sigmoid top-k routing with an expert bias (Megatron-Core developer guide,
  * "core.inference.moe.sigmoid_topk": the description of _sigmoid_topk_kernel
  * and the API of sigmoid_topk_routing).  Per token row t and expert e:
