@@ -370,9 +370,9 @@ def mlp_main(args):
     print(json.dumps(line), flush=True)
 
 
-def mhffn_cpu_baseline(q, r, k, u, v, seconds):
+def mhffn_cpu_baseline(q, r, k, u, v, do, seconds):
     """The multi-head core oracle (fp64 numpy, as it stands) on consecutive
-    token slices until `seconds` have passed (forward only)."""
+    token slices until `seconds` have passed: forward and backward."""
     import numpy as np
     from oracle import mhffn_oracle as M
     try:
@@ -382,20 +382,26 @@ def mhffn_cpu_baseline(q, r, k, u, v, seconds):
         cores = os.cpu_count()
     f64 = lambda t: t.float().numpy().astype(np.float64)
     W = (f64(k), f64(u), f64(v))
-    rows, done, t0 = 128, 0, time.perf_counter()
+    rows, done, t0 = 64, 0, time.perf_counter()
     while True:
         s0 = done % q.shape[0]
-        M.mhffn_forward(f64(q[s0:s0 + rows]), f64(r[s0:s0 + rows]), *W)
-        done += min(rows, q.shape[0] - s0)
+        qs, rs, ds = f64(q[s0:s0 + rows]), f64(r[s0:s0 + rows]), f64(do[s0:s0 + rows])
+        M.mhffn_forward(qs, rs, *W)
+        M.mhffn_backward(ds, qs, rs, *W)
+        done += qs.shape[0]
         el = time.perf_counter() - t0
         if el >= seconds:
             break
     return {"value": round(done / el, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} tokens in slices of {rows} (fp64 forward), {el:.1f} s"}
+            "sample": f"{done} tokens in slices of {rows} (fp64 forward + backward), {el:.1f} s"}
+
+
+MHFFN_KERNEL_UNITS = {"mhffn_fwd": 6, "mhffn_bwd_dq": 6, "mhffn_bwd_dw": 6}   # x tokens*heads*E*d_sub*d_head
 
 
 def mhffn_main(args):
-    """FlashFFN multi-head sub-network core: one fused forward launch per step."""
+    """FlashFFN multi-head sub-network core: fused forward, then the backward
+    (dQ/dR kernel and weight-gradient kernel, both recomputing) per step."""
     import torch
     import esg_inputs as I
     import group_sparse_swiglu_amd as E
@@ -407,11 +413,13 @@ def mhffn_main(args):
     torch.cuda.set_device(dev)
     E.lib()
     host = I.make_mhffn_inputs(w.tokens, w.heads, w.d_head, w.subnets, w.d_sub, seed=0)
-    Q, R, K, U, V, _ = (t.to(dev) for t in host)
+    Q, R, K, U, V, DO = (t.to(dev) for t in host)
     O = torch.empty_like(Q)
+    GR = (torch.empty_like(Q), torch.empty_like(R), torch.empty_like(K), torch.empty_like(U), torch.empty_like(V))
 
     def step():
         E.mhffn_fwd(Q, R, K, U, V, out=O)
+        E.mhffn_bwd(DO, Q, R, K, U, V, outs=GR)
 
     for _ in range(args.warmup):
         step()
@@ -433,37 +441,46 @@ def mhffn_main(args):
         graph.replay() if graph is not None else step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    flops = 6.0 * w.tokens * w.heads * w.subnets * w.d_sub * w.d_head
+    unit = float(w.tokens) * w.heads * w.subnets * w.d_sub * w.d_head
+    active = 18.0 * unit      # forward 6 units, backward 12 (recompute not credited)
     peak = PEAK_TFLOPS["bf16"]
-    roofline = None
+    roofline, per_kernel = None, {}
     if not args.no_kernel_timing:
         E.timing_reset()
         E.timing_enable(True)
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
-        ms, n = E.timing_read("mhffn_fwd")
+        for k_ in MHFFN_KERNEL_UNITS:
+            ms, n = E.timing_read(k_)
+            if n:
+                per_kernel[k_] = 1e3 * ms / n
         E.timing_enable(False)
         E.timing_reset()
-        avg = 1e3 * ms / n
-        ach = flops / (avg * 1e-6) / 1e12
-        roofline = {"kernel": "mhffn_fwd", "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": recorded_traffic(w.name, "mhffn_fwd"),
-                    "flops_per_launch": flops, "avg_launch_us": round(avg, 2)}
+        dom = max(per_kernel, key=per_kernel.get)
+        flops = MHFFN_KERNEL_UNITS[dom] * unit
+        ach = flops / (per_kernel[dom] * 1e-6) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": recorded_traffic(w.name, dom), "flops_per_launch": flops,
+                    "avg_launch_us": round(per_kernel[dom], 2)}
     sec = elapsed / args.steps
     line = {
-        "metric": "FlashFFN multi-head sub-network FFN forward tokens/s",
+        "metric": "FlashFFN multi-head sub-network FFN fwd+bwd tokens/s",
         "value": round(w.tokens / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(1e3 * sec, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "heads": w.heads, "d_head": w.d_head,
-                   "subnets": w.subnets, "d_sub": w.d_sub, "step": "fused forward"},
+                   "subnets": w.subnets, "d_sub": w.d_sub, "step": "fused forward, dQ/dR, dK/dU/dV"},
         "launch": "hip_graph_replay" if graph is not None else "eager",
-        "active_tflops": round(flops / sec / 1e12, 2), "active_mfma_frac": round(flops / sec / 1e12 / peak, 4),
+        "active_tflops": round(active / sec / 1e12, 2), "active_mfma_frac": round(active / sec / 1e12 / peak, 4),
         "roofline": roofline,
     }
+    if per_kernel:
+        line["kernels_us_per_step"] = {k_: round(v_, 2) for k_, v_ in per_kernel.items()}
+        line["kernels_algorithmic_tflops"] = {k_: round(MHFFN_KERNEL_UNITS[k_] * unit / (v_ * 1e-6) / 1e12, 1)
+                                              for k_, v_ in per_kernel.items()}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = mhffn_cpu_baseline(*host[:5], min(args.cpu_seconds, 10.0))
+        line["cpu_baseline"] = mhffn_cpu_baseline(*host, min(args.cpu_seconds, 10.0))
     print(json.dumps(line), flush=True)
 
 

@@ -11,7 +11,7 @@ update_load_balance_bias; and, from the Megatron-Core developer guide page
 "core.inference.moe.sigmoid_topk", sigmoid_topk_routing; and, from the
 parameter-golf pull request 1105 page, the LeakyReLU(0.5)^2 MLP with a stored
 activation gradient (leaky_mlp_fwd / leaky_mlp_bwd); and, from the FlashFFN
-README, the multi-head sub-network FFN core (mhffn_fwd).
+README, the multi-head sub-network FFN core (mhffn_fwd / mhffn_bwd).
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ __all__ = [
     "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
     "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
     "leaky_mlp_workspace_size", "leaky_mlp_fwd", "leaky_mlp_bwd", "leaky_mlp_saved_views",
-    "mhffn_supported", "mhffn_fwd",
+    "mhffn_supported", "mhffn_fwd", "mhffn_bwd",
 ]
 
 ESG_F32 = 0
@@ -70,6 +70,8 @@ _SIGNATURES = {
                                    _c_vp, _c_size, _c_vp]),
     "esg_mhffn_supported": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "esg_mhffn_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
+    "esg_mhffn_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp,
+                               _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "esg_sigmoid_topk_supported": (_c_int, [_c_int, _c_int]),
     "esg_sigmoid_topk_routing": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_vp, _c_vp,
                                           _c_vp]),
@@ -373,6 +375,22 @@ def mhffn_fwd(q, r, k, u, v, out=None):
                                _dev(v, "v", bf), T, H, dh, E, de, _dev(o, "out", bf), _stream(q.device)),
            "mhffn_fwd")
     return o
+
+
+def mhffn_bwd(dout, q, r, k, u, v, outs=None):
+    """(dQ, dR, dK, dU, dV) of the multi-head core (overwritten)."""
+    T, H, dh = q.shape
+    _, E, de, _ = k.shape
+    if outs is None:
+        outs = (torch.empty_like(q), torch.empty_like(r), torch.empty_like(k), torch.empty_like(u),
+                torch.empty_like(v))
+    dq, dr, dk, du, dv = outs
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(lib().esg_mhffn_bwd(_dev(dout, "dout", bf), _dev(q, "q", bf), _dev(r, "r", f32), _dev(k, "k", bf),
+                               _dev(u, "u", bf), _dev(v, "v", bf), T, H, dh, E, de, _dev(dq, "dq", bf),
+                               _dev(dr, "dr", f32), _dev(dk, "dk", bf), _dev(du, "du", bf), _dev(dv, "dv", bf),
+                               _stream(k.device)), "mhffn_bwd")
+    return dq, dr, dk, du, dv
 
 
 def sigmoid_topk_supported(num_experts: int, topk: int) -> bool:

@@ -425,6 +425,20 @@ int esg_mhffn_fwd(const void* q, const float* r, const void* k, const void* u, c
   return hip_status(launch_mhffn_fwd(q, r, k, u, v, tokens, heads, subnets, d_sub, out, (hipStream_t)stream));
 }
 
+int esg_mhffn_bwd(const void* dout, const void* q, const float* r, const void* k, const void* u, const void* v,
+                  int tokens, int heads, int d_head, int subnets, int d_sub, void* dq, float* dr, void* dk, void* du,
+                  void* dv, void* stream) {
+  if (tokens < 0 || heads <= 0 || subnets <= 0 || d_sub <= 0) return ESG_ERR_INVALID_ARG;
+  if (!mhffn_supported(tokens, heads, d_head, subnets, d_sub)) return ESG_ERR_UNSUPPORTED;
+  for (const void* p : {k, u, v, (const void*)dk, (const void*)du, (const void*)dv})
+    if (p == nullptr || !aligned16(p)) return ESG_ERR_INVALID_ARG;
+  if (tokens > 0)
+    for (const void* p : {dout, q, (const void*)r, (const void*)dq, (const void*)dr})
+      if (p == nullptr || !aligned16(p)) return ESG_ERR_INVALID_ARG;
+  return hip_status(launch_mhffn_bwd(dout, q, r, k, u, v, tokens, heads, subnets, d_sub, dq, dr, dk, du, dv,
+                                     (hipStream_t)stream));
+}
+
 int esg_sigmoid_topk_supported(int num_experts, int topk) { return sigmoid_topk_supported(num_experts, topk) ? 1 : 0; }
 
 int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int bias_stride, int tokens,

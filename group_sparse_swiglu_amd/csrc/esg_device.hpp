@@ -151,6 +151,16 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[FM][FN]) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
+template <int N>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+template <int A, int B, int C>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[A][B][C]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i) zero_acc(acc[i]);
+}
 
 // ---------------------------------------------------------------------------
 // Loaders: global -> registers (load) -> LDS (store), for one K-stage of KC

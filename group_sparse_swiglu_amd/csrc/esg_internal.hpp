@@ -116,6 +116,9 @@ hipError_t launch_mlp_bwd(const void* dy, const void* x, const void* w_up, const
 bool mhffn_supported(int tokens, int heads, int d_head, int subnets, int d_sub);
 hipError_t launch_mhffn_fwd(const void* q, const float* r, const void* k, const void* u, const void* v, int tokens,
                             int heads, int subnets, int d_sub, void* out, hipStream_t stream);
+hipError_t launch_mhffn_bwd(const void* dout, const void* q, const float* r, const void* k, const void* u,
+                            const void* v, int tokens, int heads, int subnets, int d_sub, void* dq, float* dr,
+                            void* dk, void* du, void* dv, hipStream_t stream);
 
 // ---- sigmoid top-k routing (esg_route.hip) ------------------------------------
 constexpr int kRouteMaxExperts = 2048;  // 32 experts per lane of one wavefront

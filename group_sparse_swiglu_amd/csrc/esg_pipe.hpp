@@ -135,6 +135,21 @@ __device__ __forceinline__ uint4 frag_nrow(const ESG_LDS char* t, int kb, int n0
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// The same transposed fragment (columns m0..m0+15, K rows kb*32 ..) read from
+// a K-row tile (128-byte rows, K-row swizzle): the tile's rows are taken as
+// the K index and its 64 columns as the M/N index.  Used where one staged
+// tile is an operand both along and across its rows.
+__device__ __forceinline__ uint4 frag_krow_t(const ESG_LDS char* t, int kb, int m0, int lane) {
+  const int q = lane >> 4, i = lane & 15;
+  const int row = kb * 32 + q * 8 + (i >> 2);
+  const int colb = m0 * 2 + (i & 3) * 8;  // byte column addressed by this lane (within one 16-byte chunk)
+  const int c = colb >> 4, half = colb & 15;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + krow_off(row, c) + half));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + krow_off(row + 4, c) + half));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 __device__ __forceinline__ void mma_bf16(f32x4& acc, const uint4& a, const uint4& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                acc, 0, 0, 0);

@@ -254,6 +254,21 @@ int esg_leaky_mlp_bwd(const void* dy, const void* x, const void* w_up, const voi
 int esg_mhffn_supported(int tokens, int heads, int d_head, int subnets, int d_sub);
 int esg_mhffn_fwd(const void* q, const float* r, const void* k, const void* u, const void* v, int tokens, int heads,
                   int d_head, int subnets, int d_sub, void* out, void* stream);
+/*
+ * Gradients of the same core given dout = dL/dO [tokens, heads, d_head]
+ * (bf16): dq (bf16, like q), dr (float, like r), dk, du, dv (bf16, like k).
+ * All are overwritten (tokens == 0: dk, du, dv zero, nothing else written).
+ * Nothing is saved by the forward: both backward kernels recompute the
+ * sub-networks' pre-activations.  Per token t, head h, sub-network e, with
+ * a = SiLU(h1) h2 and g = dO V^T: dR = sum_n a g; da = R g; dh2 = da SiLU(h1);
+ * dh1 = da h2 SiLU'(h1); dQ = sum_e (dh1 K + dh2 U); dK = dh1^T Q;
+ * dU = dh2^T Q; dV = (R a)^T dO.  dh1, dh2 and R a are rounded to bf16 before
+ * their products; sums over tokens and sub-networks run in fp32 in a fixed
+ * order (deterministic).  Same shape rules and errors as esg_mhffn_fwd.
+ */
+int esg_mhffn_bwd(const void* dout, const void* q, const float* r, const void* k, const void* u, const void* v,
+                  int tokens, int heads, int d_head, int subnets, int d_sub, void* dq, float* dr, void* dk, void* du,
+                  void* dv, void* stream);
 
 /*
  * Sigmoid top-k routing with an expert bias (Megatron-Core developer guide,
