@@ -213,43 +213,53 @@ __global__ __launch_bounds__(MH_NT, 1) void mhffn_fwd_kernel(const bf16_t* __res
 
 // ===========================================================================
 // Backward.  Nothing [tokens, sub-networks, d_sub]-sized is kept by the
-// forward, so both kernels recompute h1, h2 and g = dO . V^T per chunk of 48
-// neurons (one 36 KB stage holds the chunk's [K; U; V] rows over all of d_h,
-// as two 64-column K-row sub-tiles):
+// forward, so both kernels recompute h1, h2 and g = dO . V^T per chunk of
+// neurons (a chunk's [K; U; V] rows over all of d_h sit in one stage as two
+// 64-column K-row sub-tiles):
 //   per token:   a = SiLU(h1) h2;  dR[t,e] = sum_n a g;  da = R g;
 //                dh2 = da SiLU(h1);  dh1 = da h2 SiLU'(h1)
-//   dQ/dR kernel (per head and 64 tokens; four wavefronts of 16 tokens):
+//   dQ/dR kernel (per head and 64 tokens; four wavefronts of 16 tokens;
+//                chunks of 32 neurons through a three-stage ring):
 //                dQ^T += [K; U]^T [dh1 dh2]^T, the stage's K and U rows read
 //                transposed (rows = neuron = the K index, columns = d_h);
 //                dQ accumulates in registers, dR in LDS, both over all chunks
-//   dW kernel    (per head, sub-network and 48-neuron chunk, all tokens in
+//   dW kernel    (per head, sub-network and 48-neuron chunk held in LDS, all tokens in
 //                steps of 64): dK^T += Q^T dh1, dU^T += Q^T dh2,
 //                dV^T += dO^T (R a), the Q / dO tiles and the per-step
 //                [token][neuron] tiles read transposed
 // ===========================================================================
 constexpr int MB_TM = 64;                 // tokens per tile
-constexpr int MB_NC = 48;                 // neurons per chunk
-constexpr int MB_ROWS = 3 * MB_NC;        // [K; U; V] rows of a chunk
-constexpr int MB_HALF = MB_ROWS * 128;    // one 64-column sub-tile of the chunk (18 KB)
-constexpr int MB_STAGE = 2 * MB_HALF;     // the chunk over all of d_h (36 KB)
 constexpr int MB_TSUB = MB_TM * 128;      // one 64-wide K-row sub-tile of a 64-token tile (8 KB)
 constexpr int MB_NW = 4;
-constexpr int MB_LW = MB_STAGE / 1024 / MB_NW;  // DMA instructions per lane for a chunk stage (9)
-static_assert(MB_STAGE % (1024 * MB_NW) == 0, "whole DMA instructions per wave");
 
-// DMA of one chunk's [K; U; V] rows (neurons n0 .. n0+47 of sub-network e) into
-// a 36 KB stage: instruction ii covers sub-tile ii/18, rows (ii%18)*8 .. +7.
+// A chunk of NC neurons of one sub-network: its [K; U; V] rows over all of
+// d_h as two 64-column K-row sub-tiles.
+template <int NC>
+struct Chunk {
+  static constexpr int ROWS = 3 * NC;
+  static constexpr int FR = ROWS / 16;           // 16-row fragments: K, U, V in turn
+  static constexpr int HALF = ROWS * 128;        // one 64-column sub-tile
+  static constexpr int STAGE = 2 * HALF;
+  static constexpr int LW = STAGE / 1024 / MB_NW;  // DMA instructions per lane
+  static_assert(NC % 16 == 0 && STAGE % (1024 * MB_NW) == 0, "whole fragments and DMA instructions");
+};
+
+// DMA of one chunk's [K; U; V] rows (neurons n0 .. n0+NC-1 of the sub-network
+// at `base`): instruction ii covers sub-tile ii/(ROWS/8), rows (ii%(ROWS/8))*8 .. +7.
+template <int NC>
 __device__ __forceinline__ void issue_chunk(const DmaSrc& rk, const DmaSrc& ru, const DmaSrc& rv, ESG_LDS char* st,
                                             int w, int lane, uint32_t base, int n0, int d_sub) {
+  using C = Chunk<NC>;
+  constexpr int PER = C::ROWS / 8;
   const int c8 = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-  for (int i = 0; i < MB_LW; ++i) {
-    const int ii = w * MB_LW + i;
-    const int sub = ii / 18, rb = (ii % 18) * 8;
-    const int mat = rb / MB_NC;  // 0 K, 1 U, 2 V (wave-uniform: 8-row blocks never straddle)
-    const int n = n0 + rb % MB_NC + (lane >> 3);
+  for (int i = 0; i < C::LW; ++i) {
+    const int ii = w * C::LW + i;
+    const int sub = ii / PER, rb = (ii % PER) * 8;
+    const int mat = rb / NC;  // 0 K, 1 U, 2 V (wave-uniform: 8-row blocks never straddle)
+    const int n = n0 + rb % NC + (lane >> 3);
     const uint32_t off = n < d_sub ? base + (uint32_t)n * MH_DH * 2 + sub * 128 + c8 * 16 : kOOB;
-    dma16(mat == 0 ? rk : (mat == 1 ? ru : rv), st + sub * MB_HALF + (ii % 18) * 1024, off);
+    dma16(mat == 0 ? rk : (mat == 1 ? ru : rv), st + sub * C::HALF + (ii % PER) * 1024, off);
   }
 }
 
@@ -268,10 +278,12 @@ __device__ __forceinline__ void issue_tokens(const DmaSrc& src, ESG_LDS char* ds
   }
 }
 
-// Phase 1 of a chunk for the 16 tokens [tok0, +16): acc[f] (f = 0..8: K, U, V
-// row fragments of 16) = stage rows . [Q | Q | dO]^T over all of d_h.
+// Phase 1 of a chunk for the 16 tokens [tok0, +16): acc[f] (K, U, V row
+// fragments in turn) = stage rows . [Q | Q | dO]^T over all of d_h.
+template <int NC>
 __device__ __forceinline__ void chunk_phase1(const ESG_LDS char* st, const ESG_LDS char* qt, const ESG_LDS char* dot,
-                                             int tok0, int lane, f32x4 (&acc)[9]) {
+                                             int tok0, int lane, f32x4 (&acc)[Chunk<NC>::FR]) {
+  using C = Chunk<NC>;
   zero_acc(acc);
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
@@ -281,9 +293,9 @@ __device__ __forceinline__ void chunk_phase1(const ESG_LDS char* st, const ESG_L
       const uint4 bq = frag_krow(qt + sub * MB_TSUB, tok0 + (lane & 15), c);
       const uint4 bo = frag_krow(dot + sub * MB_TSUB, tok0 + (lane & 15), c);
 #pragma unroll
-      for (int f = 0; f < 9; ++f) {
-        const uint4 a = frag_krow(st + sub * MB_HALF, f * 16 + (lane & 15), c);
-        mma_bf16(acc[f], a, f < 6 ? bq : bo);
+      for (int f = 0; f < C::FR; ++f) {
+        const uint4 a = frag_krow(st + sub * C::HALF, f * 16 + (lane & 15), c);
+        mma_bf16(acc[f], a, f < 2 * C::FR / 3 ? bq : bo);
       }
     }
 }
@@ -294,13 +306,15 @@ struct ChunkGrads {
   float dr;
   uint32_t dh1[2], dh2[2], ra[2];
 };
-__device__ __forceinline__ ChunkGrads chunk_grads(const f32x4 (&acc)[9], int p, float rw) {
+template <int NC>
+__device__ __forceinline__ ChunkGrads chunk_grads(const f32x4 (&acc)[Chunk<NC>::FR], int p, float rw) {
+  constexpr int F1 = NC / 16;
   ChunkGrads o;
   float d1[4], d2[4], ra[4];
   o.dr = 0.0f;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const float h1 = acc[p][x], h2 = acc[3 + p][x], g = acc[6 + p][x];
+    const float h1 = acc[p][x], h2 = acc[F1 + p][x], g = acc[2 * F1 + p][x];
     const float sg = sigmoid_f(h1);
     const float silu = h1 * sg;
     const float a = silu * h2;
@@ -319,14 +333,20 @@ __device__ __forceinline__ ChunkGrads chunk_grads(const f32x4 (&acc)[9], int p, 
   return o;
 }
 
+// chunk widths: 32 neurons for the dQ/dR kernel (three 24 KB ring stages fit
+// beside its resident tiles), 48 for the weight-gradient kernel (its chunk is
+// resident; wider chunks mean fewer passes over the tokens)
+constexpr int MBQ_NC = 32, MBW_NC = 48;
+
 __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ q, const float* __restrict__ r,
     const bf16_t* __restrict__ kw, const bf16_t* __restrict__ uw, const bf16_t* __restrict__ vw, int tokens,
     int heads, int subnets, int d_sub, bf16_t* __restrict__ dq, float* __restrict__ dr) {
-  __shared__ __attribute__((aligned(1024))) char ring_[2 * MB_STAGE];
+  using C = Chunk<MBQ_NC>;
+  __shared__ __attribute__((aligned(1024))) char ring_[3 * C::STAGE];
   __shared__ __attribute__((aligned(1024))) char qt_[2 * MB_TSUB];
   __shared__ __attribute__((aligned(1024))) char dot_[2 * MB_TSUB];
-  __shared__ __attribute__((aligned(1024))) char dh_[2 * MB_TSUB];  // [token][dh1 (48) | dh2 (48)]
+  __shared__ __attribute__((aligned(1024))) char dh_[MB_TSUB];  // [token][dh1 (32) | dh2 (32)]
   __shared__ float rtab[MB_TM * MH_MAXE];
   __shared__ float drtab[MB_TM * MH_MAXE];
   ESG_LDS char* ring = (ESG_LDS char*)ring_;
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
 
   const int h = blockIdx.y, t0 = blockIdx.x * MB_TM;
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int nchunks = (d_sub + MB_NC - 1) / MB_NC;
+  const int nchunks = (d_sub + MBQ_NC - 1) / MBQ_NC;
   const uint32_t qrow = (uint32_t)heads * MH_DH * 2;
   const uint32_t wbytes_he = (uint32_t)d_sub * MH_DH * 2;
   const uint32_t wtotal = (uint32_t)heads * subnets * wbytes_he;
@@ -351,26 +371,26 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
   issue_tokens(make_dma_src(dout, (uint32_t)tokens * qrow), dot, w, lane, t0, tokens, qrow, h);
 
   const int tok0 = w * 16, tl = tok0 + (lane & 15);  // the wave's tokens; this lane's token
-  f32x4 acc1[9];
+  f32x4 acc1[C::FR];
   f32x4 acc2[8];  // dQ^T: d_h fragments x the wave's 16 tokens
   zero_acc(acc2);
   auto issue = [&](ESG_LDS char* st, int s) __attribute__((always_inline)) {
-    const int e = s / nchunks, n0 = (s % nchunks) * MB_NC;
-    issue_chunk(rk, ru, rv, st, w, lane, (uint32_t)(h * subnets + e) * wbytes_he, n0, d_sub);
+    const int e = s / nchunks, n0 = (s % nchunks) * MBQ_NC;
+    issue_chunk<MBQ_NC>(rk, ru, rv, st, w, lane, (uint32_t)(h * subnets + e) * wbytes_he, n0, d_sub);
   };
   auto compute = [&](const ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int e = s / nchunks;
-    chunk_phase1(st, qt, dot, tok0, lane, acc1);
+    chunk_phase1<MBQ_NC>(st, qt, dot, tok0, lane, acc1);
     const float rw = rtab[tl * subnets + e];
     float drp = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const ChunkGrads cg = chunk_grads(acc1, p, rw);
+    for (int p = 0; p < MBQ_NC / 16; ++p) {
+      const ChunkGrads cg = chunk_grads<MBQ_NC>(acc1, p, rw);
       drp += cg.dr;
-      const int n = p * 16 + (lane >> 4) * 4;  // dh1 column n, dh2 column 48 + n
+      const int n = p * 16 + (lane >> 4) * 4;  // dh1 column n, dh2 column 32 + n
       lds_write8(dh + krow_off(tl, n >> 3) + (n & 7) * 2, cg.dh1[0], cg.dh1[1]);
-      const int n2 = MB_NC + n;
-      lds_write8(dh + (n2 >> 6) * MB_TSUB + krow_off(tl, (n2 & 63) >> 3) + (n2 & 7) * 2, cg.dh2[0], cg.dh2[1]);
+      const int n2 = MBQ_NC + n;
+      lds_write8(dh + krow_off(tl, n2 >> 3) + (n2 & 7) * 2, cg.dh2[0], cg.dh2[1]);
     }
     drp += __shfl_xor(drp, 16);
     drp += __shfl_xor(drp, 32);
@@ -379,18 +399,19 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // dQ^T += [K; U]^T [dh1 dh2]^T  (K index = the 96 neuron rows of the stage)
+    // dQ^T += [K; U]^T [dh1 dh2]^T  (K index = the 64 K and U neuron rows of the stage)
 #pragma unroll
-    for (int kb = 0; kb < 3; ++kb) {
-      const uint4 b = frag_krow(dh + (kb >> 1) * MB_TSUB, tl, (kb & 1) * 4 + (lane >> 4));
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4 b = frag_krow(dh, tl, kb * 4 + (lane >> 4));
 #pragma unroll
       for (int jf = 0; jf < 8; ++jf) {
-        const uint4 a = frag_krow_t(st + (jf >> 2) * MB_HALF, kb, (jf & 3) * 16, lane);
+        const uint4 a = frag_krow_t(st + (jf >> 2) * C::HALF, kb, (jf & 3) * 16, lane);
         mma_bf16(acc2[jf], a, b);
       }
     }
   };
-  kloop<2, MB_LW, 0>(subnets * nchunks, ring, ring + MB_STAGE, ring, issue, compute);
+  // the Q and dO tiles' loads are older than the ring's: the first wait covers them
+  kloop<3, C::LW, 0>(subnets * nchunks, ring, ring + C::STAGE, ring + 2 * C::STAGE, issue, compute);
   wait_lgkm0();
   barrier();
 
@@ -415,8 +436,9 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ q, const float* __restrict__ r,
     const bf16_t* __restrict__ kw, const bf16_t* __restrict__ uw, const bf16_t* __restrict__ vw, int tokens,
     int heads, int subnets, int d_sub, bf16_t* __restrict__ dk, bf16_t* __restrict__ du, bf16_t* __restrict__ dv) {
+  using C = Chunk<MBW_NC>;
   constexpr int TSTAGE = 4 * MB_TSUB + 1024;  // Q (2 sub-tiles), dO (2), router weights (4 x 256 B)
-  __shared__ __attribute__((aligned(1024))) char wt_[MB_STAGE];
+  __shared__ __attribute__((aligned(1024))) char wt_[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char ring_[3 * TSTAGE];
   __shared__ __attribute__((aligned(1024))) char tiles_[3 * MB_TSUB];  // [token][48] dh1 | dh2 | R*a
   ESG_LDS char* wt = (ESG_LDS char*)wt_;
@@ -425,14 +447,14 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
   ESG_LDS char* t_dh2 = t_dh1 + MB_TSUB;
   ESG_LDS char* t_ra = t_dh2 + MB_TSUB;
 
-  const int n0 = blockIdx.x * MB_NC, e = blockIdx.y, h = blockIdx.z;
+  const int n0 = blockIdx.x * MBW_NC, e = blockIdx.y, h = blockIdx.z;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t qrow = (uint32_t)heads * MH_DH * 2;
   const uint32_t wbytes_he = (uint32_t)d_sub * MH_DH * 2;
   const uint32_t wtotal = (uint32_t)heads * subnets * wbytes_he;
   const uint32_t base = (uint32_t)(h * subnets + e) * wbytes_he;
-  issue_chunk(make_dma_src(kw, wtotal), make_dma_src(uw, wtotal), make_dma_src(vw, wtotal), wt, w, lane, base, n0,
-              d_sub);
+  issue_chunk<MBW_NC>(make_dma_src(kw, wtotal), make_dma_src(uw, wtotal), make_dma_src(vw, wtotal), wt, w, lane, base,
+                      n0, d_sub);
   const DmaSrc rq = make_dma_src(q, (uint32_t)tokens * qrow);
   const DmaSrc ro = make_dma_src(dout, (uint32_t)tokens * qrow);
   const DmaSrc rr = make_dma_src(r, (uint32_t)tokens * heads * subnets * 4);
@@ -450,15 +472,15 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
   // phase 2 wave tile: d_h [w*32, +32) x the chunk's 48 neurons, for dK, dU, dV
   f32x4 acc2[3][2][3];
   zero_acc(acc2);
-  f32x4 acc1[9];
+  f32x4 acc1[C::FR];
   auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
     const ESG_LDS char* qs = st;
     const ESG_LDS char* os = st + 2 * MB_TSUB;
-    chunk_phase1(wt, qs, os, tok0, lane, acc1);
+    chunk_phase1<MBW_NC>(wt, qs, os, tok0, lane, acc1);
     const float rw = *(const ESG_LDS float*)(st + 4 * MB_TSUB + w * 256 + (lane & 15) * 4);
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
-      const ChunkGrads cg = chunk_grads(acc1, p, rw);
+      const ChunkGrads cg = chunk_grads<MBW_NC>(acc1, p, rw);
       const int n = p * 16 + (lane >> 4) * 4;
       const int o = krow_off(tl, n >> 3) + (n & 7) * 2;
       lds_write8(t_dh1 + o, cg.dh1[0], cg.dh1[1]);
@@ -536,7 +558,7 @@ hipError_t launch_mhffn_bwd(const void* dout, const void* q, const float* r, con
     if (e != hipSuccess) return e;
   }
   LaunchTimer timer("mhffn_bwd_dw", stream);
-  hipLaunchKernelGGL(mhffn_bwd_dw_kernel, dim3((d_sub + MB_NC - 1) / MB_NC, subnets, heads), dim3(NT), 0, stream,
+  hipLaunchKernelGGL(mhffn_bwd_dw_kernel, dim3((d_sub + MBW_NC - 1) / MBW_NC, subnets, heads), dim3(NT), 0, stream,
                      (const bf16_t*)dout, (const bf16_t*)q, r, (const bf16_t*)k, (const bf16_t*)u, (const bf16_t*)v,
                      tokens, heads, subnets, d_sub, (bf16_t*)dk, (bf16_t*)du, (bf16_t*)dv);
   return hipGetLastError();
