@@ -473,10 +473,32 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
   f32x4 acc2[3][2][3];
   zero_acc(acc2);
   f32x4 acc1[C::FR];
-  auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
+  // the resident chunk's phase-1 fragments, read from LDS once (step 0) and
+  // kept in registers: [d_h sub-tile][32-wide K block][row fragment]
+  uint4 wf[2][2][C::FR];
+  auto compute = [&](const ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const ESG_LDS char* qs = st;
     const ESG_LDS char* os = st + 2 * MB_TSUB;
-    chunk_phase1<MBW_NC>(wt, qs, os, tok0, lane, acc1);
+    if (s == 0) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int f = 0; f < C::FR; ++f)
+            wf[sub][kb][f] = frag_krow(wt + sub * C::HALF, f * 16 + (lane & 15), kb * 4 + (lane >> 4));
+    }
+    zero_acc(acc1);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int c = kb * 4 + (lane >> 4);
+        const uint4 bq = frag_krow(qs + sub * MB_TSUB, tl, c);
+        const uint4 bo = frag_krow(os + sub * MB_TSUB, tl, c);
+#pragma unroll
+        for (int f = 0; f < C::FR; ++f) mma_bf16(acc1[f], wf[sub][kb][f], f < 2 * C::FR / 3 ? bq : bo);
+      }
     const float rw = *(const ESG_LDS float*)(st + 4 * MB_TSUB + w * 256 + (lane & 15) * 4);
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
