@@ -221,8 +221,9 @@ __global__ __launch_bounds__(MH_NT, 1) void mhffn_fwd_kernel(const bf16_t* __res
 //   dQ/dR kernel (per head and 64 tokens; four wavefronts of 16 tokens;
 //                chunks of 32 neurons through a three-stage ring):
 //                dQ^T += [K; U]^T [dh1 dh2]^T, the stage's K and U rows read
-//                transposed (rows = neuron = the K index, columns = d_h);
-//                dQ accumulates in registers, dR in LDS, both over all chunks
+//                transposed (rows = neuron = the K index, columns = d_h),
+//                each wave a 32-wide d_h slice for all 64 tokens; dQ
+//                accumulates in registers, dR in LDS, both over all chunks
 //   dW kernel    (per head, sub-network and 48-neuron chunk held in LDS, all tokens in
 //                steps of 64): dK^T += Q^T dh1, dU^T += Q^T dh2,
 //                dV^T += dO^T (R a), the Q / dO tiles and the per-step
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
 
   const int tok0 = w * 16, tl = tok0 + (lane & 15);  // the wave's tokens; this lane's token
   f32x4 acc1[C::FR];
-  f32x4 acc2[8];  // dQ^T: d_h fragments x the wave's 16 tokens
+  f32x4 acc2[2][4];  // dQ^T: d_h [w*32, +32) x the tile's 4 token fragments
   zero_acc(acc2);
   auto issue = [&](ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int e = s / nchunks, n0 = (s % nchunks) * MBQ_NC;
@@ -395,19 +396,24 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
     drp += __shfl_xor(drp, 16);
     drp += __shfl_xor(drp, 32);
     if (lane < 16) drtab[tl * subnets + e] += drp;  // the wave owns these tokens: no other writer
-    // the wave reads back only its own dh rows: a wavefront-level LDS fence suffices
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // dQ^T += [K; U]^T [dh1 dh2]^T  (K index = the 64 K and U neuron rows of the stage)
+    wait_lgkm0();
+    barrier();  // every wave's dh rows are written
+    // dQ^T += [K; U]^T [dh1 dh2]^T  (K index = the 64 K and U neuron rows of the
+    // stage); wave w takes d_h [w*32, +32) for all 64 tokens
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint4 b = frag_krow(dh, tl, kb * 4 + (lane >> 4));
+      uint4 a[2], b[4];
 #pragma unroll
-      for (int jf = 0; jf < 8; ++jf) {
-        const uint4 a = frag_krow_t(st + (jf >> 2) * C::HALF, kb, (jf & 3) * 16, lane);
-        mma_bf16(acc2[jf], a, b);
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jf = 2 * w + jj;
+        a[jj] = frag_krow_t(st + (jf >> 2) * C::HALF, kb, (jf & 3) * 16, lane);
       }
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) b[tf] = frag_krow(dh, tf * 16 + (lane & 15), kb * 4 + (lane >> 4));
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf) mma_bf16(acc2[jj][tf], a[jj], b[tf]);
     }
   };
   // the Q and dO tiles' loads are older than the ring's: the first wait covers them
@@ -415,15 +421,18 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
   wait_lgkm0();
   barrier();
 
-  const int t = t0 + tl;
-  if (t < tokens) {
 #pragma unroll
-    for (int jf = 0; jf < 8; ++jf) {
-      const int j = jf * 16 + (lane >> 4) * 4;
-      float v[4];
+  for (int tf = 0; tf < 4; ++tf) {
+    const int t = t0 + tf * 16 + (lane & 15);
+    if (t < tokens) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) v[x] = acc2[jf][x];
-      Quad<bf16_t>::store(dq + ((size_t)t * heads + h) * MH_DH + j, v);
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = (2 * w + jj) * 16 + (lane >> 4) * 4;
+        float v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = acc2[jj][tf][x];
+        Quad<bf16_t>::store(dq + ((size_t)t * heads + h) * MH_DH + j, v);
+      }
     }
   }
   for (int i = threadIdx.x; i < MB_TM * subnets; i += NT) {
