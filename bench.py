@@ -61,14 +61,18 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources: traffic counters apply only to the code they were taken on."""
+def kernel_source_digest(kernel: str) -> str:
+    """sha256 over the shared HIP headers and the sources that launch `kernel` (by its timing name):
+    traffic counters apply only to the code they were taken on."""
     import hashlib
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "group_sparse_swiglu_amd", "csrc")
     h = hashlib.sha256()
+    tag = ('"' + kernel + '"').encode()
     for name in sorted(os.listdir(root)):
         with open(os.path.join(root, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+            text = f.read()
+        if name.endswith(".hpp") or (name.endswith(".hip") and tag in text):
+            h.update(name.encode() + b"\0" + text)
     return h.hexdigest()[:16]
 
 
@@ -78,7 +82,7 @@ def recorded_traffic(workload: str, kernel: str):
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
-    digest = kernel_source_digest()
+    digest = kernel_source_digest(kernel)
     for line in open(path):
         cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
         if len(cells) >= 5 and cells[0] == kernel and cells[1] == digest:
