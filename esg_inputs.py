@@ -107,7 +107,7 @@ def random_group_idx(tokens: int, groups: int, k: int, seed: int = 0) -> torch.T
     Used where a test needs valid routing without running a selection."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
-    scores = torch.rand(tokens, groups, generator=g)
+    scores = torch.rand(tokens, groups, generator=g, dtype=torch.float32)
     idx = torch.topk(scores, k, dim=1).indices
     return torch.sort(idx, dim=1).values.to(torch.int32)
 
@@ -143,11 +143,11 @@ def make_routing_inputs(tokens: int, experts: int, seed: int = 0, scale: float =
     if levels > 0:
         logits = torch.randint(0, levels, (tokens, experts), generator=g).float()
     else:
-        logits = torch.randn(tokens, experts, generator=g) * scale
-    bias = torch.rand(experts, generator=g) * 0.2 - 0.1
+        logits = torch.randn(tokens, experts, generator=g, dtype=torch.float32) * scale
+    bias = torch.rand(experts, generator=g, dtype=torch.float32) * 0.2 - 0.1
     if saturate:
         sign = torch.randint(0, 2, (tokens, experts), generator=g).float() * 2 - 1
-        half = torch.rand(tokens, experts, generator=g) < 0.5
+        half = torch.rand(tokens, experts, generator=g, dtype=torch.float32) < 0.5
         logits = torch.where(half, logits + 30.0 * sign, logits)
     return logits.contiguous(), bias.contiguous()
 
@@ -177,10 +177,10 @@ MLP_WORKLOADS = {
 
 def make_mlp_inputs(tokens: int, d_model: int, d_ff: int, seed: int = 0, dtype: str = "bf16"):
     g = torch.Generator().manual_seed(seed)
-    x = torch.randn(tokens, d_model, generator=g)
-    w_up = torch.randn(d_ff, d_model, generator=g) / d_model ** 0.5
-    w_down = torch.randn(d_model, d_ff, generator=g) / d_ff ** 0.5
-    dy = torch.randn(tokens, d_model, generator=g)
+    x = torch.randn(tokens, d_model, generator=g, dtype=torch.float32)
+    w_up = torch.randn(d_ff, d_model, generator=g, dtype=torch.float32) / d_model ** 0.5
+    w_down = torch.randn(d_model, d_ff, generator=g, dtype=torch.float32) / d_ff ** 0.5
+    dy = torch.randn(tokens, d_model, generator=g, dtype=torch.float32)
     td = torch_dtype(dtype)
     return tuple(t.to(td).contiguous() for t in (x, w_up, w_down, dy))
 
@@ -212,12 +212,12 @@ MHFFN_WORKLOADS = {
 
 def make_mhffn_inputs(tokens: int, heads: int, d_head: int, subnets: int, d_sub: int, seed: int = 0):
     g = torch.Generator().manual_seed(seed)
-    q = torch.randn(tokens, heads, d_head, generator=g)
-    r = torch.rand(tokens, heads, subnets, generator=g) * (2.0 / subnets)
-    k = torch.randn(heads, subnets, d_sub, d_head, generator=g) / d_head ** 0.5
-    u = torch.randn(heads, subnets, d_sub, d_head, generator=g) / d_head ** 0.5
-    v = torch.randn(heads, subnets, d_sub, d_head, generator=g) / d_sub ** 0.5
-    do = torch.randn(tokens, heads, d_head, generator=g)
+    q = torch.randn(tokens, heads, d_head, generator=g, dtype=torch.float32)
+    r = torch.rand(tokens, heads, subnets, generator=g, dtype=torch.float32) * (2.0 / subnets)
+    k = torch.randn(heads, subnets, d_sub, d_head, generator=g, dtype=torch.float32) / d_head ** 0.5
+    u = torch.randn(heads, subnets, d_sub, d_head, generator=g, dtype=torch.float32) / d_head ** 0.5
+    v = torch.randn(heads, subnets, d_sub, d_head, generator=g, dtype=torch.float32) / d_sub ** 0.5
+    do = torch.randn(tokens, heads, d_head, generator=g, dtype=torch.float32)
     bf = torch.bfloat16
     return (q.to(bf).contiguous(), r.contiguous(), k.to(bf).contiguous(), u.to(bf).contiguous(),
             v.to(bf).contiguous(), do.to(bf).contiguous())

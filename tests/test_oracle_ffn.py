@@ -5,7 +5,16 @@ import torch
 
 from oracle import esg_oracle as O
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _fp64_default():
+    """This module's torch pins run in fp64; the default is restored after each
+    test so that no other module sees it."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def _rand(T, d, F, seed=0):
