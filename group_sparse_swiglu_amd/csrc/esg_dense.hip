@@ -264,7 +264,10 @@ __global__ __launch_bounds__(NT, 1) void dense_rec_kernel(const bf16_t* __restri
   const uint32_t prow0 = (uint32_t)tile * BM;
 
   f32x4 gu[2 * CF::FMP][CF::FN];
-  gateup_tile<NB, NS>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, gu);
+  {
+    ESG_LDS char* const st[NS] = {st0, st1, st2};
+    gateup_tile<NB, NS>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, gu);
+  }
   wait_lgkm0();
   barrier();  // the stages are reused
   f32x4 da[CD::FM][CD::FN];

@@ -89,6 +89,14 @@ struct Quad<float> {
     *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
+// four bf16 values (8 bytes) to fp32
+__device__ __forceinline__ void unpack_bf16x4(uint2 q, float (&v)[4]) {
+  v[0] = __uint_as_float(q.x << 16);
+  v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16);
+  v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
 template <>
 struct Quad<bf16_t> {
   static __device__ __forceinline__ void load(const void* p, float (&v)[4]) {

@@ -33,12 +33,13 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
     bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials) {
   using C = Fwd2<GSB>;
   constexpr int NS = stages_for<GSB>();
-  // with two stages the third buffer only holds the second W_down tile
-  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE],
-      st2_[NS == 3 ? C::STAGE : C::W2_BYTES];
-  ESG_LDS char* st0 = (ESG_LDS char*)st0_;
-  ESG_LDS char* st1 = (ESG_LDS char*)st1_;
-  ESG_LDS char* st2 = (ESG_LDS char*)st2_;
+  // with two stages a third W_down buffer follows them
+  __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE + (NS == 2 ? C::W2_BYTES : 0)];
+  ESG_LDS char* st[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) st[i] = (ESG_LDS char*)stages_ + i * C::STAGE;
+  ESG_LDS char* const st0 = st[0];
+  ESG_LDS char* const st1 = st[1];
 
   const int tile = blockIdx.x;
   const int g = tile_group[tile];
@@ -54,8 +55,17 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   int brow[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
+  // phase-2 output rows (read before phase 1, so the load latency hides behind it)
+  using RS = RowStore<DB>;
+  const uint32_t psub = (uint32_t)s * rows_total * d * 2;
+  uint32_t row_off[RS::IT];
+#pragma unroll
+  for (int it = 0; it < RS::IT; ++it) {
+    const int r = RS::row(it, threadIdx.x);
+    row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
+  }
   f32x4 acc[2 * C::FMP][C::FN];
-  gateup_tile<GSB, NS>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, acc);
+  gateup_tile<GSB, NS>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, acc);
   wait_lgkm0();
   barrier();  // every wave is done with the stages
 
@@ -92,7 +102,6 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   const int c_lane = (lane & 7) ^ (lane >> 3);
   const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
   const rsrc_t rp = make_rsrc(partials, gridDim.y * rows_total * (uint32_t)d * 2);
-  const uint32_t psub = (uint32_t)s * rows_total * d * 2;
   uint32_t voffW[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -115,16 +124,9 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   for (int i = 0; i < C::FM2; ++i) arow2[i] = wm * 64 + i * 16 + (lane & 15);
 #pragma unroll
   for (int j = 0; j < C::FN2; ++j) brow2[j] = wn * 64 + j * 16 + (lane & 15);
-  using RS = RowStore<DB>;
-  uint32_t row_off[RS::IT];
-#pragma unroll
-  for (int it = 0; it < RS::IT; ++it) {
-    const int r = RS::row(it, threadIdx.x);
-    row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
-  }
   // staging of the output block: stage tails the W_down tiles and the act tile leave free
   ESG_LDS char* out0 = NS == 3 ? st1 + C::W2_BYTES : st0 + C::ACT_BYTES;
-  ESG_LDS char* out1 = NS == 3 ? st2 + C::W2_BYTES : st1 + C::W2_BYTES;
+  ESG_LDS char* out1 = NS == 3 ? st[NS - 1] + C::W2_BYTES : st1 + C::W2_BYTES;
   auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
     f32x4 acc2[C::FM2][C::FN2];
     zero_acc(acc2);
@@ -154,9 +156,12 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
     barrier();  // the whole block is staged
     RS::flush(out0, out1, rp, row_off, blk * DB, d);
   };
-  // st1 and st2 are free (the barrier above); the first step's full wait
-  // covers the epilogue stores, and its barrier publishes the act tile
-  kloop<2, 0, C::STORES2>((d + DB - 1) / DB, st1, st2, st2, issueW, compute2);
+  // the stages after st0 are free (the barrier above); the first step's wait
+  // covers the epilogue stores (they precede every W_down load), and its
+  // barrier publishes the act tile.  The two W_down buffers: st1 and the last
+  // stage (three stages) or the region after st1 (two)
+  ESG_LDS char* const wbuf[2] = {st1, NS == 2 ? st1 + C::STAGE : st[NS - 1]};
+  kloop_ring<2, C::KSUB * 4, C::STORES2>((d + DB - 1) / DB, wbuf, issueW, compute2);
 }
 
 // ===========================================================================
@@ -193,11 +198,22 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
   int brow[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
+  // the saved pre-activations of the wave's outputs, loaded before phase 1 so
+  // that their latency hides behind it (plain loads, older than every DMA)
+  const size_t sub_el = (size_t)s * rows_total * GSB;
+  uint2 hgq[C::FM][C::FN], huq[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const size_t q = sub_el + (size_t)(prow0 + brow[j]) * GSB + wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
+      hgq[i][j] = *(const uint2*)(hg_saved + q);
+      huq[i][j] = *(const uint2*)(hu_saved + q);
+    }
   f32x4 acc[C::FM][C::FN];
   da_tile<GSB, NS>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, acc);
 
   // ---- epilogue: SiLU' ----
-  const size_t sub_el = (size_t)s * rows_total * GSB;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int n = wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
@@ -206,8 +222,8 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
       const int r = brow[j];
       const size_t q = sub_el + (size_t)(prow0 + r) * GSB + n;
       float hg[4], hu[4], dgv[4], duv[4], av[4];
-      Quad<bf16_t>::load(hg_saved + q, hg);
-      Quad<bf16_t>::load(hu_saved + q, hu);
+      unpack_bf16x4(hgq[i][j], hg);
+      unpack_bf16x4(huq[i][j], hu);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float da = acc[i][j][e];

@@ -64,49 +64,67 @@ constexpr int stages_for() {
   return GSB >= 128 ? 3 : 2;
 }
 
+
 // ---------------------------------------------------------------------------
-// Direct-to-LDS K loop with NS stages (2 or 3): tile t lands in stage t % NS
-// and NS-1 tiles are in flight ahead of the one consumed.
+// Direct-to-LDS K loop over a ring of NS stages (2 to 4): tile t lands in
+// stage t % NS and NS-1 tiles are in flight ahead of the one consumed.
 //   issue(stage, t)    enqueues tile t's loads (L per lane; called once per
 //                      tile, in order);
 //   compute(stage, t)  consumes a landed tile and may end with S global stores
-//                      per lane (S > 0 only with NS = 2).
+//                      per lane.
 // Step t waits for tile t with the exact vmcnt the issue order implies
 // (vector loads and stores retire in order): younger than tile t are the
-// loads of the tiles issued ahead of it and the stores of step t-1.  The
-// direct-to-LDS loads are invisible to the compiler (esg_pipe.hpp), so these
-// explicit waits are the only ones that order them, and the loop can stay a
-// plain rolled loop: the accumulators then stay in place across steps.
+// loads of the min(NS-2, nk-1-t) tiles issued after it and the stores of the
+// min(t, NS-1) steps computed since it was issued.  The direct-to-LDS loads
+// are invisible to the compiler (esg_pipe.hpp), so these explicit waits are
+// the only ones that order them, and the loop can stay a plain rolled loop:
+// the accumulators then stay in place across steps.
 // ---------------------------------------------------------------------------
+template <int L, int S, int A, int B>
+__device__ __forceinline__ void wait_tile(int a, int b) {
+  // a in [0, A], b in [0, B], wave-uniform: one immediate wait per case
+  if (a == A && b == B) {
+    static_assert(A * L + B * S < 64, "vmcnt range");
+    wait_vmcnt<A * L + B * S>();
+  } else if constexpr (B > 0) {
+    if (a == A) wait_tile<L, S, A, B - 1>(a, b);
+    else if constexpr (A > 0) wait_tile<L, S, A - 1, B>(a, b);
+  } else if constexpr (A > 0) {
+    wait_tile<L, S, A - 1, B>(a, b);
+  }
+}
+
+template <int NS, int L, int S, class Issue, class Compute>
+__device__ __forceinline__ void kloop_ring(int nk, ESG_LDS char* const (&st)[NS], Issue&& issue,
+                                           Compute&& compute) {
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  if (nk <= 0) return;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nk) issue(st[j], j);
+  int cur = 0;       // t % NS
+  int nxt = NS - 1;  // (t + NS - 1) % NS
+  for (int t = 0; t < nk; ++t) {
+    wait_tile<L, S, NS - 2, (S > 0 ? NS - 1 : 0)>(min(NS - 2, nk - 1 - t), S > 0 ? min(t, NS - 1) : 0);
+    wait_lgkm0();
+    barrier();
+    if (t + NS - 1 < nk) issue(st[nxt], t + NS - 1);
+    compute(st[cur], t);
+    cur = cur + 1 == NS ? 0 : cur + 1;
+    nxt = nxt + 1 == NS ? 0 : nxt + 1;
+  }
+}
+
 template <int NS, int L, int S, class Issue, class Compute>
 __device__ __forceinline__ void kloop(int nk, ESG_LDS char* s0, ESG_LDS char* s1, ESG_LDS char* s2, Issue&& issue,
                                       Compute&& compute) {
   static_assert(NS == 2 || NS == 3, "two or three stages");
-  static_assert(NS == 2 || S == 0, "stores inside the loop only with two stages");
-  auto stage = [&](int i) __attribute__((always_inline)) { return i == 0 ? s0 : (i == 1 ? s1 : s2); };
-  if (nk <= 0) return;
-  issue(s0, 0);
-  if (NS == 3 && nk > 1) issue(s1, 1);
-  int cur = 0;                   // t % NS
-  int nxt = NS - 1;              // (t + NS - 1) % NS
-  for (int t = 0; t < nk; ++t) {
-    if constexpr (NS == 3) {
-      if (t + 1 < nk)
-        wait_vmcnt<L>();
-      else
-        wait_vmcnt<0>();
-    } else {
-      if (t == 0)
-        wait_vmcnt<0>();
-      else
-        wait_vmcnt<S>();
-    }
-    wait_lgkm0();
-    barrier();
-    if (t + NS - 1 < nk) issue(stage(nxt), t + NS - 1);
-    compute(stage(cur), t);
-    cur = cur + 1 == NS ? 0 : cur + 1;
-    nxt = nxt + 1 == NS ? 0 : nxt + 1;
+  if constexpr (NS == 2) {
+    ESG_LDS char* const st[2] = {s0, s1};
+    kloop_ring<2, L, S>(nk, st, issue, compute);
+  } else {
+    ESG_LDS char* const st[3] = {s0, s1, s2};
+    kloop_ring<3, L, S>(nk, st, issue, compute);
   }
 }
 
@@ -140,8 +158,8 @@ struct Fwd2 {
 template <int GSB, int NS>
 __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
                                             const bf16_t* __restrict__ wu, int tokens, int d, int F, int nb0,
-                                            const int32_t* __restrict__ ptoken, uint32_t prow0, ESG_LDS char* st0,
-                                            ESG_LDS char* st1, ESG_LDS char* st2,
+                                            const int32_t* __restrict__ ptoken, uint32_t prow0,
+                                            ESG_LDS char* const (&st)[NS],
                                             f32x4 (&acc)[2 * Fwd2<GSB>::FMP][Fwd2<GSB>::FN]) {
   using C = Fwd2<GSB>;
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -205,7 +223,7 @@ __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const 
         for (int j = 0; j < C::FN; ++j) mma_bf16(acc[i][j], a[i], b[j]);
     }
   };
-  kloop<NS, C::L, 0>((int)((kbytes + 127) / 128), st0, st1, st2, issue, compute);
+  kloop_ring<NS, C::L, 0>((int)((kbytes + 127) / 128), st, issue, compute);
 }
 
 // ===========================================================================
