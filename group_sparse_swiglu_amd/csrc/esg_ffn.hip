@@ -221,64 +221,11 @@ __global__ __launch_bounds__(NT) void fwd_grouped_kernel(
   }
 }
 
-// y[t] = sum of the token's partial rows in a fixed order: sub-block by
-// sub-block, slots in order within each.  A thread owns one 16-byte vector of one token's output row; the partial
-// rows' positions are read for up to KB slots at a time and all their vectors
-// are requested before the first is summed, so the k loads overlap.
-template <typename T>
-__device__ __forceinline__ void add_vec(float (&acc)[Elem<T>::EPC], const uint4& q) {
-  if constexpr (Elem<T>::EPC == 8) {
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      acc[2 * m] += __uint_as_float(w[m] << 16);
-      acc[2 * m + 1] += __uint_as_float(w[m] & 0xffff0000u);
-    }
-  } else {
-    acc[0] += __uint_as_float(q.x);
-    acc[1] += __uint_as_float(q.y);
-    acc[2] += __uint_as_float(q.z);
-    acc[3] += __uint_as_float(q.w);
-  }
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void rowsum_kernel(const T* __restrict__ partials, size_t sub_stride,
                                                      int nsub, const int32_t* __restrict__ pinv, int tokens,
                                                      int k, int d, T* __restrict__ out) {
-  constexpr int EPC = Elem<T>::EPC;
-  constexpr int KB = 16;
-  const int vpr = d / EPC;  // 16-byte vectors per row
-  const size_t total = (size_t)tokens * vpr;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(i / vpr), v = (int)(i % vpr);
-    float acc[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-    const int32_t* prow = pinv + (size_t)t * k;
-    for (int sb = 0; sb < nsub; ++sb) {
-      const T* base = partials + sb * sub_stride + v * EPC;
-      for (int j0 = 0; j0 < k; j0 += KB) {
-        int p[KB];
-#pragma unroll
-        for (int j = 0; j < KB; ++j) p[j] = j0 + j < k ? prow[j0 + j] : -1;
-        uint4 q[KB];
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-          q[j] = p[j] >= 0 ? *(const uint4*)(base + (size_t)p[j] * d) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-          if (p[j] >= 0) add_vec<T>(acc, q[j]);
-      }
-    }
-    T* o = out + (size_t)t * d + v * EPC;
-    if constexpr (EPC == 8) {
-      *(uint4*)o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    } else {
-      *(float4*)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
+  rowsum_range<T>(partials, sub_stride, nsub, pinv, tokens, k, d, out, blockIdx.x, gridDim.x);
 }
 
 // ===========================================================================

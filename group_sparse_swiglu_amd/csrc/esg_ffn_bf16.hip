@@ -48,7 +48,6 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   const int nb0 = g * gs + s * GSB;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t prow0 = (uint32_t)tile * BM;
-  const uint32_t kbytes = (uint32_t)d * 2;
 
   // wave (wm, wn) owns neurons [wm*GSB/2, +GSB/2) of gate and up, positions [wn*64, +64)
   const int wm = w & 1, wn = w >> 1;

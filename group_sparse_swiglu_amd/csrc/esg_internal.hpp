@@ -128,4 +128,7 @@ hipError_t launch_sigmoid_topk(const float* logits, const float* bias, int bias_
                                float scaling, int apply_scaling, float* probs, int64_t* indices,
                                hipStream_t stream);
 
+// Compute units of the current device (cached per device).
+int compute_units();
+
 }  // namespace esg

@@ -58,4 +58,17 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stre
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int compute_units() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace esg

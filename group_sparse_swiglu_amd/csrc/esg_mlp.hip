@@ -302,18 +302,6 @@ __global__ void mlp_reduce_kernel(const float* __restrict__ part, int splits, si
   }
 }
 
-int compute_units() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int TQ, int AL, int BL, int EPI>
 hipError_t launch_gemm(const char* name, GemmArgs a, int splits, hipStream_t stream) {
   a.nq = (a.Q + TQ - 1) / TQ;

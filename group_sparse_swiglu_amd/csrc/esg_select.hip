@@ -33,7 +33,6 @@ template <typename T, int BM, int FNW, bool USE_DMA = true>
 struct SelCfg {
   static constexpr int NSC = 4 * FNW * 16;  // sampled rows per super-chunk
   static constexpr int FM = BM / 16;
-  // (with only two stages of the wider super-chunks the staged loop measured faster)
   static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && BM == 32 && FNW <= 4;
   static constexpr int PA = Plane<BM>::BYTES;
   static constexpr int PB = Plane<NSC>::BYTES;
@@ -318,6 +317,15 @@ hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int 
                     int rpg, const float* bias, int32_t* idx, int32_t* counts, hipStream_t st) {
   if (groups > 256)
     return launch_select_t<T, 16, 8>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+  if (std::is_same<T, bf16_t>::value) {
+    // direct-to-LDS: up to 256 sampled rows in one super-chunk of 4 fragments
+    // per wave; beyond, super-chunks of 128 rows, whose small stages let two
+    // workgroups share a CU (more waves issuing loads; measured faster than
+    // fewer, wider super-chunks)
+    if (groups * rpg > 128 && groups * rpg <= 256)
+      return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+    return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+  }
   switch (pick_fnw(groups * rpg)) {
     case 2: return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
     case 4: return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
