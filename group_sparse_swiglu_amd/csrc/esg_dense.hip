@@ -241,8 +241,11 @@ __global__ void dense_route_kernel(int t0, int tc, int tc_pad, int32_t* __restri
 }
 
 // hg, hu, dA for one (128-token tile, 128-neuron block) of a chunk; writes
-// dg, du, a rows to the packed layout [block][tc_pad][128].
-__global__ __launch_bounds__(NT, 1) void dense_rec_kernel(const bf16_t* __restrict__ x,
+// dg, du, a rows to the packed layout [block][tc_pad][128].  Eight waves:
+// the direct-to-LDS loads of the one workgroup per CU are issued by twice
+// the waves of the 4-wave tile helpers' default.
+constexpr int REC_NW = 8;
+__global__ __launch_bounds__(64 * REC_NW, 1) void dense_rec_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ dy,
                                                           const bf16_t* __restrict__ wg,
                                                           const bf16_t* __restrict__ wu,
@@ -250,8 +253,8 @@ __global__ __launch_bounds__(NT, 1) void dense_rec_kernel(const bf16_t* __restri
                                                           const int32_t* __restrict__ ptoken, int tc_pad,
                                                           bf16_t* __restrict__ dg, bf16_t* __restrict__ du,
                                                           bf16_t* __restrict__ act) {
-  using CF = Fwd2<NB>;
-  using CD = Dh2<NB>;
+  using CF = Fwd2<NB, REC_NW>;
+  using CD = Dh2<NB, REC_NW>;
   constexpr int NS = 3;
   constexpr int STG = CF::STAGE > CD::STAGE ? CF::STAGE : CD::STAGE;
   __shared__ __attribute__((aligned(1024))) char st0_[STG], st1_[STG], st2_[STG];
@@ -266,19 +269,20 @@ __global__ __launch_bounds__(NT, 1) void dense_rec_kernel(const bf16_t* __restri
   f32x4 gu[2 * CF::FMP][CF::FN];
   {
     ESG_LDS char* const st[NS] = {st0, st1, st2};
-    gateup_tile<NB, NS>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, gu);
+    gateup_tile<NB, NS, REC_NW>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, gu);
   }
   wait_lgkm0();
   barrier();  // the stages are reused
   f32x4 da[CD::FM][CD::FN];
-  da_tile<NB, NS>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, da);
+  da_tile<NB, NS, REC_NW>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, da);
 
-  // both tiles use the same mapping: neurons wm*64 + i*16 + (lane/16)*4 + e,
+  // both tiles use the same mapping: neurons wm*(NB/WM) + i*16 + (lane/16)*4 + e,
   // positions wn*64 + j*16 + lane%16
-  const int wm = w & 1, wn = w >> 1;
+  static_assert(CF::WM == CD::WM && CF::FMP == CD::FM && CF::FN == CD::FN, "one wave mapping");
+  const int wm = w % CD::WM, wn = w / CD::WM;
 #pragma unroll
   for (int i = 0; i < CD::FM; ++i) {
-    const int n = wm * (NB / 2) + i * 16 + (lane >> 4) * 4;
+    const int n = wm * (NB / CD::WM) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < CD::FN; ++j) {
       const int r = wn * 64 + j * 16 + (lane & 15);
@@ -303,14 +307,19 @@ __global__ __launch_bounds__(NT, 1) void dense_rec_kernel(const bf16_t* __restri
 // dx[t0 + tile*128 + m, d-block] = sum over blocks of dg W_g + du W_u.
 // C^T (d x tokens) = W^T (d x K) . [dg du]^T (K x tokens): the weights come in
 // as N-row tiles (K = neuron rows, d contiguous), dg/du as K-row tiles.
+// Eight waves (one workgroup per CU): wave (wm, wn) owns d [wm*32, +32) x
+// tokens [wn*64, +64) of the block; every wave issues IA + IB loads per stage.
 struct DDx {
+  static constexpr int NW = 8;
   static constexpr int A_BYTES = 64 * 256;  // 64 neuron rows x 128 d
   static constexpr int B_BYTES = BM * 128;  // 128 tokens x 64 neurons
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int L = 8;
+  static constexpr int IA = A_BYTES / 1024 / NW, IB = B_BYTES / 1024 / NW;
+  static constexpr int L = IA + IB;
+  static constexpr int WM = NW / 2, FM = 128 / WM / 16, FN = 4;
 };
 
-__global__ __launch_bounds__(NT, 1) void dense_dx_kernel(const bf16_t* __restrict__ wg,
+__global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t* __restrict__ wg,
                                                          const bf16_t* __restrict__ wu, int d, int F, int t0,
                                                          int tc, int tc_pad, const bf16_t* __restrict__ dg,
                                                          const bf16_t* __restrict__ du, bf16_t* __restrict__ dx) {
@@ -329,56 +338,56 @@ __global__ __launch_bounds__(NT, 1) void dense_dx_kernel(const bf16_t* __restric
   const DmaSrc rdg = make_dma_src(dg, pbytes);
   const DmaSrc rdu = make_dma_src(du, pbytes);
 
-  // A: neuron row kr = (w*4 + i)*4 + lane/16 of the stage, 16-byte chunk jz
-  int jz[4];
+  // A: neuron row kr = (w*IA + i)*4 + lane/16 of the stage, 16-byte chunk jz
+  int jz[C::IA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) jz[i] = (lane & 15) ^ mn_swz<16>((w * 4 + i) * 4 + (lane >> 4));
-  // B: packed row (w*4 + i)*8 + lane/8, chunk c_lane
+  for (int i = 0; i < C::IA; ++i) jz[i] = (lane & 15) ^ mn_swz<16>((w * C::IA + i) * 4 + (lane >> 4));
+  // B: packed row (w*IB + i)*8 + lane/8, chunk c_lane
   const int c_lane = (lane & 7) ^ (lane >> 3);
   // stage kt: block kt/4, half (kt/2)&1 (0: dg with W_g, 1: du with W_u), 64-neuron sub-block kt&1
   auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
     const int blk = kt >> 2, h = (kt >> 1) & 1, sb = kt & 1;
     const int n0 = blk * NB + sb * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kr = (w * 4 + i) * 4 + (lane >> 4);
+    for (int i = 0; i < C::IA; ++i) {
+      const int kr = (w * C::IA + i) * 4 + (lane >> 4);
       const bool ok = n0 + kr < F && db0 + jz[i] * 8 < d;
-      dma16(h ? ru : rg, st + (w * 4 + i) * 1024,
+      dma16(h ? ru : rg, st + (w * C::IA + i) * 1024,
             ok ? (uint32_t)(n0 + kr) * kbytes + (uint32_t)db0 * 2 + jz[i] * 16 : kOOB);
     }
     const uint32_t rbase = ((uint32_t)blk * tc_pad + (uint32_t)tile * BM) * (NB * 2) + sb * 128 + c_lane * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (w * 4 + i) * 8 + (lane >> 3);
-      dma16(h ? rdu : rdg, st + C::A_BYTES + (w * 4 + i) * 1024, rbase + (uint32_t)r * (NB * 2));
+    for (int i = 0; i < C::IB; ++i) {
+      const int r = (w * C::IB + i) * 8 + (lane >> 3);
+      dma16(h ? rdu : rdg, st + C::A_BYTES + (w * C::IB + i) * 1024, rbase + (uint32_t)r * (NB * 2));
     }
   };
-  const int wm = w & 1, wn = w >> 1;
-  f32x4 acc[4][4];
+  const int wm = w % C::WM, wn = w / C::WM;
+  f32x4 acc[C::FM][C::FN];
   zero_acc(acc);
   auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
-    uint4 a[2][4];
+    uint4 a[2][C::FM];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[kb][i] = frag_nrow<16>(st, kb, wm * 64 + i * 16, lane);
+      for (int i = 0; i < C::FM; ++i) a[kb][i] = frag_nrow<16>(st, kb, wm * (128 / C::WM) + i * 16, lane);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint4 b[4];
+      uint4 b[C::FN];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = frag_krow(st + C::A_BYTES, wn * 64 + j * 16 + (lane & 15), kb * 4 + (lane >> 4));
+      for (int j = 0; j < C::FN; ++j) b[j] = frag_krow(st + C::A_BYTES, wn * 64 + j * 16 + (lane & 15), kb * 4 + (lane >> 4));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma_bf16(acc[i][j], a[kb][i], b[j]);
+        for (int j = 0; j < C::FN; ++j) mma_bf16(acc[i][j], a[kb][i], b[j]);
     }
   };
   kloop<3, C::L, 0>(nblk * 4, st0, st1, st2, issue, compute);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int dd = db0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+  for (int i = 0; i < C::FM; ++i) {
+    const int dd = db0 + wm * (128 / C::WM) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < C::FN; ++j) {
       const int m = tile * BM + wn * 64 + j * 16 + (lane & 15);
       if (dd >= d || m >= tc) continue;
       float v[4];
@@ -486,7 +495,7 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
     }
     {
       LaunchTimer timer("dense_rec", stream);
-      hipLaunchKernelGGL(dense_rec_kernel, dim3(tiles, L.nblk), dim3(NT), 0, stream, (const bf16_t*)x,
+      hipLaunchKernelGGL(dense_rec_kernel, dim3(tiles, L.nblk), dim3(64 * REC_NW), 0, stream, (const bf16_t*)x,
                          (const bf16_t*)dy, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, d, F,
                          ptoken, L.tc, dg, du, act);
       hipError_t e = hipGetLastError();
@@ -494,7 +503,7 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
     }
     {
       LaunchTimer timer("dense_dx", stream);
-      hipLaunchKernelGGL(dense_dx_kernel, dim3(tiles, (d + 127) / 128), dim3(NT), 0, stream, (const bf16_t*)wg,
+      hipLaunchKernelGGL(dense_dx_kernel, dim3(tiles, (d + 127) / 128), dim3(64 * DDx::NW), 0, stream, (const bf16_t*)wg,
                          (const bf16_t*)wu, d, F, t0, tc, L.tc, dg, du, (bf16_t*)dx);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

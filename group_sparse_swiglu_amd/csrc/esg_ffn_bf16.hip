@@ -25,13 +25,22 @@ namespace {
 
 using namespace tiles;
 
+// Waves of the forward tile: 64-neuron blocks two 4-wave workgroups per CU,
+// 128-neuron blocks one 8-wave workgroup (the loads of the one workgroup are
+// issued by eight waves: direct-to-LDS throughput grows with the issuing waves).
 template <int GSB>
-__global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
+constexpr int fwd_waves() {
+  return GSB >= 128 ? 8 : 4;
+}
+
+template <int GSB>
+__global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void fwd2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
     const bf16_t* __restrict__ wd, int tokens, int d, int F, int gs, const int32_t* __restrict__ tile_group,
     const int32_t* __restrict__ ptoken, uint32_t rows_total, bf16_t* __restrict__ hg_saved,
     bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials) {
-  using C = Fwd2<GSB>;
+  constexpr int NW = fwd_waves<GSB>();
+  using C = Fwd2<GSB, NW>;
   constexpr int NS = stages_for<GSB>();
   // with two stages a third W_down buffer follows them
   __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE + (NS == 2 ? C::W2_BYTES : 0)];
@@ -49,13 +58,13 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t prow0 = (uint32_t)tile * BM;
 
-  // wave (wm, wn) owns neurons [wm*GSB/2, +GSB/2) of gate and up, positions [wn*64, +64)
-  const int wm = w & 1, wn = w >> 1;
+  // wave (wm, wn) owns neurons [wm*GSB/WM, +GSB/WM) of gate and up, positions [wn*64, +64)
+  const int wm = w % C::WM, wn = w / C::WM;
   int brow[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
   // phase-2 output rows (read before phase 1, so the load latency hides behind it)
-  using RS = RowStore<DB>;
+  using RS = RowStore<DB, C::NTH>;
   const uint32_t psub = (uint32_t)s * rows_total * d * 2;
   uint32_t row_off[RS::IT];
 #pragma unroll
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
     row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
   }
   f32x4 acc[2 * C::FMP][C::FN];
-  gateup_tile<GSB, NS>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, acc);
+  gateup_tile<GSB, NS, NW>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, acc);
   wait_lgkm0();
   barrier();  // every wave is done with the stages
 
@@ -76,7 +85,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   const uint32_t sub_off = (uint32_t)s * rows_total * GSB * 2;
 #pragma unroll
   for (int p = 0; p < C::FMP; ++p) {
-    const int n = wm * (GSB / 2) + p * 16 + (lane >> 4) * 4;  // 4 consecutive neurons
+    const int n = wm * (GSB / C::WM) + p * 16 + (lane >> 4) * 4;  // 4 consecutive neurons
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int r = brow[j];
@@ -101,10 +110,10 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   const int c_lane = (lane & 7) ^ (lane >> 3);
   const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
   const rsrc_t rp = make_rsrc(partials, gridDim.y * rows_total * (uint32_t)d * 2);
-  uint32_t voffW[4];
+  uint32_t voffW[C::IW2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (w * 4 + i) * 8 + (lane >> 3);
+  for (int i = 0; i < C::IW2; ++i) {
+    const int r = (w * C::IW2 + i) * 8 + (lane >> 3);
     voffW[i] = (uint32_t)r * F * 2 + (uint32_t)nb0 * 2 + c_lane * 16;
   }
   auto issueW = [&](ESG_LDS char* st, int blk) __attribute__((always_inline)) {
@@ -112,15 +121,15 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
 #pragma unroll
     for (int sb = 0; sb < C::KSUB; ++sb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = (w * 4 + i) * 8 + (lane >> 3);
+      for (int i = 0; i < C::IW2; ++i) {
+        const int r = (w * C::IW2 + i) * 8 + (lane >> 3);
         const uint32_t off = db0 + r < d ? voffW[i] + (uint32_t)db0 * F * 2 + sb * 128 : kOOB;
-        dma16(rd, st + sb * DB * 128 + (w * 4 + i) * 1024, off);
+        dma16(rd, st + sb * DB * 128 + (w * C::IW2 + i) * 1024, off);
       }
   };
   int arow2[C::FM2], brow2[C::FN2];
 #pragma unroll
-  for (int i = 0; i < C::FM2; ++i) arow2[i] = wm * 64 + i * 16 + (lane & 15);
+  for (int i = 0; i < C::FM2; ++i) arow2[i] = wm * (DB / C::WM) + i * 16 + (lane & 15);
 #pragma unroll
   for (int j = 0; j < C::FN2; ++j) brow2[j] = wn * 64 + j * 16 + (lane & 15);
   // staging of the output block: stage tails the W_down tiles and the act tile leave free
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
-        RS::put(out0, out1, brow2[j], wm * 64 + i * 16 + (lane >> 4) * 4, v);
+        RS::put(out0, out1, brow2[j], wm * (DB / C::WM) + i * 16 + (lane >> 4) * 4, v);
       }
     wait_lgkm0();
     barrier();  // the whole block is staged
@@ -160,20 +169,21 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void fwd2_kernel(
   // barrier publishes the act tile.  The two W_down buffers: st1 and the last
   // stage (three stages) or the region after st1 (two)
   ESG_LDS char* const wbuf[2] = {st1, NS == 2 ? st1 + C::STAGE : st[NS - 1]};
-  kloop_ring<2, C::KSUB * 4, C::STORES2>((d + DB - 1) / DB, wbuf, issueW, compute2);
+  kloop_ring<2, C::KSUB * C::IW2, C::STORES2>((d + DB - 1) / DB, wbuf, issueW, compute2);
 }
 
 // ===========================================================================
 // Backward dh (+ SiLU' epilogue) and dx partials (see da_tile for phase 1).
 // ===========================================================================
 template <int GSB>
-__global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
+__global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhdx2_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
     const bf16_t* __restrict__ wd, int tokens, int d, int F, int gs, const int32_t* __restrict__ tile_group,
     const int32_t* __restrict__ ptoken, uint32_t rows_total, const bf16_t* __restrict__ hg_saved,
     const bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ dg_out, bf16_t* __restrict__ du_out,
     bf16_t* __restrict__ act_out, bf16_t* __restrict__ partials) {
-  using C = Dh2<GSB>;
+  constexpr int NW = fwd_waves<GSB>();
+  using C = Dh2<GSB, NW>;
   constexpr int NS = stages_for<GSB>();
   // NS stages in one array (with two stages nothing uses st2; no placeholder
   // array, so that two workgroups fit in a compute unit's LDS)
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
   const uint32_t prow0 = (uint32_t)tile * BM;
   const uint32_t kbytes = (uint32_t)d * 2;
 
-  const int wm = w & 1, wn = w >> 1;
+  const int wm = w % C::WM, wn = w / C::WM;
   int brow[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
@@ -205,17 +215,17 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      const size_t q = sub_el + (size_t)(prow0 + brow[j]) * GSB + wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
+      const size_t q = sub_el + (size_t)(prow0 + brow[j]) * GSB + wm * (GSB / C::WM) + i * 16 + (lane >> 4) * 4;
       hgq[i][j] = *(const uint2*)(hg_saved + q);
       huq[i][j] = *(const uint2*)(hu_saved + q);
     }
   f32x4 acc[C::FM][C::FN];
-  da_tile<GSB, NS>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, acc);
+  da_tile<GSB, NS, NW>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, acc);
 
   // ---- epilogue: SiLU' ----
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    const int n = wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
+    const int n = wm * (GSB / C::WM) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int r = brow[j];
@@ -267,7 +277,12 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
             db0 + jW[i] * 8 < (uint32_t)d ? voffW[i] + db0 * 2 : kOOB);
     }
   };
-  using RS = RowStore<C::DB2>;
+  using RS = RowStore<C::DB2, C::NTH>;
+  // phase-2 wave tile: d half wm2 (32 d) x position slice wn2 (PW2 positions)
+  const int wm2 = w & 1, wn2 = w >> 1;
+  int brow2[C::FN2];
+#pragma unroll
+  for (int j = 0; j < C::FN2; ++j) brow2[j] = wn2 * C::PW2 + j * 16 + (lane & 15);
   uint32_t row_off[RS::IT];
 #pragma unroll
   for (int it = 0; it < RS::IT; ++it) {
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < C::FM2; ++i) a[kb][i] = frag_nrow<8>(cur, kb, wm * 32 + i * 16, lane);
+      for (int i = 0; i < C::FM2; ++i) a[kb][i] = frag_nrow<8>(cur, kb, wm2 * 32 + i * 16, lane);
     f32x4 acc2[C::FM2][C::FN2];
     zero_acc(acc2);
 #pragma unroll
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
       const int c = (kb & 1) * 4 + (lane >> 4);
       uint4 b[C::FN2];
 #pragma unroll
-      for (int j = 0; j < C::FN2; ++j) b[j] = frag_krow(dgu + (kb >> 1) * BM * 128, brow[j], c);
+      for (int j = 0; j < C::FN2; ++j) b[j] = frag_krow(dgu + (kb >> 1) * BM * 128, brow2[j], c);
 #pragma unroll
       for (int i = 0; i < C::FM2; ++i)
 #pragma unroll
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dhdx2_kernel(
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
-        RS::put(out0, out1, brow[j], wm * 32 + i * 16 + (lane >> 4) * 4, v);
+        RS::put(out0, out1, brow2[j], wm2 * 32 + i * 16 + (lane >> 4) * 4, v);
       }
     wait_lgkm0();
     barrier();  // the whole block is staged
@@ -354,7 +369,8 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
                   const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg, void* hu,
                   void* partials, hipStream_t stream) {
   LaunchTimer timer("fwd_grouped", stream);
-  hipLaunchKernelGGL((fwd2_kernel<GSB>), dim3(ntiles_max, s.nsub()), dim3(NT), 0, stream, (const bf16_t*)x,
+  hipLaunchKernelGGL((fwd2_kernel<GSB>), dim3(ntiles_max, s.nsub()), dim3(64 * fwd_waves<GSB>()), 0, stream,
+                     (const bf16_t*)x,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
                      (bf16_t*)partials);
@@ -366,7 +382,8 @@ hipError_t dhdx2_t(const FfnShape& s, const void* dy, const void* wg, const void
                    const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, const void* hg, const void* hu,
                    void* dg, void* du, void* act, void* partials, hipStream_t stream) {
   LaunchTimer timer("bwd_dh_dx", stream);
-  hipLaunchKernelGGL((dhdx2_kernel<GSB>), dim3(ntiles_max, s.nsub()), dim3(NT), 0, stream, (const bf16_t*)dy,
+  hipLaunchKernelGGL((dhdx2_kernel<GSB>), dim3(ntiles_max, s.nsub()), dim3(64 * fwd_waves<GSB>()), 0, stream,
+                     (const bf16_t*)dy,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (const bf16_t*)hg,
                      (const bf16_t*)hu, (bf16_t*)dg, (bf16_t*)du, (bf16_t*)act, (bf16_t*)partials);

@@ -28,13 +28,14 @@ __device__ __forceinline__ void store8(rsrc_t r, uint32_t voff, const float (&v)
 // staged in lds0, rows 64..127 in lds1 (DW*2*64 bytes each); 16-byte chunks
 // are XOR-swizzled by row.  row_off[it]: byte offset of the partial row this
 // thread stores at iteration it (kOOB for padding rows).
-template <int DW>
+template <int DW, int NTH = 256>
 struct RowStore {
   static constexpr int RB = DW * 2;       // bytes per staged row
   static constexpr int NCHK = RB / 16;    // 16-byte chunks per row
-  static constexpr int IT = 128 * NCHK / 256;  // 16-byte stores per thread
-  static __device__ __forceinline__ int row(int it, int tid) { return (it * 256 + tid) / NCHK; }
-  static __device__ __forceinline__ int chunk(int it, int tid) { return (it * 256 + tid) % NCHK; }
+  static constexpr int IT = 128 * NCHK / NTH;  // 16-byte stores per thread (NTH threads)
+  static_assert(IT * NTH == 128 * NCHK, "whole rows per pass");
+  static __device__ __forceinline__ int row(int it, int tid) { return (it * NTH + tid) / NCHK; }
+  static __device__ __forceinline__ int chunk(int it, int tid) { return (it * NTH + tid) % NCHK; }
   static __device__ __forceinline__ int off(int rr, int c) { return rr * RB + ((c ^ (rr & (NCHK - 1))) << 4); }
   // acc value e of a lane: d = dl + e (dl % 4 == 0, dl < DW), position r (0..127)
   static __device__ __forceinline__ void put(ESG_LDS char* lds0, ESG_LDS char* lds1, int r, int dl,
@@ -132,36 +133,41 @@ __device__ __forceinline__ void kloop(int nk, ESG_LDS char* s0, ESG_LDS char* s1
 // ===========================================================================
 // Forward
 // ===========================================================================
-template <int GSB>
+// NW wavefronts: WM = NW/2 neuron slices x 2 position halves (64 each).
+template <int GSB, int NW = 4>
 struct Fwd2 {
+  static constexpr int NTH = 64 * NW;
+  static constexpr int WM = NW / 2;
   static constexpr int RA = 2 * GSB;           // weight rows per tile (gate, then up)
   static constexpr int A_BYTES = RA * 128;     // one 64-wide K stage
   static constexpr int B_BYTES = BM * 128;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int IA = RA / 32;           // DMA instructions per lane per stage (A)
-  static constexpr int IB = BM / 32;           // (B)
+  static constexpr int IA = RA / (8 * NW);     // DMA instructions per lane per stage (A)
+  static constexpr int IB = BM / (8 * NW);     // (B)
   static constexpr int L = IA + IB;
-  static constexpr int FMP = GSB / 32;         // gate/up fragment pairs per wave
+  static constexpr int FMP = GSB / WM / 16;    // gate/up fragment pairs per wave
   static constexpr int FN = 4;                 // 64 positions per wave
   static constexpr int KSUB = GSB / 64;        // 64-wide K sub-tiles of the group width
   static constexpr int ACT_BYTES = KSUB * BM * 128;
   static constexpr int W2_BYTES = KSUB * DB * 128;
-  static constexpr int FM2 = 4, FN2 = 4;       // phase-2 wave tile 64 d x 64 positions
-  static constexpr int STORES2 = RowStore<DB>::IT;  // buffer stores per lane per d-block
+  static constexpr int IW2 = DB / (8 * NW);    // W_down DMA instructions per lane per K sub-tile
+  static constexpr int FM2 = DB / WM / 16, FN2 = 4;  // phase-2 wave tile DB/WM d x 64 positions
+  static constexpr int STORES2 = RowStore<DB, NTH>::IT;  // buffer stores per lane per d-block
   static_assert(ACT_BYTES <= STAGE && W2_BYTES <= STAGE, "phase-2 tiles reuse the stages");
+  static_assert(IA * 8 * NW == RA && IB * 8 * NW == BM && FMP >= 1, "whole DMA instructions and fragments");
 };
 
 // Phase 1 of a forward tile: [hg; hu]^T for the GSB neurons from nb0 (gate
 // rows, then up rows) against the 128 bucket positions from prow0, whose token
 // ids come from ptoken (-1 = padding, reads zeros).  K = d in 64-wide stages.
 // acc[p][j] (p < FMP: gate, p >= FMP: up) follows the wave mapping below.
-template <int GSB, int NS>
+template <int GSB, int NS, int NW = 4>
 __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
                                             const bf16_t* __restrict__ wu, int tokens, int d, int F, int nb0,
                                             const int32_t* __restrict__ ptoken, uint32_t prow0,
                                             ESG_LDS char* const (&st)[NS],
-                                            f32x4 (&acc)[2 * Fwd2<GSB>::FMP][Fwd2<GSB>::FN]) {
-  using C = Fwd2<GSB>;
+                                            f32x4 (&acc)[2 * Fwd2<GSB, NW>::FMP][Fwd2<GSB, NW>::FN]) {
+  using C = Fwd2<GSB, NW>;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t kbytes = (uint32_t)d * 2;
   const DmaSrc rx = make_dma_src(x, (uint32_t)tokens * kbytes);
@@ -197,12 +203,12 @@ __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const 
       dma16(rx, st + C::A_BYTES + (w * C::IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
   };
 
-  // MFMA: wave (wm, wn) owns neurons [wm*GSB/2, +GSB/2) of gate and up, positions [wn*64, +64) ----
-  const int wm = w & 1, wn = w >> 1;
+  // MFMA: wave (wm, wn) owns neurons [wm*GSB/WM, +GSB/WM) of gate and up, positions [wn*64, +64) ----
+  const int wm = w % C::WM, wn = w / C::WM;
   int arow[2 * C::FMP], brow[C::FN];
 #pragma unroll
   for (int p = 0; p < C::FMP; ++p) {
-    arow[p] = wm * (GSB / 2) + p * 16 + (lane & 15);
+    arow[p] = wm * (GSB / C::WM) + p * 16 + (lane & 15);
     arow[C::FMP + p] = GSB + arow[p];
   }
 #pragma unroll
@@ -235,34 +241,40 @@ __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const 
 //   phase 2  Q^T = [W_gate; W_up]^T[d-block] . [dg du]^T  (K = 2*gsb); the
 //            weights come in as N-row tiles (rows = neurons, columns = d)
 // ===========================================================================
-template <int GSB>
+// NW wavefronts: phase 1 WM = NW/2 neuron slices x 2 position halves;
+// phase 2 two d halves (32 each) x NW/2 position slices.
+template <int GSB, int NW = 4>
 struct Dh2 {
+  static constexpr int NTH = 64 * NW;
+  static constexpr int WM = NW / 2;
   static constexpr int NCH = GSB / 8;            // 16-byte chunks per neuron row segment
   static constexpr int A_BYTES = 64 * GSB * 2;   // N-row: 64 d rows x GSB neurons
   static constexpr int B_BYTES = BM * 128;       // K-row: BM positions x 64 d
   static constexpr int STAGE1 = A_BYTES + B_BYTES;
-  static constexpr int IA = NCH / 4;
-  static constexpr int IB = BM / 32;
+  static constexpr int IA = NCH / NW;
+  static constexpr int IB = BM / (8 * NW);
   static constexpr int L = IA + IB;
-  static constexpr int FM = GSB / 32, FN = 4;    // wave tile GSB/2 neurons x 64 positions
+  static constexpr int FM = GSB / WM / 16, FN = 4;  // wave tile GSB/WM neurons x 64 positions
   static constexpr int KSUB2 = 2 * GSB / 64;
   static constexpr int DGU_BYTES = KSUB2 * BM * 128;
   static constexpr int DB2 = 64;
   static constexpr int W2_BYTES = 2 * GSB * DB2 * 2;  // N-row: 2*GSB neuron rows x 64 d
-  static constexpr int IW = 2 * GSB / 32;
-  static constexpr int FM2 = 2, FN2 = 4;         // wave tile 32 d x 64 positions
-  static constexpr int STORES2 = RowStore<DB2>::IT;
+  static constexpr int IW = 2 * GSB / (8 * NW);
+  static constexpr int PW2 = BM / (NW / 2);      // positions per wave in phase 2
+  static constexpr int FM2 = 2, FN2 = PW2 / 16;  // wave tile 32 d x PW2 positions
+  static constexpr int STORES2 = RowStore<DB2, NTH>::IT;
   static constexpr int STAGE = STAGE1 > W2_BYTES ? STAGE1 : W2_BYTES;
+  static_assert(IA * NW == NCH && IB * 8 * NW == BM && IW * 8 * NW == 2 * GSB && FM >= 1, "whole instructions");
 };
 
 // Phase 1 of a backward tile: dA^T = W_down[:, nb0 .. nb0+GSB)^T . dY_tile^T
 // (K = d) for the 128 bucket positions from prow0 (token ids from ptoken).
-template <int GSB, int NS>
+template <int GSB, int NS, int NW = 4>
 __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf16_t* __restrict__ wd, int tokens,
                                         int d, int F, int nb0, const int32_t* __restrict__ ptoken, uint32_t prow0,
                                         ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2,
-                                        f32x4 (&acc)[Dh2<GSB>::FM][Dh2<GSB>::FN]) {
-  using C = Dh2<GSB>;
+                                        f32x4 (&acc)[Dh2<GSB, NW>::FM][Dh2<GSB, NW>::FN]) {
+  using C = Dh2<GSB, NW>;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t kbytes = (uint32_t)d * 2;
   const DmaSrc ry = make_dma_src(dy, (uint32_t)tokens * kbytes);
@@ -297,7 +309,7 @@ __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf1
     for (int i = 0; i < C::IB; ++i)
       dma16(ry, st + C::A_BYTES + (w * C::IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
   };
-  const int wm = w & 1, wn = w >> 1;
+  const int wm = w % C::WM, wn = w / C::WM;
   int brow[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
@@ -308,7 +320,7 @@ __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf1
     for (int kb = 0; kb < 2; ++kb) {
       const int c = kb * 4 + (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) a[kb][i] = frag_nrow<C::NCH>(st, kb, wm * (GSB / 2) + i * 16, lane);
+      for (int i = 0; i < C::FM; ++i) a[kb][i] = frag_nrow<C::NCH>(st, kb, wm * (GSB / C::WM) + i * 16, lane);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) b[kb][j] = frag_krow(st + C::A_BYTES, brow[j], c);
     }
