@@ -233,6 +233,7 @@ __global__ __launch_bounds__(DFwd::NTD, 1) void dense_fwd_kernel(const bf16_t* _
 // Backward
 // ===========================================================================
 constexpr int NB = 128;  // neurons per block
+constexpr int DENSE_DW_XS = 2;  // 128-d sub-tiles per weight-gradient workgroup
 
 // Token ids of a chunk's padded rows (-1 past the chunk's last token).
 __global__ void dense_route_kernel(int t0, int tc, int tc_pad, int32_t* __restrict__ ptoken) {
@@ -409,23 +410,24 @@ __global__ __launch_bounds__(NT, 1) void dense_dw_kernel(const bf16_t* __restric
                                                          float* __restrict__ fu, float* __restrict__ fd,
                                                          bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu,
                                                          bf16_t* __restrict__ dwd) {
-  using C = Dw2<NB>;
-  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE], st2_[C::STAGE];
+  // 256 d per workgroup (two 128-d sub-tiles, two 64 KB stages): the packed
+  // dg/du/a rows are read d/256 times
+  using C = Dw2<NB, DENSE_DW_XS>;
+  __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE];
   ESG_LDS char* st0 = (ESG_LDS char*)st0_;
   ESG_LDS char* st1 = (ESG_LDS char*)st1_;
-  ESG_LDS char* st2 = (ESG_LDS char*)st2_;
   const int nblk = (F + NB - 1) / NB;
   DwWork wk;
-  if (!dw_work(blockIdx.x, 2 * nblk, (d + 127) / 128, wk)) return;
-  const int blk = wk.unit >> 1, db0 = wk.db * 128;
+  if (!dw_work(blockIdx.x, 2 * nblk, (d + C::DW - 1) / C::DW, wk)) return;
+  const int blk = wk.unit >> 1, db0 = wk.db * C::DW;
   const uint32_t pbytes = (uint32_t)((size_t)nblk * tc_pad * NB * 2);
   const int p0 = blk * tc_pad;
   if ((wk.unit & 1) == 0)
-    dw2_body<NB, 0, 3, MODE>(x, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fg, fu, dg, du, pbytes, dwg, dwu,
-                             db0, st0, st1, st2);
+    dw2_body<NB, 0, 2, MODE, DENSE_DW_XS>(x, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fg, fu, dg, du, pbytes,
+                                          dwg, dwu, db0, st0, st1, st1);
   else
-    dw2_body<NB, 1, 3, MODE>(dy, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fd, fd, act, act, pbytes, dwd,
-                             dwd, db0, st0, st1, st2);
+    dw2_body<NB, 1, 2, MODE, DENSE_DW_XS>(dy, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fd, fd, act, act, pbytes, dwd,
+                             dwd, db0, st0, st1, st1);
 }
 
 }  // namespace
@@ -510,7 +512,7 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
     }
     {
       LaunchTimer timer("dense_dw", stream);
-      const dim3 grid(dw_grid(2 * L.nblk, (d + 127) / 128));  // order: dw_work
+      const dim3 grid(dw_grid(2 * L.nblk, (d + 128 * DENSE_DW_XS - 1) / (128 * DENSE_DW_XS)));  // order: dw_work
       const int mode = L.chunks == 1 ? 0 : (c == 0 ? 1 : (c == L.chunks - 1 ? 3 : 2));
 #define ESG_DW(M)                                                                                                  \
   hipLaunchKernelGGL(dense_dw_kernel<M>, grid, dim3(NT), 0, stream, (const bf16_t*)x, (const bf16_t*)dy, s.tokens, \

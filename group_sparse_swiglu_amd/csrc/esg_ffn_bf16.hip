@@ -33,6 +33,14 @@ constexpr int fwd_waves() {
   return GSB >= 128 ? 8 : 4;
 }
 
+// 128-d sub-tiles per weight-gradient workgroup: two for 128-neuron blocks
+// (one workgroup per CU holds the 256 accumulator registers per wave; the
+// packed dg/du/a rows are then read half as often), one for 64-neuron blocks.
+template <int GSB>
+constexpr int dw_subtiles() {
+  return GSB >= 128 ? 2 : 1;
+}
+
 template <int GSB>
 __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void fwd2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
@@ -339,13 +347,14 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ ptoken, uint32_t rows_total,
     const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du, const bf16_t* __restrict__ act,
     bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu, bf16_t* __restrict__ dwd) {
-  using C = Dw2<GSB>;
-  constexpr int NS = stages_for<GSB>();
+  constexpr int XS = dw_subtiles<GSB>();
+  using C = Dw2<GSB, XS>;
+  constexpr int NS = XS == 2 ? 2 : stages_for<GSB>();
   __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE];  // no placeholder for a third stage
   DwWork wk;
-  if (!dw_work(blockIdx.x, 2 * (F / gs) * nsub, (d + 127) / 128, wk)) return;
+  if (!dw_work(blockIdx.x, 2 * (F / gs) * nsub, (d + C::DW - 1) / C::DW, wk)) return;
   const int g = (wk.unit >> 1) / nsub, s = (wk.unit >> 1) % nsub;
-  const int db0 = wk.db * 128;
+  const int db0 = wk.db * C::DW;
   const int nb0 = g * gs + s * GSB;
   const int p0 = tile_off[g] * BM, p1 = tile_off[g + 1] * BM;
   const size_t sub_el = (size_t)s * rows_total * GSB;
@@ -354,10 +363,10 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
   ESG_LDS char* st1 = st0 + C::STAGE;
   ESG_LDS char* st2 = NS == 3 ? st1 + C::STAGE : st0;
   if ((wk.unit & 1) == 0)
-    dw2_body<GSB, 0, NS>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du, pbytes,
+    dw2_body<GSB, 0, NS, 0, XS>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du, pbytes,
                          dwg, dwu, db0, st0, st1, st2);
   else
-    dw2_body<GSB, 1, NS>(dy, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, act, act, pbytes,
+    dw2_body<GSB, 1, NS, 0, XS>(dy, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, act, act, pbytes,
                          dwd, dwd, db0, st0, st1, st2);
 }
 
@@ -395,7 +404,8 @@ hipError_t dw2_t(const FfnShape& s, const void* x, const void* dy, const int32_t
                  int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
                  hipStream_t stream) {
   LaunchTimer timer("bwd_dw", stream);
-  const dim3 grid(dw_grid(2 * s.groups() * s.nsub(), (s.d_model + 127) / 128));  // order: dw_work
+  const dim3 grid(dw_grid(2 * s.groups() * s.nsub(), (s.d_model + 128 * dw_subtiles<GSB>() - 1) /
+                                                         (128 * dw_subtiles<GSB>())));  // order: dw_work
   hipLaunchKernelGGL((dw2_kernel<GSB>), grid, dim3(NT), 0, stream, (const bf16_t*)x, (const bf16_t*)dy, s.tokens,
                      s.d_model, s.d_ff, s.group_size, s.nsub(), tile_off, ptoken, (uint32_t)rows_total,
                      (const bf16_t*)dg, (const bf16_t*)du, (const bf16_t*)act, (bf16_t*)dwg, (bf16_t*)dwu,

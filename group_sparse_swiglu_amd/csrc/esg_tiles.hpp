@@ -345,17 +345,22 @@ __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf1
 // come from one 16-byte load; both operands use the same row order, which
 // only permutes the K summation.
 // ===========================================================================
-template <int GSB>
+// XS 128-d sub-tiles of the gathered operand per stage: a workgroup covers
+// DW = 128*XS d of one neuron block, so the packed dg/du/a rows (which every
+// d-block of the block reads again) are read ceil(d/DW) times.
+template <int GSB, int XS = 1>
 struct Dw2 {
+  static constexpr int DW = 128 * XS;
   static constexpr int NCHP = GSB / 8;           // chunks per position row of dg/du/a
-  static constexpr int X_BYTES = 64 * 256;       // N-row: 64 positions x 128 d
+  static constexpr int X_SUB = 64 * 256;         // N-row: 64 positions x 128 d
+  static constexpr int X_BYTES = XS * X_SUB;
   static constexpr int P_BYTES = 64 * GSB * 2;   // N-row: 64 positions x GSB neurons
   static constexpr int STAGE = X_BYTES + 2 * P_BYTES;
-  static constexpr int IX = 4;
+  static constexpr int IX = 4 * XS;
   static constexpr int IP = NCHP / 4;
   static constexpr int L0 = IX + 2 * IP, L1 = IX + IP;
-  static constexpr int FM0 = 4, FN0 = GSB / 16;  // kind 0 wave tile: 64 d x GSB neurons
-  static constexpr int FM1 = GSB / 32, FN1 = 4;  // kind 1 wave tile: GSB/2 neurons x 64 d
+  static constexpr int FM0 = 4 * XS, FN0 = GSB / 16;  // kind 0 wave tile: 64*XS d x GSB neurons
+  static constexpr int FM1 = GSB / 32, FN1 = 4 * XS;  // kind 1 wave tile: GSB/2 neurons x 64*XS d
 };
 
 // Order of the weight-gradient workgroups.  A "unit" is one (neuron block,
@@ -397,14 +402,14 @@ __device__ __forceinline__ int dw_perm(int r) { return (r & ~15) | ((r & 3) << 2
 // f0/f1; 3 adds f0/f1 and stores bf16 (K split over consecutive launches, in
 // a fixed order).  Ids of the K positions come from ptoken[pid0 ..], their
 // packed dg/du/a rows start at row p0; np positions (a multiple of 64).
-template <int GSB, int KIND, int NS, int MODE = 0>
+template <int GSB, int KIND, int NS, int MODE = 0, int XS = 1>
 __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tokens, int d, int F, int nb0,
                                          const int32_t* __restrict__ ptoken, int pid0, int p0, int np,
                                          size_t sub_el, float* __restrict__ f0, float* __restrict__ f1,
                                          const bf16_t* __restrict__ pa, const bf16_t* __restrict__ pb,
                                          uint32_t pbytes, bf16_t* __restrict__ out0, bf16_t* __restrict__ out1,
                                          int db0, ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2) {
-  using C = Dw2<GSB>;
+  using C = Dw2<GSB, XS>;
   constexpr int NP = KIND == 0 ? 2 : 1;  // packed operand tiles per stage
   constexpr int L = KIND == 0 ? C::L0 : C::L1;
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -458,10 +463,13 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
       tk[c] = q >= 2 ? hi : lo;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = tk[i] >= 0 && db0 + jz[i] * 8 < d;
-      dma16(rz, st + (w * 4 + i) * 1024, ok ? (uint32_t)tk[i] * kbytes + (uint32_t)db0 * 2 + jz[i] * 16 : kOOB);
-    }
+    for (int x = 0; x < XS; ++x)  // 128-d sub-tile x: d from db0 + 128x
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dx = db0 + x * 128 + jz[i] * 8;
+        const bool ok = tk[i] >= 0 && dx < d;
+        dma16(rz, st + x * C::X_SUB + (w * 4 + i) * 1024, ok ? (uint32_t)tk[i] * kbytes + (uint32_t)dx * 2 : kOOB);
+      }
     const uint32_t kofs = (uint32_t)kt * 64 * GSB * 2;
 #pragma unroll
     for (int i = 0; i < C::IP; ++i) dma16(rpa, st + C::X_BYTES + (w * C::IP + i) * 1024, voffP[i] + kofs);
@@ -483,7 +491,10 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (KIND == 0) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[kb][i] = frag_nrow<16>(st, kb, wm * 64 + i * 16, lane);
+        for (int i = 0; i < FM; ++i) {
+          const int dl = wm * 64 * XS + i * 16;  // d within the workgroup's DW
+          a[kb][i] = frag_nrow<16>(st + (dl >> 7) * C::X_SUB, kb, dl & 127, lane);
+        }
         const ESG_LDS char* tb = st + C::X_BYTES + wn * C::P_BYTES;
 #pragma unroll
         for (int j = 0; j < FN; ++j) b[kb][j] = frag_nrow<C::NCHP>(tb, kb, j * 16, lane);
@@ -492,7 +503,10 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
         for (int i = 0; i < FM; ++i)
           a[kb][i] = frag_nrow<C::NCHP>(st + C::X_BYTES, kb, wm * (GSB / 2) + i * 16, lane);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[kb][j] = frag_nrow<16>(st, kb, wn * 64 + j * 16, lane);
+        for (int j = 0; j < FN; ++j) {
+          const int dl = wn * 64 * XS + j * 16;
+          b[kb][j] = frag_nrow<16>(st + (dl >> 7) * C::X_SUB, kb, dl & 127, lane);
+        }
       }
     }
 #pragma unroll
@@ -507,7 +521,7 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
   if constexpr (KIND == 0) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int dd = db0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+      const int dd = db0 + wm * 64 * XS + i * 16 + (lane >> 4) * 4;
       if (dd >= d) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -526,7 +540,7 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
       const int n = wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int dd = db0 + wn * 64 + j * 16 + (lane & 15);
+        const int dd = db0 + wn * 64 * XS + j * 16 + (lane & 15);
         if (dd >= d) continue;
         float v[4];
 #pragma unroll
