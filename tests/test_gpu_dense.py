@@ -30,6 +30,7 @@ DENSE = [
     ("small", 200, 128, 512, 64),            # one chunk, whole 128-neuron blocks
     ("ragged_f448_d208", 257, 208, 448, 64),  # last neuron block half full, d not a multiple of 64
     ("d16", 70, 16, 256, 32),
+    ("ragged_d400", 300, 400, 384, 64),      # second 256-d weight-gradient block: 128 + 16 d
     ("d2048_max", 100, 2048, 256, 128),      # widest d the fused forward holds
     ("two_chunks", 9000, 64, 256, 128),      # backward over 2 token chunks (fp32 dW accumulation)
     ("three_chunks", 20000, 32, 128, 64),    # 3 chunks: first / middle / last accumulation modes

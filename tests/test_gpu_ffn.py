@@ -102,6 +102,7 @@ EDGE = [
     ("d16_gs64", 77, 16, 256, 64, 2, "bf16"),
     ("d208_gs128", 150, 208, 512, 128, 2, "bf16"),
     ("d1040_gs64_k3", 700, 1040, 640, 64, 3, "bf16"),
+    ("d400_gs128_k3", 333, 400, 1024, 128, 3, "bf16"),  # ragged 256-d weight-gradient block
 ]
 
 
