@@ -203,7 +203,39 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   // score, or equal score and lower id); its output slot is its rank among the
   // selected ids (a ballot prefix)
   const uint64_t lt = (1ull << lane) - 1ull;
-  if (groups <= 64) {
+  if (groups <= 32) {
+    // the two half-waves rank two tokens at a time: lane l holds group l % 32
+    // of token half l / 32; a token's other scores are broadcast reads
+    constexpr int TPW = BM / 8;  // token pairs per wave
+    const int hf = lane >> 5, g = lane & 31;
+    float sg[TPW];
+    int beat[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int r = wave + 4 * (2 * i + hf);
+      sg[i] = g < groups ? E[r * ES + g] : 0.0f;
+      beat[i] = 0;
+    }
+    for (int q = 0; q < groups; ++q) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const float sq = E[(wave + 4 * (2 * i + hf)) * ES + q];
+        beat[i] += (sq > sg[i]) || (sq == sg[i] && q < g);
+      }
+    }
+    const uint64_t half = hf ? 0xffffffff00000000ull : 0x00000000ffffffffull;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = t0 + wave + 4 * (2 * i + hf);
+      const bool sel = g < groups && beat[i] < k;
+      const uint64_t m = __ballot(sel) & half;
+      const int pos = __popcll(m & lt);
+      if (t < tokens && sel && pos < k) {  // NaN scores could select more than k: never write past the row
+        idx_out[(size_t)t * k + pos] = g;
+        if (counts) atomicAdd(&cnt[g], 1);
+      }
+    }
+  } else if (groups <= 64) {
     // lane g holds group g of the wave's BM/4 tokens at once; every other
     // group's score comes as a broadcast LDS read (same address in all lanes)
     constexpr int TPW = BM / 4;
