@@ -235,22 +235,22 @@ constexpr int MB_NW = 4;
 
 // A chunk of NC neurons of one sub-network: its [K; U; V] rows over all of
 // d_h as two 64-column K-row sub-tiles.
-template <int NC>
+template <int NC, int NW = MB_NW>
 struct Chunk {
   static constexpr int ROWS = 3 * NC;
   static constexpr int FR = ROWS / 16;           // 16-row fragments: K, U, V in turn
   static constexpr int HALF = ROWS * 128;        // one 64-column sub-tile
   static constexpr int STAGE = 2 * HALF;
-  static constexpr int LW = STAGE / 1024 / MB_NW;  // DMA instructions per lane
-  static_assert(NC % 16 == 0 && STAGE % (1024 * MB_NW) == 0, "whole fragments and DMA instructions");
+  static constexpr int LW = STAGE / 1024 / NW;   // DMA instructions per lane (NW waves)
+  static_assert(NC % 16 == 0 && STAGE % (1024 * NW) == 0, "whole fragments and DMA instructions");
 };
 
 // DMA of one chunk's [K; U; V] rows (neurons n0 .. n0+NC-1 of the sub-network
 // at `base`): instruction ii covers sub-tile ii/(ROWS/8), rows (ii%(ROWS/8))*8 .. +7.
-template <int NC>
+template <int NC, int NW = MB_NW>
 __device__ __forceinline__ void issue_chunk(const DmaSrc& rk, const DmaSrc& ru, const DmaSrc& rv, ESG_LDS char* st,
                                             int w, int lane, uint32_t base, int n0, int d_sub) {
-  using C = Chunk<NC>;
+  using C = Chunk<NC, NW>;
   constexpr int PER = C::ROWS / 8;
   const int c8 = (lane & 7) ^ (lane >> 3);
 #pragma unroll
@@ -265,13 +265,14 @@ __device__ __forceinline__ void issue_chunk(const DmaSrc& rk, const DmaSrc& ru, 
 }
 
 // DMA of a [64 tokens][128] bf16 head slice (Q or dO) into two K-row sub-tiles:
-// 16 instructions, 4 per wave.
+// 16 instructions, 16/NW per wave.
+template <int NW = MB_NW>
 __device__ __forceinline__ void issue_tokens(const DmaSrc& src, ESG_LDS char* dst, int w, int lane, int t0,
                                              int tokens, uint32_t qrow, int h) {
   const int c8 = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ii = w * 4 + i;
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int ii = w * (16 / NW) + i;
     const int sb = ii >> 3, row = (ii & 7) * 8 + (lane >> 3);
     const int t = t0 + row;
     dma16(src, dst + sb * MB_TSUB + (ii & 7) * 1024,
@@ -297,6 +298,31 @@ __device__ __forceinline__ void chunk_phase1(const ESG_LDS char* st, const ESG_L
       for (int f = 0; f < C::FR; ++f) {
         const uint4 a = frag_krow(st + sub * C::HALF, f * 16 + (lane & 15), c);
         mma_bf16(acc[f], a, f < 2 * C::FR / 3 ? bq : bo);
+      }
+    }
+}
+
+// Phase 1 of 16 of a chunk's neurons (fragment p of each of K, U, V) for the
+// 16 tokens [tok0, +16): acc = {h1, h2, g} of those neurons (the layout of a
+// 16-neuron chunk, so chunk_grads<16> applies).
+template <int NC>
+__device__ __forceinline__ void chunk_phase1_part(const ESG_LDS char* st, const ESG_LDS char* qt,
+                                                  const ESG_LDS char* dot, int tok0, int p, int lane,
+                                                  f32x4 (&acc)[3]) {
+  using C = Chunk<NC>;
+  constexpr int F1 = NC / 16;
+  zero_acc(acc);
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int c = kb * 4 + (lane >> 4);
+      const uint4 bq = frag_krow(qt + sub * MB_TSUB, tok0 + (lane & 15), c);
+      const uint4 bo = frag_krow(dot + sub * MB_TSUB, tok0 + (lane & 15), c);
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        const uint4 a = frag_krow(st + sub * C::HALF, (m * F1 + p) * 16 + (lane & 15), c);
+        mma_bf16(acc[m], a, m < 2 ? bq : bo);
       }
     }
 }
@@ -339,17 +365,25 @@ __device__ __forceinline__ ChunkGrads chunk_grads(const f32x4 (&acc)[Chunk<NC>::
 // resident; wider chunks mean fewer passes over the tokens)
 constexpr int MBQ_NC = 32, MBW_NC = 48;
 
-__global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
+// Eight waves: for phase 1 wave w takes tokens [(w%4)*16, +16) and neurons
+// [(w/4)*16, +16) of the chunk (the two neuron halves' dR partials are added
+// in a fixed order through LDS); for phase 2 it takes d_h [w*16, +16) for all
+// 64 tokens.  Two waves per SIMD: one's epilogue overlaps the other's MFMAs.
+constexpr int MBQ_NW = 8;
+__global__ __launch_bounds__(64 * MBQ_NW, 1) void mhffn_bwd_dq_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ q, const float* __restrict__ r,
     const bf16_t* __restrict__ kw, const bf16_t* __restrict__ uw, const bf16_t* __restrict__ vw, int tokens,
     int heads, int subnets, int d_sub, bf16_t* __restrict__ dq, float* __restrict__ dr) {
-  using C = Chunk<MBQ_NC>;
+  constexpr int NTQ = 64 * MBQ_NW;
+  using C = Chunk<MBQ_NC, MBQ_NW>;
+  static_assert(MBQ_NC == 32 && MBQ_NW == 8, "two neuron halves of 16 x four token groups");
   __shared__ __attribute__((aligned(1024))) char ring_[3 * C::STAGE];
   __shared__ __attribute__((aligned(1024))) char qt_[2 * MB_TSUB];
   __shared__ __attribute__((aligned(1024))) char dot_[2 * MB_TSUB];
   __shared__ __attribute__((aligned(1024))) char dh_[MB_TSUB];  // [token][dh1 (32) | dh2 (32)]
   __shared__ float rtab[MB_TM * MH_MAXE];
   __shared__ float drtab[MB_TM * MH_MAXE];
+  __shared__ float drpart[2][MB_TM];  // the step's dR sums of each neuron half
   ESG_LDS char* ring = (ESG_LDS char*)ring_;
   ESG_LDS char* qt = (ESG_LDS char*)qt_;
   ESG_LDS char* dot = (ESG_LDS char*)dot_;
@@ -363,57 +397,49 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
   const uint32_t wtotal = (uint32_t)heads * subnets * wbytes_he;
   const DmaSrc rk = make_dma_src(kw, wtotal), ru = make_dma_src(uw, wtotal), rv = make_dma_src(vw, wtotal);
 
-  for (int i = threadIdx.x; i < MB_TM * subnets; i += NT) {
+  for (int i = threadIdx.x; i < MB_TM * subnets; i += NTQ) {
     const int t = t0 + i / subnets;
     rtab[i] = t < tokens ? r[((size_t)t * heads + h) * subnets + i % subnets] : 0.0f;
     drtab[i] = 0.0f;
   }
-  issue_tokens(make_dma_src(q, (uint32_t)tokens * qrow), qt, w, lane, t0, tokens, qrow, h);
-  issue_tokens(make_dma_src(dout, (uint32_t)tokens * qrow), dot, w, lane, t0, tokens, qrow, h);
+  issue_tokens<MBQ_NW>(make_dma_src(q, (uint32_t)tokens * qrow), qt, w, lane, t0, tokens, qrow, h);
+  issue_tokens<MBQ_NW>(make_dma_src(dout, (uint32_t)tokens * qrow), dot, w, lane, t0, tokens, qrow, h);
 
-  const int tok0 = w * 16, tl = tok0 + (lane & 15);  // the wave's tokens; this lane's token
-  f32x4 acc1[C::FR];
-  f32x4 acc2[2][4];  // dQ^T: d_h [w*32, +32) x the tile's 4 token fragments
+  const int nh = w >> 2;                                 // neuron half of phase 1
+  const int tok0 = (w & 3) * 16, tl = tok0 + (lane & 15);  // the wave's tokens; this lane's token
+  f32x4 acc1[3];
+  f32x4 acc2[4];  // dQ^T: d_h [w*16, +16) x the tile's 4 token fragments
   zero_acc(acc2);
   auto issue = [&](ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int e = s / nchunks, n0 = (s % nchunks) * MBQ_NC;
-    issue_chunk<MBQ_NC>(rk, ru, rv, st, w, lane, (uint32_t)(h * subnets + e) * wbytes_he, n0, d_sub);
+    issue_chunk<MBQ_NC, MBQ_NW>(rk, ru, rv, st, w, lane, (uint32_t)(h * subnets + e) * wbytes_he, n0, d_sub);
   };
   auto compute = [&](const ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int e = s / nchunks;
-    chunk_phase1<MBQ_NC>(st, qt, dot, tok0, lane, acc1);
+    chunk_phase1_part<MBQ_NC>(st, qt, dot, tok0, nh, lane, acc1);
     const float rw = rtab[tl * subnets + e];
-    float drp = 0.0f;
-#pragma unroll
-    for (int p = 0; p < MBQ_NC / 16; ++p) {
-      const ChunkGrads cg = chunk_grads<MBQ_NC>(acc1, p, rw);
-      drp += cg.dr;
-      const int n = p * 16 + (lane >> 4) * 4;  // dh1 column n, dh2 column 32 + n
-      lds_write8(dh + krow_off(tl, n >> 3) + (n & 7) * 2, cg.dh1[0], cg.dh1[1]);
-      const int n2 = MBQ_NC + n;
-      lds_write8(dh + krow_off(tl, n2 >> 3) + (n2 & 7) * 2, cg.dh2[0], cg.dh2[1]);
-    }
+    const ChunkGrads cg = chunk_grads<16>(acc1, 0, rw);
+    const int n = nh * 16 + (lane >> 4) * 4;  // dh1 column n, dh2 column 32 + n
+    lds_write8(dh + krow_off(tl, n >> 3) + (n & 7) * 2, cg.dh1[0], cg.dh1[1]);
+    const int n2 = MBQ_NC + n;
+    lds_write8(dh + krow_off(tl, n2 >> 3) + (n2 & 7) * 2, cg.dh2[0], cg.dh2[1]);
+    float drp = cg.dr;
     drp += __shfl_xor(drp, 16);
     drp += __shfl_xor(drp, 32);
-    if (lane < 16) drtab[tl * subnets + e] += drp;  // the wave owns these tokens: no other writer
+    if (lane < 16) drpart[nh][tl] = drp;
     wait_lgkm0();
-    barrier();  // every wave's dh rows are written
+    barrier();  // every wave's dh rows and dR halves are written
+    if (nh == 0 && lane < 16) drtab[tl * subnets + e] += drpart[0][tl] + drpart[1][tl];  // one writer per row
     // dQ^T += [K; U]^T [dh1 dh2]^T  (K index = the 64 K and U neuron rows of the
-    // stage); wave w takes d_h [w*32, +32) for all 64 tokens
+    // stage); wave w takes d_h [w*16, +16) for all 64 tokens
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint4 a[2], b[4];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jf = 2 * w + jj;
-        a[jj] = frag_krow_t(st + (jf >> 2) * C::HALF, kb, (jf & 3) * 16, lane);
-      }
+      const uint4 a = frag_krow_t(st + (w >> 2) * C::HALF, kb, (w & 3) * 16, lane);
+      uint4 b[4];
 #pragma unroll
       for (int tf = 0; tf < 4; ++tf) b[tf] = frag_krow(dh, tf * 16 + (lane & 15), kb * 4 + (lane >> 4));
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int tf = 0; tf < 4; ++tf) mma_bf16(acc2[jj][tf], a[jj], b[tf]);
+      for (int tf = 0; tf < 4; ++tf) mma_bf16(acc2[tf], a, b[tf]);
     }
   };
   // the Q and dO tiles' loads are older than the ring's: the first wait covers them
@@ -425,17 +451,14 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dq_kernel(
   for (int tf = 0; tf < 4; ++tf) {
     const int t = t0 + tf * 16 + (lane & 15);
     if (t < tokens) {
+      const int j = w * 16 + (lane >> 4) * 4;
+      float v[4];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = (2 * w + jj) * 16 + (lane >> 4) * 4;
-        float v[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = acc2[jj][tf][x];
-        Quad<bf16_t>::store(dq + ((size_t)t * heads + h) * MH_DH + j, v);
-      }
+      for (int x = 0; x < 4; ++x) v[x] = acc2[tf][x];
+      Quad<bf16_t>::store(dq + ((size_t)t * heads + h) * MH_DH + j, v);
     }
   }
-  for (int i = threadIdx.x; i < MB_TM * subnets; i += NT) {
+  for (int i = threadIdx.x; i < MB_TM * subnets; i += NTQ) {
     const int tt = t0 + i / subnets;
     if (tt < tokens) dr[((size_t)tt * heads + h) * subnets + i % subnets] = drtab[i];
   }
@@ -582,7 +605,8 @@ hipError_t launch_mhffn_bwd(const void* dout, const void* q, const float* r, con
                             void* dk, void* du, void* dv, hipStream_t stream) {
   if (tokens > 0) {
     LaunchTimer timer("mhffn_bwd_dq", stream);
-    hipLaunchKernelGGL(mhffn_bwd_dq_kernel, dim3((tokens + MB_TM - 1) / MB_TM, heads), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(mhffn_bwd_dq_kernel, dim3((tokens + MB_TM - 1) / MB_TM, heads), dim3(64 * MBQ_NW), 0,
+                       stream,
                        (const bf16_t*)dout, (const bf16_t*)q, r, (const bf16_t*)k, (const bf16_t*)u,
                        (const bf16_t*)v, tokens, heads, subnets, d_sub, (bf16_t*)dq, dr);
     hipError_t e = hipGetLastError();
