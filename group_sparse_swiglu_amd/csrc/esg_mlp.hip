@@ -38,17 +38,21 @@ constexpr int GP = 128, GK = 64;
 constexpr int B_BYTES = GP * 128;  // 16 KB: K-row 128 x 128 B, or N-row 64 x 256 B
 
 // Output tile TQ (256 or 128) columns x 128 rows.  256: three 48 KB stages,
-// one workgroup per compute unit, waves of 128 x 64.  128: two 32 KB stages,
-// two workgroups per compute unit (one's epilogue overlaps the other's
-// loop), waves of 64 x 64.
+// one 8-wave workgroup per compute unit, waves of 64 x 64.  128: two 32 KB
+// stages, two 4-wave workgroups per compute unit (one's epilogue overlaps
+// the other's loop), waves of 64 x 64.  Eight waves per CU either way: the
+// direct-to-LDS loads of a CU go faster with more waves issuing them.
 template <int TQ>
 struct TileCfg {
   static constexpr int NS = TQ == 256 ? 3 : 2;
   static constexpr int OCC = TQ == 256 ? 1 : 2;
+  static constexpr int NW = TQ == 256 ? 8 : 4;    // waves: NW/2 q slices x 2 p halves
+  static constexpr int NTH = 64 * NW;
   static constexpr int A_BYTES = TQ * 128;  // K-row TQ x 128 B, or N-row TQ/128 x (64 x 256 B)
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDMA = STAGE / 1024 / 4;  // 1 KB DMA instructions per wave per stage
-  static constexpr int FM = TQ / 32;             // 16-wide q fragments per wave
+  static constexpr int LDMA = STAGE / 1024 / NW;  // 1 KB DMA instructions per wave per stage
+  static constexpr int HQ = TQ / (NW / 2);        // q columns per wave
+  static constexpr int FM = HQ / 16;              // 16-wide q fragments per wave
 };
 
 struct GemmArgs {
@@ -71,9 +75,9 @@ struct GemmArgs {
 // of 128 bytes, lane -> row lane/8, logical chunk (lane%8)^(row%8).  N-row:
 // instruction covers 4 K rows of 256 bytes, lane -> row lane/16, logical
 // chunk (lane%16)^swz(row).
-template <int LAY, int ROWS>
+template <int LAY, int ROWS, int NW>
 struct OperandDma {
-  static constexpr int NI = ROWS * 128 / 1024 / 4;  // instructions per wave per stage
+  static constexpr int NI = ROWS * 128 / 1024 / NW;  // instructions per wave per stage
   uint32_t base[NI];    // byte offset of this lane's chunk at K step 0 (kOOB: outside)
   uint32_t kstep;       // bytes to add per K step
   int koff[NI];         // K offset within a step: of the lane's chunk (K-row) or of its row (N-row)
@@ -92,7 +96,7 @@ struct OperandDma {
       // stage rows: ROWS/128 halves of 128 columns, 64 K rows each
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int ii = w * NI + i;           // 0 .. 4*NI-1
+        const int ii = w * NI + i;           // 0 .. NW*NI-1
         const int half = ii / 16;            // 16 instructions per half (64 rows x 256 B)
         const int kr = (ii % 16) * 4 + (lane >> 4);
         const int j = (lane & 15) ^ mn_swz<16>(kr);
@@ -137,13 +141,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int qb, int pb, int
 
   const DmaSrc ra = make_dma_src(g.a, AL == KROW ? (uint32_t)g.Q * g.lda * 2 : (uint32_t)g.K * g.lda * 2);
   const DmaSrc rb = make_dma_src(g.b, BL == KROW ? (uint32_t)g.P * g.ldb * 2 : (uint32_t)g.K * g.ldb * 2);
-  OperandDma<AL, TQ> da;
-  OperandDma<BL, GP> db;
+  OperandDma<AL, TQ, C::NW> da;
+  OperandDma<BL, GP, C::NW> db;
   da.init(w, lane, q0, g.Q, g.lda, kbeg);
   db.init(w, lane, p0, g.P, g.ldb, kbeg);
 
-  const int wm = w & 1, wn = w >> 1;  // wave: q [wm*TQ/2, +TQ/2), p [wn*64, +64)
-  constexpr int FM = C::FM, FN = 4, HQ = TQ / 2;
+  const int wm = w % (C::NW / 2), wn = w / (C::NW / 2);  // wave: q [wm*HQ, +HQ), p [wn*64, +64)
+  constexpr int FM = C::FM, FN = 4, HQ = C::HQ;
 
   // EPI_MUL: the act_grad values of this lane's outputs, loaded before the K
   // loop (the first pipeline wait covers them)
@@ -198,7 +202,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int qb, int pb, int
           *(float4*)(out + (size_t)p * g.Q + q) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       }
   } else {
-    using RS = RowStore<TQ>;
+    using RS = RowStore<TQ, C::NTH>;
     const rsrc_t rc0 = make_rsrc(g.c0, (uint32_t)g.P * g.ldc * 2);
     uint32_t row_off[RS::IT];
 #pragma unroll
@@ -265,7 +269,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int qb, int pb, int
 // block (same token rows) share an XCD; with splits, item t takes split
 // t % splits, so with 8 splits each split's token range is read by one XCD.
 template <int TQ, int AL, int BL, int EPI>
-__global__ __launch_bounds__(NT, TileCfg<TQ>::OCC) void mlp_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(TileCfg<TQ>::NTH, TileCfg<TQ>::OCC) void mlp_gemm_kernel(GemmArgs g) {
   using C = TileCfg<TQ>;
   __shared__ __attribute__((aligned(1024))) char stages_[C::NS * C::STAGE];
   for (int t = blockIdx.x; t < g.nitems; t += gridDim.x) {
@@ -312,7 +316,7 @@ hipError_t launch_gemm(const char* name, GemmArgs a, int splits, hipStream_t str
   const int slots = compute_units() * TileCfg<TQ>::OCC;
   const int blocks = std::min((a.nitems + 7) / 8 * 8, slots / 8 * 8);
   LaunchTimer timer(name, stream);
-  hipLaunchKernelGGL((mlp_gemm_kernel<TQ, AL, BL, EPI>), dim3(blocks), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((mlp_gemm_kernel<TQ, AL, BL, EPI>), dim3(blocks), dim3(TileCfg<TQ>::NTH), 0, stream, a);
   return hipGetLastError();
 }
 
