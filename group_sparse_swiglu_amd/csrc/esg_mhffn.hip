@@ -363,7 +363,7 @@ __device__ __forceinline__ ChunkGrads chunk_grads(const f32x4 (&acc)[Chunk<NC>::
 // chunk widths: 32 neurons for the dQ/dR kernel (three 24 KB ring stages fit
 // beside its resident tiles), 48 for the weight-gradient kernel (its chunk is
 // resident; wider chunks mean fewer passes over the tokens)
-constexpr int MBQ_NC = 32, MBW_NC = 48;
+constexpr int MBQ_NC = 32, MBW_NC = 64;
 
 // Eight waves: for phase 1 wave w takes tokens [(w%4)*16, +16) and neurons
 // [(w/4)*16, +16) of the chunk (the two neuron halves' dR partials are added
@@ -464,15 +464,26 @@ __global__ __launch_bounds__(64 * MBQ_NW, 1) void mhffn_bwd_dq_kernel(
   }
 }
 
-__global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
+// Eight waves over a resident chunk of 64 neurons: for phase 1 wave w takes
+// tokens [(w%4)*16, +16) and neurons [(w/4)*32, +32) (fragments of K, U, V in
+// the layout of a 32-neuron chunk); for phase 2 it takes d_h [(w%4)*32, +32) x
+// neurons [(w/4)*32, +32) of dK, dU and dV.  Two ring stages fit beside the
+// 48 KB chunk and the three [token][neuron] tiles.
+constexpr int MBW_NW = 8;
+__global__ __launch_bounds__(64 * MBW_NW, 1) void mhffn_bwd_dw_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ q, const float* __restrict__ r,
     const bf16_t* __restrict__ kw, const bf16_t* __restrict__ uw, const bf16_t* __restrict__ vw, int tokens,
     int heads, int subnets, int d_sub, bf16_t* __restrict__ dk, bf16_t* __restrict__ du, bf16_t* __restrict__ dv) {
-  using C = Chunk<MBW_NC>;
-  constexpr int TSTAGE = 4 * MB_TSUB + 1024;  // Q (2 sub-tiles), dO (2), router weights (4 x 256 B)
+  using C = Chunk<MBW_NC, MBW_NW>;
+  static_assert(MBW_NC == 64 && MBW_NW == 8, "four token groups x two neuron halves of 32");
+  // Q (2 sub-tiles), dO (2), router weights (4 x 256 B), and 1 KB where the
+  // second neuron half's empty router loads land (an out-of-range load still
+  // writes its zeros to LDS)
+  constexpr int TSTAGE = 4 * MB_TSUB + 2048;
+  constexpr int LT = 2 * (16 / MBW_NW) + 1;  // loads per lane per token stage
   __shared__ __attribute__((aligned(1024))) char wt_[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char ring_[3 * TSTAGE];
-  __shared__ __attribute__((aligned(1024))) char tiles_[3 * MB_TSUB];  // [token][48] dh1 | dh2 | R*a
+  __shared__ __attribute__((aligned(1024))) char ring_[2 * TSTAGE];
+  __shared__ __attribute__((aligned(1024))) char tiles_[3 * MB_TSUB];  // [token][64] dh1 | dh2 | R*a
   ESG_LDS char* wt = (ESG_LDS char*)wt_;
   ESG_LDS char* ring = (ESG_LDS char*)ring_;
   ESG_LDS char* t_dh1 = (ESG_LDS char*)tiles_;
@@ -485,29 +496,32 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
   const uint32_t wbytes_he = (uint32_t)d_sub * MH_DH * 2;
   const uint32_t wtotal = (uint32_t)heads * subnets * wbytes_he;
   const uint32_t base = (uint32_t)(h * subnets + e) * wbytes_he;
-  issue_chunk<MBW_NC>(make_dma_src(kw, wtotal), make_dma_src(uw, wtotal), make_dma_src(vw, wtotal), wt, w, lane, base,
-                      n0, d_sub);
+  issue_chunk<MBW_NC, MBW_NW>(make_dma_src(kw, wtotal), make_dma_src(uw, wtotal), make_dma_src(vw, wtotal), wt, w,
+                              lane, base, n0, d_sub);
   const DmaSrc rq = make_dma_src(q, (uint32_t)tokens * qrow);
   const DmaSrc ro = make_dma_src(dout, (uint32_t)tokens * qrow);
   const DmaSrc rr = make_dma_src(r, (uint32_t)tokens * heads * subnets * 4);
 
-  const int tok0 = w * 16, tl = tok0 + (lane & 15);
+  const int tg = w & 3, nh = w >> 2;
+  const int tok0 = tg * 16, tl = tok0 + (lane & 15);
   auto issue = [&](ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int t0 = s * MB_TM;
-    issue_tokens(rq, st, w, lane, t0, tokens, qrow, h);
-    issue_tokens(ro, st + 2 * MB_TSUB, w, lane, t0, tokens, qrow, h);
-    // router weights of the wave's 16 tokens: lanes 0..15, 4 bytes each
+    issue_tokens<MBW_NW>(rq, st, w, lane, t0, tokens, qrow, h);
+    issue_tokens<MBW_NW>(ro, st + 2 * MB_TSUB, w, lane, t0, tokens, qrow, h);
+    // router weights of token group tg: lanes 0..15 of the waves of the first
+    // neuron half, 4 bytes each (the other waves issue an empty load into the
+    // sink, so that every wave counts the same loads)
     const int t = t0 + tok0 + lane;
-    dma4(rr, st + 4 * MB_TSUB + w * 256,
-         (lane < 16 && t < tokens) ? ((uint32_t)t * heads + h) * subnets * 4 + e * 4 : kOOB);
+    dma4(rr, st + 4 * MB_TSUB + nh * 1024 + tg * 256,
+         (nh == 0 && lane < 16 && t < tokens) ? ((uint32_t)t * heads + h) * subnets * 4 + e * 4 : kOOB);
   };
-  // phase 2 wave tile: d_h [w*32, +32) x the chunk's 48 neurons, for dK, dU, dV
-  f32x4 acc2[3][2][3];
+  // phase 2 wave tile: d_h [tg*32, +32) x neurons [nh*32, +32), for dK, dU, dV
+  f32x4 acc2[3][2][2];
   zero_acc(acc2);
-  f32x4 acc1[C::FR];
-  // the resident chunk's phase-1 fragments, read from LDS once (step 0) and
-  // kept in registers: [d_h sub-tile][32-wide K block][row fragment]
-  uint4 wf[2][2][C::FR];
+  f32x4 acc1[6];  // K0 K1 U0 U1 V0 V1 of the wave's 32 neurons
+  // the resident chunk's phase-1 fragments of the wave's neurons, read from
+  // LDS once (step 0) and kept in registers: [d_h sub-tile][32-wide K block][fragment]
+  uint4 wf[2][2][6];
   auto compute = [&](const ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const ESG_LDS char* qs = st;
     const ESG_LDS char* os = st + 2 * MB_TSUB;
@@ -517,8 +531,10 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int f = 0; f < C::FR; ++f)
-            wf[sub][kb][f] = frag_krow(wt + sub * C::HALF, f * 16 + (lane & 15), kb * 4 + (lane >> 4));
+          for (int f = 0; f < 6; ++f) {
+            const int row = ((f >> 1) * (MBW_NC / 16) + nh * 2 + (f & 1)) * 16 + (lane & 15);  // mat f/2
+            wf[sub][kb][f] = frag_krow(wt + sub * C::HALF, row, kb * 4 + (lane >> 4));
+          }
     }
     zero_acc(acc1);
 #pragma unroll
@@ -529,39 +545,40 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
         const uint4 bq = frag_krow(qs + sub * MB_TSUB, tl, c);
         const uint4 bo = frag_krow(os + sub * MB_TSUB, tl, c);
 #pragma unroll
-        for (int f = 0; f < C::FR; ++f) mma_bf16(acc1[f], wf[sub][kb][f], f < 2 * C::FR / 3 ? bq : bo);
+        for (int f = 0; f < 6; ++f) mma_bf16(acc1[f], wf[sub][kb][f], f < 4 ? bq : bo);
       }
-    const float rw = *(const ESG_LDS float*)(st + 4 * MB_TSUB + w * 256 + (lane & 15) * 4);
+    const float rw = *(const ESG_LDS float*)(st + 4 * MB_TSUB + tg * 256 + (lane & 15) * 4);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const ChunkGrads cg = chunk_grads<MBW_NC>(acc1, p, rw);
-      const int n = p * 16 + (lane >> 4) * 4;
+    for (int p = 0; p < 2; ++p) {
+      const ChunkGrads cg = chunk_grads<32>(acc1, p, rw);
+      const int n = nh * 32 + p * 16 + (lane >> 4) * 4;
       const int o = krow_off(tl, n >> 3) + (n & 7) * 2;
       lds_write8(t_dh1 + o, cg.dh1[0], cg.dh1[1]);
       lds_write8(t_dh2 + o, cg.dh2[0], cg.dh2[1]);
       lds_write8(t_ra + o, cg.ra[0], cg.ra[1]);
     }
     wait_lgkm0();
-    barrier();  // every wave's token rows of the tiles are written
+    barrier();  // every wave's part of the tiles is written
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {  // K = the tile's 64 tokens
-      uint4 aq[2], ao[2], b1[3], b2[3], br[3];
+      uint4 aq[2], ao[2], b1[2], b2[2], br[2];
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf) {
-        const int j0 = w * 32 + jf * 16;
+        const int j0 = tg * 32 + jf * 16;
         aq[jf] = frag_krow_t(qs + (j0 >> 6) * MB_TSUB, kb, j0 & 63, lane);
         ao[jf] = frag_krow_t(os + (j0 >> 6) * MB_TSUB, kb, j0 & 63, lane);
       }
 #pragma unroll
-      for (int nf = 0; nf < 3; ++nf) {
-        b1[nf] = frag_krow_t(t_dh1, kb, nf * 16, lane);
-        b2[nf] = frag_krow_t(t_dh2, kb, nf * 16, lane);
-        br[nf] = frag_krow_t(t_ra, kb, nf * 16, lane);
+      for (int nf = 0; nf < 2; ++nf) {
+        const int c0 = nh * 32 + nf * 16;
+        b1[nf] = frag_krow_t(t_dh1, kb, c0, lane);
+        b2[nf] = frag_krow_t(t_dh2, kb, c0, lane);
+        br[nf] = frag_krow_t(t_ra, kb, c0, lane);
       }
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-        for (int nf = 0; nf < 3; ++nf) {
+        for (int nf = 0; nf < 2; ++nf) {
           mma_bf16(acc2[0][jf][nf], aq[jf], b1[nf]);
           mma_bf16(acc2[1][jf][nf], aq[jf], b2[nf]);
           mma_bf16(acc2[2][jf][nf], ao[jf], br[nf]);
@@ -569,7 +586,7 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
     }
   };
   // the resident chunk's loads are older than the ring's: the first wait covers them
-  kloop<3, 9, 0>((tokens + MB_TM - 1) / MB_TM, ring, ring + TSTAGE, ring + 2 * TSTAGE, issue, compute);
+  kloop<2, LT, 0>((tokens + MB_TM - 1) / MB_TM, ring, ring + TSTAGE, ring, issue, compute);
   wait_vmcnt<0>();  // with no tokens the resident chunk may still be landing
 
   bf16_t* outs[3] = {dk, du, dv};
@@ -578,9 +595,9 @@ __global__ __launch_bounds__(NT, 1) void mhffn_bwd_dw_kernel(
 #pragma unroll
     for (int jf = 0; jf < 2; ++jf)
 #pragma unroll
-      for (int nf = 0; nf < 3; ++nf) {
-        const int j = w * 32 + jf * 16 + (lane >> 4) * 4;
-        const int n = n0 + nf * 16 + (lane & 15);
+      for (int nf = 0; nf < 2; ++nf) {
+        const int j = tg * 32 + jf * 16 + (lane >> 4) * 4;
+        const int n = n0 + nh * 32 + nf * 16 + (lane & 15);
         if (n < d_sub) {
           float v[4];
 #pragma unroll
@@ -613,7 +630,7 @@ hipError_t launch_mhffn_bwd(const void* dout, const void* q, const float* r, con
     if (e != hipSuccess) return e;
   }
   LaunchTimer timer("mhffn_bwd_dw", stream);
-  hipLaunchKernelGGL(mhffn_bwd_dw_kernel, dim3((d_sub + MBW_NC - 1) / MBW_NC, subnets, heads), dim3(NT), 0, stream,
+  hipLaunchKernelGGL(mhffn_bwd_dw_kernel, dim3((d_sub + MBW_NC - 1) / MBW_NC, subnets, heads), dim3(64 * MBW_NW), 0, stream,
                      (const bf16_t*)dout, (const bf16_t*)q, r, (const bf16_t*)k, (const bf16_t*)u, (const bf16_t*)v,
                      tokens, heads, subnets, d_sub, (bf16_t*)dk, (bf16_t*)du, (bf16_t*)dv);
   return hipGetLastError();
