@@ -354,7 +354,17 @@ __device__ __forceinline__ void add_vec(float (&acc)[Elem<T>::EPC], const uint4&
   }
 }
 
-// Workgroup `bid` of `nblk` (256 threads each) takes every nblk-th run of 256 vectors.
+// 16-byte load marked nontemporal: the line is not kept in the caches (for data
+// read exactly once, such as the partial rows of a row sum).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t w = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
+// Workgroup `bid` of `nblk` (256 threads each) takes every nblk-th run of 256
+// vectors.  The partial rows are read once, with nontemporal loads (measured
+// about 20% faster than cached loads right after the kernel that wrote them).
 template <typename T>
 __device__ __forceinline__ void rowsum_range(const T* __restrict__ partials, size_t sub_stride, int nsub,
                                              const int32_t* __restrict__ pinv, int tokens, int k, int d,
@@ -378,7 +388,7 @@ __device__ __forceinline__ void rowsum_range(const T* __restrict__ partials, siz
         uint4 q[KB];
 #pragma unroll
         for (int j = 0; j < KB; ++j)
-          q[j] = p[j] >= 0 ? *(const uint4*)(base + (size_t)p[j] * d) : make_uint4(0, 0, 0, 0);
+          q[j] = p[j] >= 0 ? load_nt16(base + (size_t)p[j] * d) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < KB; ++j)
           if (p[j] >= 0) add_vec<T>(acc, q[j]);

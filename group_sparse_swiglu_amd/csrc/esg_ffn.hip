@@ -660,7 +660,8 @@ hipError_t launch_rowsum(const FfnShape& s, const void* partials, size_t sub_str
   if (s.tokens == 0) return hipSuccess;
   const int epc = s.dtype == 0 ? 4 : 8;
   const size_t vecs = (size_t)s.tokens * (s.d_model / epc);
-  const int blocks = (int)((vecs + 255) / 256 < 8192 ? (vecs + 255) / 256 : 8192);
+  // one vector per thread (measured faster than fewer workgroups looping)
+  const int blocks = (int)((vecs + 255) / 256 < (1u << 20) ? (vecs + 255) / 256 : (1u << 20));
   LaunchTimer timer("rowsum", stream);
   if (s.dtype == 0)
     hipLaunchKernelGGL(rowsum_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)partials,

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("T,G,k,shuffle", [(1, 2, 1, False), (100, 16, 4, False), (777, 43, 11, True),
                                            (8192, 32, 8, False), (32768, 43, 11, False), (5000, 1024, 3, True),
-                                           (64, 8, 8, True), (129, 300, 128, True)])
+                                           (64, 8, 8, True), (129, 300, 128, True), (65, 43, 11, True),
+                                           (64, 1024, 128, True), (0, 16, 4, False)])
 def test_bucket_matches_oracle(T, G, k, shuffle):
     require_gpu()
     note(f"bucket T={T} G={G} k={k}")
@@ -32,11 +33,21 @@ def test_bucket_matches_oracle(T, G, k, shuffle):
     assert status.item() == 0
 
 
-def test_bucket_skips_invalid_ids():
+def _invalid_idx(T, G, k, seed):
+    """Ids drawn from [-3, G + 3) with many repeats: out-of-range ids and repeats in every block."""
+    if T == 5:
+        return torch.tensor([[1, 3, 5], [2, 2, 4], [-1, 9, 10], [7, 1000, 7], [0, 1, 2]], dtype=torch.int32)
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.randint(-3, G + 3, (T, k), generator=g, dtype=torch.int32)
+    idx[:, -1] = idx[:, 0]   # a repeat in every token
+    return idx
+
+
+@pytest.mark.parametrize("T,G,k", [(5, 10, 3), (300, 50, 6), (64, 40, 12)])
+def test_bucket_skips_invalid_ids(T, G, k):
     require_gpu()
-    note("bucket invalid ids")
-    G = 10
-    idx = torch.tensor([[1, 3, 5], [2, 2, 4], [-1, 9, 10], [7, 1000, 7], [0, 1, 2]], dtype=torch.int32)
+    note(f"bucket invalid ids T={T} G={G} k={k}")
+    idx = _invalid_idx(T, G, k, seed=T)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     off, perm_t, inv = E.bucket_by_group(idx.to(DEV), G, status)
     torch.cuda.synchronize()
