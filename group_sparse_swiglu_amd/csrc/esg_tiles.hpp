@@ -43,7 +43,9 @@ struct RowStore {
     ESG_LDS char* h = r < 64 ? lds0 : lds1;
     lds_write8(h + off(r & 63, dl >> 3) + (dl & 7) * 2, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
-  // after a barrier: every thread stores IT chunks of 16 bytes
+  // after a barrier: every thread stores IT chunks of 16 bytes (CPOL: the
+  // buffer store's cache policy, 2 = nontemporal)
+  template <int CPOL = 0>
   static __device__ __forceinline__ void flush(const ESG_LDS char* lds0, const ESG_LDS char* lds1, rsrc_t rp,
                                                const uint32_t (&row_off)[IT], int db0, int d) {
     const int tid = threadIdx.x;
@@ -53,7 +55,7 @@ struct RowStore {
       const u32x4_t q = *(const ESG_LDS u32x4_t*)((r < 64 ? lds0 : lds1) + off(r & 63, c));
       const int dd = db0 + c * 8;
       const uint32_t o = (row_off[it] != kOOB && dd < d) ? row_off[it] + dd * 2 : kOOB;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32, q), rp, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32, q), rp, o, 0, CPOL);
     }
   }
 };

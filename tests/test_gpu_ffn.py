@@ -57,6 +57,8 @@ def test_ffn_workload_full(case):
 WORKLOAD_SAMPLED = [
     ("s370m_bf16", 16384, 1024, 2688, 128, 5, "bf16", 16, True),
     ("s1p3b_bf16", 32768, 2048, 5504, 128, 11, "bf16", 16, True),
+    # 64-neuron groups with partial rows past the cached-store limit (about 270 MB)
+    ("gs64_partials_270mb", 16384, 2048, 4096, 64, 4, "bf16", 8, True),
 ]
 
 
