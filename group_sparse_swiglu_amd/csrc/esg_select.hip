@@ -23,23 +23,27 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int KC = 4;  // chunks per K stage
+constexpr size_t kSelLds = 160 * 1024;
 
 // BM tokens per workgroup; each wave owns FNW 16-column fragments of a
 // super-chunk of 4*FNW*16 sampled rows, interleaved across the waves, so the
 // x tile is read once per super-chunk.
-// bf16 with BM = 32 streams both operands by direct-to-LDS loads into K-row
-// tiles (64 K per stage, DMA_NS stages); other cases stage through registers.
+// bf16 with BM = 32 or 128 streams both operands by direct-to-LDS loads
+// into K-row tiles (64 K per stage, DMA_NS stages); other cases stage through
+// registers.  Every workgroup streams all sampled rows once per K step, so a
+// larger BM divides that traffic over more tokens.
 template <typename T, int BM, int FNW, bool USE_DMA = true>
 struct SelCfg {
   static constexpr int NSC = 4 * FNW * 16;  // sampled rows per super-chunk
   static constexpr int FM = BM / 16;
-  static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && BM == 32 && FNW <= 4;
+  static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && (BM == 32 || BM == 128) && FNW <= 4;
+  static constexpr int IA = BM / 32;  // x rows loads per lane per stage (8 rows per wave each)
   static constexpr int PA = Plane<BM>::BYTES;
   static constexpr int PB = Plane<NSC>::BYTES;
   static constexpr int A_BYTES = DMA ? BM * 128 : KC * PA;
   static constexpr int B_BYTES = DMA ? NSC * 128 : KC * PB;
   static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES) <= 112 * 1024 ? 3 : 2;
-  static constexpr int DMA_L = 1 + NSC / 32;  // loads per lane per stage
+  static constexpr int DMA_L = IA + NSC / 32;  // loads per lane per stage
   static constexpr int STAGES = (DMA ? DMA_NS : 2) * (A_BYTES + B_BYTES);
   static constexpr int S_STRIDE = NSC + 1;  // odd float stride: conflict-free column walks
   static constexpr int S_BYTES = BM * S_STRIDE * 4;
@@ -115,8 +119,12 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
     const DmaSrc rwg = make_dma_src(wg, (uint32_t)d_ff * kbytes);
     const int w = wave_id();
     const int c_lane = (lane & 7) ^ (lane >> 3);
-    const int xr = w * 8 + (lane >> 3);
-    const uint32_t voffA = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
+    uint32_t voffA[C::IA];
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i) {
+      const int xr = (w * C::IA + i) * 8 + (lane >> 3);
+      voffA[i] = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
+    }
     constexpr int IB = C::NSC / 32;
     for (int n0 = 0; n0 < ncols; n0 += C::NSC) {
       uint32_t voffB[IB];
@@ -129,7 +137,9 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
       auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
         const uint32_t kb = (uint32_t)kt * 128;
         const bool kin = kb + c_lane * 16 < (uint32_t)kbytes;
-        dma16(rx, st + w * 1024, (kin && voffA != kOOB) ? voffA + kb : kOOB);
+#pragma unroll
+        for (int i = 0; i < C::IA; ++i)
+          dma16(rx, st + (w * C::IA + i) * 1024, (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
 #pragma unroll
         for (int i = 0; i < IB; ++i)
           dma16(rwg, st + C::A_BYTES + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
@@ -306,7 +316,7 @@ hipError_t launch_select_v(const void* x, const void* wg, int tokens, int d_mode
   using C = SelCfg<T, BM, FNW, USE_DMA>;
   const size_t smem = C::FIXED + (size_t)BM * (groups | 1) * 4 + (size_t)groups * 4;
   static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW, USE_DMA>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
   if (attr != hipSuccess) return attr;
   const int blocks = (tokens + BM - 1) / BM;
   LaunchTimer timer("select", stream);
@@ -316,6 +326,7 @@ hipError_t launch_select_v(const void* x, const void* wg, int tokens, int d_mode
 }
 
 // The direct-to-LDS path addresses x and w_gate through 32-bit buffer offsets.
+// (the register-staged fallback keeps BM = 32)
 template <typename T, int BM, int FNW>
 hipError_t launch_select_t(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
                            const int32_t* sub, int rpg, const float* bias, int32_t* idx, int32_t* counts,
@@ -324,8 +335,8 @@ hipError_t launch_select_t(const void* x, const void* wg, int tokens, int d_mode
   if ((unsigned long long)tokens * kb < (1ull << 31) && (unsigned long long)d_ff * kb < (1ull << 31))
     return launch_select_v<T, BM, FNW, true>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts,
                                              stream);
-  return launch_select_v<T, BM, FNW, false>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts,
-                                            stream);
+  return launch_select_v<T, (BM < 32 ? BM : 32), FNW, false>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg,
+                                                             bias, idx, counts, stream);
 }
 
 // Fragments per wave: the choice with the least padded MFMA work (ties: wider).
@@ -353,9 +364,16 @@ hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int 
     // direct-to-LDS: up to 256 sampled rows in one super-chunk of 4 fragments
     // per wave; beyond, super-chunks of 128 rows, whose small stages let two
     // workgroups share a CU (more waves issuing loads; measured faster than
-    // fewer, wider super-chunks)
+    // fewer, wider super-chunks).  From 128 tokens per CU on, 128-token
+    // workgroups (if their LDS fits): each workgroup streams all sampled rows
+    // once per K step, and the larger block divides that over more tokens
+    // (measured faster there; at 64 tokens per CU slower, since a CU then
+    // holds one workgroup instead of two)
     if (groups * rpg > 128 && groups * rpg <= 256)
       return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+    if (tokens >= 128 * compute_units() &&
+        SelCfg<T, 128, 2>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
+      return launch_select_t<T, 128, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
     return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
   }
   switch (pick_fnw(groups * rpg)) {

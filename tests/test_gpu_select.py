@@ -37,6 +37,10 @@ CASES = [
     ("k_equals_g", 100, 64, 128, 16, 8, "bf16", None, False, None),
     ("d16", 130, 16, 256, 16, 4, "bf16", 16, False, None),
     ("f32_subsample", 513, 256, 2048, 128, 5, "f32", 16, True, None),
+    # 128-token workgroups (chosen from 128 tokens per CU up)
+    ("rows256_t16384", 16384, 256, 2048, 64, 6, "bf16", 8, True, None),
+    ("bm128_g24_ragged", 32900, 128, 1536, 64, 5, "bf16", 4, True, None),
+    ("bm128_g100", 32768, 64, 1600, 16, 4, "bf16", 1, True, None),
 ]
 
 
