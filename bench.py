@@ -530,6 +530,9 @@ def main():
     CNT = torch.empty(G, dtype=torch.int32, device=dev)
     Y = torch.empty_like(X)
     GRADS = (torch.empty_like(X), torch.empty_like(WG), torch.empty_like(WU), torch.empty_like(WD))
+    # the selection's energy table (used by batches too small to fill the CUs)
+    SELWS = torch.empty(max(16, E.select_workspace_size(w.tokens, w.d_ff, w.group_size)), dtype=torch.uint8,
+                        device=dev)
     ws = {}
     saved = [None]
 
@@ -538,7 +541,8 @@ def main():
             if w.dense:
                 E.sparse_swiglu_fwd(X, WG, WU, WD, None, w.group_size, workspace=ws, out=Y, for_backward=False)
                 return
-            E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, out=IDX)
+            E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, out=IDX,
+                                  workspace=SELWS)
             E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, for_backward=False)
             return
         if w.dense:   # every group active: no selection, fused dense forward, recompute backward
@@ -547,7 +551,7 @@ def main():
             E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
             return
         E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, return_counts=True,
-                              out=IDX, counts_out=CNT)
+                              out=IDX, counts_out=CNT, workspace=SELWS)
         _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, saved=saved[0])
         saved[0] = ctx.saved
         E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
@@ -583,7 +587,7 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # Per-kernel durations: the same steps launched eagerly, each kernel bracketed by HIP events on its stream.
-    kernels = ["select", "fill", "bucket_single", "bucket_count", "bucket_scan", "bucket_scatter", "fwd_grouped",
+    kernels = ["select", "select_rank", "fill", "bucket_single", "bucket_count", "bucket_scan", "bucket_scatter", "fwd_grouped",
                "rowsum", "bwd_dh_dx", "bwd_dw", "bias_update", "dense_fwd", "dense_route", "dense_rec", "dense_dx",
                "dense_dw"]
     timing = not args.no_kernel_timing

@@ -24,7 +24,8 @@ import torch
 
 __all__ = [
     "ESG_F32", "ESG_BF16", "EsgError", "lib", "library_path", "make_subsample_index", "grouped_topk_select",
-    "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn", "update_load_balance_bias",
+    "select_workspace_size", "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn",
+    "update_load_balance_bias",
     "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
     "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
     "leaky_mlp_workspace_size", "leaky_mlp_fwd", "leaky_mlp_bwd", "leaky_mlp_saved_views",
@@ -49,6 +50,9 @@ _SIGNATURES = {
     "esg_make_subsample_index": (_c_int, [_c_int, _c_int, _c_int, ctypes.c_uint64, _c_vp]),
     "esg_grouped_topk_select": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp,
                                          _c_int, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "esg_grouped_topk_select_workspace_size": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
+    "esg_grouped_topk_select_ws": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp,
+                                            _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "esg_bucket_workspace_size": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size)]),
     "esg_bucket_by_group": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
                                      _c_vp]),
@@ -146,10 +150,22 @@ def make_subsample_index(d_ff: int, group_size: int, samples_per_group: int, see
     return out[:groups * samples_per_group], samples_per_group
 
 
+def select_workspace_size(tokens: int, d_ff: int, group_size: int) -> int:
+    """Bytes of the energy table esg_grouped_topk_select_ws can use."""
+    need = _c_size()
+    _check(lib().esg_grouped_topk_select_workspace_size(tokens, d_ff, group_size, ctypes.byref(need)),
+           "grouped_topk_select_workspace_size")
+    return need.value
+
+
 def grouped_topk_select(x, w_gate, group_size: int, num_active_groups: int, subsample_idx=None,
                         samples_per_group: Optional[int] = None, load_balance_bias=None, return_counts=False,
-                        out=None, counts_out=None):
-    """Per-token top-k groups by energy -> int32 [T, k] (and int32 counts [G])."""
+                        out=None, counts_out=None, workspace=None):
+    """Per-token top-k groups by energy -> int32 [T, k] (and int32 counts [G]).
+
+    workspace: None allocates the energy table for batches of fewer 32-token
+    blocks than the device has CUs (the selection is the same either way);
+    False never uses one; a uint8 device tensor is passed as given."""
     T, d = x.shape
     F = w_gate.shape[0]
     G = F // group_size
@@ -161,10 +177,17 @@ def grouped_topk_select(x, w_gate, group_size: int, num_active_groups: int, subs
     if return_counts:
         counts = counts_out if counts_out is not None else torch.empty(G, dtype=torch.int32, device=x.device)
     spg = samples_per_group if samples_per_group is not None else 0
-    _check(lib().esg_grouped_topk_select(
+    if workspace is None:
+        cus = torch.cuda.get_device_properties(x.device).multi_processor_count
+        workspace = False
+        if 0 < (T + 31) // 32 < cus:
+            workspace = torch.empty(select_workspace_size(T, F, group_size), dtype=torch.uint8, device=x.device)
+    ws = workspace if workspace is not False else None
+    _check(lib().esg_grouped_topk_select_ws(
         _dev(x, "x"), _dev(w_gate, "w_gate"), code, T, d, F, group_size, num_active_groups,
         _dev(subsample_idx, "subsample_idx", torch.int32), spg, _dev(load_balance_bias, "bias", torch.float32),
-        _dev(idx, "idx"), _dev(counts, "counts"), _stream(x.device)), "grouped_topk_select")
+        _dev(idx, "idx"), _dev(counts, "counts"), _dev(ws, "workspace"), 0 if ws is None else ws.numel(),
+        _stream(x.device)), "grouped_topk_select")
     return (idx, counts) if return_counts else idx
 
 

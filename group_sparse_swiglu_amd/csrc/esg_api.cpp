@@ -168,20 +168,38 @@ int esg_make_subsample_index(int d_ff, int group_size, int samples_per_group, ui
   return ESG_OK;
 }
 
-int esg_grouped_topk_select(const void* x, const void* w_gate, int dtype, int tokens, int d_model, int d_ff,
-                            int group_size, int k, const int32_t* sub, int samples_per_group, const float* bias,
-                            int32_t* idx_out, int32_t* counts_out, void* stream) {
+int esg_grouped_topk_select_ws(const void* x, const void* w_gate, int dtype, int tokens, int d_model, int d_ff,
+                               int group_size, int k, const int32_t* sub, int samples_per_group, const float* bias,
+                               int32_t* idx_out, int32_t* counts_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   int st = check_shape(dtype, tokens, d_model, d_ff, group_size, k);
   if (st != ESG_OK) return st;
   if ((tokens > 0 && (x == nullptr || idx_out == nullptr)) || w_gate == nullptr) return ESG_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_gate)) return ESG_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(workspace)) return ESG_ERR_INVALID_ARG;
   int rpg = group_size;
   if (sub != nullptr) {
     if (samples_per_group < 1 || samples_per_group > group_size) return ESG_ERR_UNSUPPORTED;
     rpg = samples_per_group;
   }
-  return hip_status(launch_select(dtype, x, w_gate, tokens, d_model, d_ff / group_size, k, sub, rpg, group_size,
-                                  bias, idx_out, counts_out, (hipStream_t)stream));
+  const int groups = d_ff / group_size;
+  float* ews = workspace != nullptr && workspace_bytes >= select_energy_bytes(tokens, groups) ? (float*)workspace
+                                                                                             : nullptr;
+  return hip_status(launch_select(dtype, x, w_gate, tokens, d_model, groups, k, sub, rpg, group_size, bias,
+                                  idx_out, counts_out, ews, (hipStream_t)stream));
+}
+
+int esg_grouped_topk_select(const void* x, const void* w_gate, int dtype, int tokens, int d_model, int d_ff,
+                            int group_size, int k, const int32_t* sub, int samples_per_group, const float* bias,
+                            int32_t* idx_out, int32_t* counts_out, void* stream) {
+  return esg_grouped_topk_select_ws(x, w_gate, dtype, tokens, d_model, d_ff, group_size, k, sub, samples_per_group,
+                                    bias, idx_out, counts_out, nullptr, 0, stream);
+}
+
+int esg_grouped_topk_select_workspace_size(int tokens, int d_ff, int group_size, size_t* workspace_bytes) {
+  if (workspace_bytes == nullptr || tokens < 0 || d_ff <= 0 || group_size <= 0 || d_ff % group_size != 0)
+    return ESG_ERR_INVALID_ARG;
+  *workspace_bytes = select_energy_bytes(tokens, d_ff / group_size);
+  return ESG_OK;
 }
 
 int esg_bucket_workspace_size(int tokens, int k, int groups, size_t* scratch_bytes) {

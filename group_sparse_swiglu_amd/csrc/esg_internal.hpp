@@ -18,9 +18,14 @@ struct LaunchTimer {
 bool timing_enabled();
 
 // ---- selection -------------------------------------------------------------
+// energy_ws: NULL, or an fp32 [tokens, groups] table (select_energy_bytes) that
+// lets batches with fewer 32-token blocks than CUs split the groups over
+// workgroups (same result).
+size_t select_energy_bytes(int tokens, int groups);
 hipError_t launch_select(int dtype, const void* x, const void* w_gate, int tokens, int d_model,
                          int groups, int k, const int32_t* sub, int rows_per_group, int group_size,
-                         const float* bias, int32_t* idx_out, int32_t* counts_out, hipStream_t stream);
+                         const float* bias, int32_t* idx_out, int32_t* counts_out, float* energy_ws,
+                         hipStream_t stream);
 
 // ---- bucketing ---------------------------------------------------------------
 // Bucketing of (token, slot) pairs by group.  Tiles of `tile_rows` padded
@@ -44,10 +49,17 @@ hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int 
 struct FfnShape {
   int dtype, tokens, d_model, d_ff, group_size, k;
   int groups() const { return d_ff / group_size; }
-  // neurons per kernel block: 128 for bf16, 64 for fp32 (LDS capacity)
+  // neurons per kernel block: 128 for bf16, 64 for fp32 (LDS capacity); bf16
+  // launches of fewer than 128 tiles of 128 neurons (decode-sized batches) take
+  // 64-neuron blocks instead, which doubles their workgroups
   int gsb() const {
     const int cap = dtype == 0 ? 64 : 128;
-    return group_size < cap ? group_size : cap;
+    if (group_size < cap) return group_size;
+    if (dtype == 1) {
+      const long long tiles = ((long long)tokens * k + (long long)groups() * 127) / 128;
+      if (tiles * (group_size / 128) < 128) return 64;
+    }
+    return cap;
   }
   int nsub() const { return group_size / gsb(); }                    // sub-blocks per group
   int elem_bytes() const { return dtype == 0 ? 4 : 2; }

@@ -12,6 +12,7 @@
 // is selected when fewer than k beat it, and its output slot is its rank among
 // the selected ids (a ballot prefix).  Every token's result depends only on
 // its own row: batch invariant and bitwise reproducible.
+#include <algorithm>
 #include <type_traits>
 
 #include "esg_device.hpp"
@@ -79,136 +80,13 @@ __device__ __forceinline__ void select_energy(const f32x4 (&acc)[FM][FNW], float
   }
 }
 
-template <typename T, int BM, int FNW, bool USE_DMA>
-__global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, const T* __restrict__ wg,
-                                                     int tokens, int d_model, int d_ff, int groups, int k,
-                                                     const int32_t* __restrict__ sub, int rpg,
-                                                     const float* __restrict__ bias,
-                                                     int32_t* __restrict__ idx_out,
-                                                     int32_t* __restrict__ counts) {
-  using C = SelCfg<T, BM, FNW, USE_DMA>;
-  extern __shared__ __align__(16) char smem[];
-  auto la = [&](int i_) -> char* { return smem + i_ * C::A_BYTES; };
-  auto lb = [&](int i_) -> char* { return smem + 2 * C::A_BYTES + i_ * C::B_BYTES; };
-  float* S = (float*)smem;                     // aliases the stage buffers after each K loop
-  const int ES = groups | 1;                   // odd row stride of the energy table
-  float* E = (float*)(smem + C::FIXED);        // [BM][ES]
-  int* cnt = (int*)(E + BM * ES);              // [groups]
-
+// Top-k of the BM tokens whose scores are E[r * ES + g] (LDS), written to
+// idx_out in ascending group id; per-group counts through the LDS table cnt
+// (zeroed by the caller) when counts is given.  256 threads.
+template <int BM>
+__device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int t0, int tokens, int groups, int k,
+                                          int32_t* __restrict__ idx_out, int32_t* __restrict__ counts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * BM;
-  const int ncols = groups * rpg;
-  const int kbytes = d_model * (int)sizeof(T);
-  const int nk = (kbytes + KC * 16 - 1) / (KC * 16);
-
-  for (int i = tid; i < BM * ES; i += NT) {
-    const int g = i % ES;
-    E[i] = (bias != nullptr && g < groups) ? bias[g] : 0.0f;
-  }
-  for (int i = tid; i < groups; i += NT) cnt[i] = 0;
-
-  int arow[C::FM], brow[FNW];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) arow[i] = i * 16 + (lane & 15);
-#pragma unroll
-  for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + wave) * 16 + (lane & 15);
-
-  if constexpr (C::DMA) {
-    ESG_LDS char* st0 = (ESG_LDS char*)smem;
-    const DmaSrc rx = make_dma_src(x, (uint32_t)tokens * kbytes);
-    const DmaSrc rwg = make_dma_src(wg, (uint32_t)d_ff * kbytes);
-    const int w = wave_id();
-    const int c_lane = (lane & 7) ^ (lane >> 3);
-    uint32_t voffA[C::IA];
-#pragma unroll
-    for (int i = 0; i < C::IA; ++i) {
-      const int xr = (w * C::IA + i) * 8 + (lane >> 3);
-      voffA[i] = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
-    }
-    constexpr int IB = C::NSC / 32;
-    for (int n0 = 0; n0 < ncols; n0 += C::NSC) {
-      uint32_t voffB[IB];
-#pragma unroll
-      for (int i = 0; i < IB; ++i) {
-        const int col = n0 + (w * IB + i) * 8 + (lane >> 3);
-        const int row = col < ncols ? (sub ? sub[col] : col) : -1;
-        voffB[i] = row >= 0 ? (uint32_t)row * kbytes + c_lane * 16 : kOOB;
-      }
-      auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
-        const uint32_t kb = (uint32_t)kt * 128;
-        const bool kin = kb + c_lane * 16 < (uint32_t)kbytes;
-#pragma unroll
-        for (int i = 0; i < C::IA; ++i)
-          dma16(rx, st + (w * C::IA + i) * 1024, (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
-#pragma unroll
-        for (int i = 0; i < IB; ++i)
-          dma16(rwg, st + C::A_BYTES + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
-      };
-      f32x4 acc[C::FM][FNW];
-      zero_acc(acc);
-      auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int cc = kb * 4 + (lane >> 4);
-          uint4 a[C::FM], b[FNW];
-#pragma unroll
-          for (int i = 0; i < C::FM; ++i) a[i] = frag_krow(st, arow[i], cc);
-#pragma unroll
-          for (int j = 0; j < FNW; ++j) b[j] = frag_krow(st + C::A_BYTES, brow[j], cc);
-#pragma unroll
-          for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FNW; ++j) mma_bf16(acc[i][j], a[i], b[j]);
-        }
-      };
-      wait_lgkm0();
-      barrier();  // the previous super-chunk's S reads (S aliases the stages) are done
-      constexpr int SB = C::A_BYTES + C::B_BYTES;
-      tiles::kloop<C::DMA_NS, C::DMA_L, 0>((kbytes + 127) / 128, st0, st0 + SB, st0 + 2 * SB, issue, compute);
-      wait_lgkm0();
-      barrier();  // every wave is done with the stages before S overwrites them
-      select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
-    }
-  } else {
-  RowKLoader<BM, KC, NT> ldA;
-  ldA.init(tid, [&](int r) -> const char* {
-    const int t = t0 + r;
-    return t < tokens ? (const char*)(x + (size_t)t * d_model) : nullptr;
-  });
-  for (int n0 = 0; n0 < ncols; n0 += C::NSC) {
-    RowKLoader<C::NSC, KC, NT> ldB;
-    ldB.init(tid, [&](int r) -> const char* {
-      const int col = n0 + r;
-      if (col >= ncols) return nullptr;
-      const int row = sub ? sub[col] : col;  // without a subsample the columns are all gate rows
-      return (const char*)(wg + (size_t)row * d_model);
-    });
-    f32x4 acc[C::FM][FNW];
-    zero_acc(acc);
-    ldA.load(0, kbytes);
-    ldB.load(0, kbytes);
-    __syncthreads();  // previous super-chunk's S reads and the E init are done
-    ldA.store(la(0));
-    ldB.store(lb(0));
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) {
-        ldA.load((kt + 1) * KC * 16, kbytes);
-        ldB.load((kt + 1) * KC * 16, kbytes);
-      }
-      mma_lds<T, C::FM, FNW, KC, C::PA, C::PB>(acc, la(kt & 1), lb(kt & 1), arow, brow, lane);
-      if (kt + 1 < nk) {
-        ldA.store(la((kt + 1) & 1));
-        ldB.store(lb((kt + 1) & 1));
-      }
-      __syncthreads();
-    }
-    select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
-    // the next super-chunk's first __syncthreads orders these before S is reused
-  }
-  }
-  __syncthreads();
-
   // rank top-k: group g is selected when fewer than k groups beat it (higher
   // score, or equal score and lower id); its output slot is its rank among the
   // selected ids (a ballot prefix)
@@ -310,33 +188,206 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
 }
 
 template <typename T, int BM, int FNW, bool USE_DMA>
-hipError_t launch_select_v(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
-                           const int32_t* sub, int rpg, const float* bias, int32_t* idx, int32_t* counts,
-                           hipStream_t stream) {
+__global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, const T* __restrict__ wg,
+                                                     int tokens, int d_model, int d_ff, int groups, int k,
+                                                     const int32_t* __restrict__ sub, int rpg,
+                                                     const float* __restrict__ bias,
+                                                     int32_t* __restrict__ idx_out,
+                                                     int32_t* __restrict__ counts, int gpc,
+                                                     float* __restrict__ e_out) {
   using C = SelCfg<T, BM, FNW, USE_DMA>;
-  const size_t smem = C::FIXED + (size_t)BM * (groups | 1) * 4 + (size_t)groups * 4;
+  extern __shared__ __align__(16) char smem[];
+  auto la = [&](int i_) -> char* { return smem + i_ * C::A_BYTES; };
+  auto lb = [&](int i_) -> char* { return smem + 2 * C::A_BYTES + i_ * C::B_BYTES; };
+  float* S = (float*)smem;                     // aliases the stage buffers after each K loop
+  const int ES = groups | 1;                   // odd row stride of the energy table
+  float* E = (float*)(smem + C::FIXED);        // [BM][ES]
+  int* cnt = (int*)(E + BM * ES);              // [groups]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * BM;
+  // this workgroup's groups [g_begin, g_end) and sampled columns [c_begin, ncols)
+  const int g_begin = blockIdx.y * gpc, g_end = min(groups, g_begin + gpc);
+  const int c_begin = g_begin * rpg, ncols = g_end * rpg;
+  const int kbytes = d_model * (int)sizeof(T);
+  const int nk = (kbytes + KC * 16 - 1) / (KC * 16);
+
+  for (int i = tid; i < BM * ES; i += NT) {
+    const int g = i % ES;
+    E[i] = (bias != nullptr && g < groups) ? bias[g] : 0.0f;
+  }
+  for (int i = tid; i < groups; i += NT) cnt[i] = 0;
+
+  int arow[C::FM], brow[FNW];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) arow[i] = i * 16 + (lane & 15);
+#pragma unroll
+  for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + wave) * 16 + (lane & 15);
+
+  if constexpr (C::DMA) {
+    ESG_LDS char* st0 = (ESG_LDS char*)smem;
+    const DmaSrc rx = make_dma_src(x, (uint32_t)tokens * kbytes);
+    const DmaSrc rwg = make_dma_src(wg, (uint32_t)d_ff * kbytes);
+    const int w = wave_id();
+    const int c_lane = (lane & 7) ^ (lane >> 3);
+    uint32_t voffA[C::IA];
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i) {
+      const int xr = (w * C::IA + i) * 8 + (lane >> 3);
+      voffA[i] = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
+    }
+    constexpr int IB = C::NSC / 32;
+    for (int n0 = c_begin; n0 < ncols; n0 += C::NSC) {
+      uint32_t voffB[IB];
+#pragma unroll
+      for (int i = 0; i < IB; ++i) {
+        const int col = n0 + (w * IB + i) * 8 + (lane >> 3);
+        const int row = col < ncols ? (sub ? sub[col] : col) : -1;
+        voffB[i] = row >= 0 ? (uint32_t)row * kbytes + c_lane * 16 : kOOB;
+      }
+      auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
+        const uint32_t kb = (uint32_t)kt * 128;
+        const bool kin = kb + c_lane * 16 < (uint32_t)kbytes;
+#pragma unroll
+        for (int i = 0; i < C::IA; ++i)
+          dma16(rx, st + (w * C::IA + i) * 1024, (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+          dma16(rwg, st + C::A_BYTES + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
+      };
+      f32x4 acc[C::FM][FNW];
+      zero_acc(acc);
+      auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int cc = kb * 4 + (lane >> 4);
+          uint4 a[C::FM], b[FNW];
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i) a[i] = frag_krow(st, arow[i], cc);
+#pragma unroll
+          for (int j = 0; j < FNW; ++j) b[j] = frag_krow(st + C::A_BYTES, brow[j], cc);
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FNW; ++j) mma_bf16(acc[i][j], a[i], b[j]);
+        }
+      };
+      wait_lgkm0();
+      barrier();  // the previous super-chunk's S reads (S aliases the stages) are done
+      constexpr int SB = C::A_BYTES + C::B_BYTES;
+      tiles::kloop<C::DMA_NS, C::DMA_L, 0>((kbytes + 127) / 128, st0, st0 + SB, st0 + 2 * SB, issue, compute);
+      wait_lgkm0();
+      barrier();  // every wave is done with the stages before S overwrites them
+      select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
+    }
+  } else {
+  RowKLoader<BM, KC, NT> ldA;
+  ldA.init(tid, [&](int r) -> const char* {
+    const int t = t0 + r;
+    return t < tokens ? (const char*)(x + (size_t)t * d_model) : nullptr;
+  });
+  for (int n0 = c_begin; n0 < ncols; n0 += C::NSC) {
+    RowKLoader<C::NSC, KC, NT> ldB;
+    ldB.init(tid, [&](int r) -> const char* {
+      const int col = n0 + r;
+      if (col >= ncols) return nullptr;
+      const int row = sub ? sub[col] : col;  // without a subsample the columns are all gate rows
+      return (const char*)(wg + (size_t)row * d_model);
+    });
+    f32x4 acc[C::FM][FNW];
+    zero_acc(acc);
+    ldA.load(0, kbytes);
+    ldB.load(0, kbytes);
+    __syncthreads();  // previous super-chunk's S reads and the E init are done
+    ldA.store(la(0));
+    ldB.store(lb(0));
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) {
+        ldA.load((kt + 1) * KC * 16, kbytes);
+        ldB.load((kt + 1) * KC * 16, kbytes);
+      }
+      mma_lds<T, C::FM, FNW, KC, C::PA, C::PB>(acc, la(kt & 1), lb(kt & 1), arow, brow, lane);
+      if (kt + 1 < nk) {
+        ldA.store(la((kt + 1) & 1));
+        ldB.store(lb((kt + 1) & 1));
+      }
+      __syncthreads();
+    }
+    select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
+    // the next super-chunk's first __syncthreads orders these before S is reused
+  }
+  }
+  __syncthreads();
+
+  // energies only: the ranking runs in select_rank_kernel over the whole table
+  if (e_out != nullptr) {
+    for (int p = tid; p < BM * (g_end - g_begin); p += NT) {
+      const int r = p / (g_end - g_begin), g = g_begin + p % (g_end - g_begin);
+      if (t0 + r < tokens) e_out[(size_t)(t0 + r) * groups + g] = E[r * ES + g];
+    }
+    return;
+  }
+  rank_topk<BM>(E, ES, cnt, t0, tokens, groups, k, idx_out, counts);
+}
+
+// Top-k from an energy table e_in [tokens, groups] (bias included) written by
+// energy-only launches of select_kernel: BM tokens per workgroup.
+template <int BM>
+__global__ __launch_bounds__(NT) void select_rank_kernel(const float* __restrict__ e_in, int tokens, int groups,
+                                                          int k, int32_t* __restrict__ idx_out,
+                                                          int32_t* __restrict__ counts) {
+  extern __shared__ __align__(16) char smem[];
+  const int ES = groups | 1;
+  float* E = (float*)smem;        // [BM][ES]
+  int* cnt = (int*)(E + BM * ES);  // [groups]
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * BM;
+  for (int i = tid; i < groups; i += NT) cnt[i] = 0;
+  for (int p = tid; p < BM * groups; p += NT) {
+    const int r = p / groups, g = p % groups;
+    E[r * ES + g] = t0 + r < tokens ? e_in[(size_t)(t0 + r) * groups + g] : 0.0f;
+  }
+  __syncthreads();
+  rank_topk<BM>(E, ES, cnt, t0, tokens, groups, k, idx_out, counts);
+}
+
+struct SelArgs {
+  const void* x;
+  const void* wg;
+  int tokens, d_model, d_ff, groups, k;
+  const int32_t* sub;
+  int rpg;
+  const float* bias;
+  int32_t* idx;
+  int32_t* counts;
+};
+
+// gpc groups per workgroup along y; e_out != NULL: energies only (no ranking).
+template <typename T, int BM, int FNW, bool USE_DMA>
+hipError_t launch_select_v(const SelArgs& a, int gpc, float* e_out, hipStream_t stream) {
+  using C = SelCfg<T, BM, FNW, USE_DMA>;
+  const size_t smem = C::FIXED + (size_t)BM * (a.groups | 1) * 4 + (size_t)a.groups * 4;
   static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW, USE_DMA>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
   if (attr != hipSuccess) return attr;
-  const int blocks = (tokens + BM - 1) / BM;
+  const dim3 grid((a.tokens + BM - 1) / BM, (a.groups + gpc - 1) / gpc);
   LaunchTimer timer("select", stream);
-  hipLaunchKernelGGL((select_kernel<T, BM, FNW, USE_DMA>), dim3(blocks), dim3(NT), smem, stream, (const T*)x,
-                     (const T*)wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts);
+  hipLaunchKernelGGL((select_kernel<T, BM, FNW, USE_DMA>), grid, dim3(NT), smem, stream, (const T*)a.x,
+                     (const T*)a.wg, a.tokens, a.d_model, a.d_ff, a.groups, a.k, a.sub, a.rpg, a.bias,
+                     e_out ? nullptr : a.idx, e_out ? nullptr : a.counts, gpc, e_out);
   return hipGetLastError();
 }
 
 // The direct-to-LDS path addresses x and w_gate through 32-bit buffer offsets.
 // (the register-staged fallback keeps BM = 32)
 template <typename T, int BM, int FNW>
-hipError_t launch_select_t(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
-                           const int32_t* sub, int rpg, const float* bias, int32_t* idx, int32_t* counts,
-                           hipStream_t stream) {
-  const unsigned long long kb = (unsigned long long)d_model * sizeof(T);
-  if ((unsigned long long)tokens * kb < (1ull << 31) && (unsigned long long)d_ff * kb < (1ull << 31))
-    return launch_select_v<T, BM, FNW, true>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts,
-                                             stream);
-  return launch_select_v<T, (BM < 32 ? BM : 32), FNW, false>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg,
-                                                             bias, idx, counts, stream);
+hipError_t launch_select_t(const SelArgs& a, hipStream_t stream, int gpc = 0, float* e_out = nullptr) {
+  if (gpc <= 0) gpc = a.groups;
+  const unsigned long long kb = (unsigned long long)a.d_model * sizeof(T);
+  if ((unsigned long long)a.tokens * kb < (1ull << 31) && (unsigned long long)a.d_ff * kb < (1ull << 31))
+    return launch_select_v<T, BM, FNW, true>(a, gpc, e_out, stream);
+  return launch_select_v<T, (BM < 32 ? BM : 32), FNW, false>(a, gpc, e_out, stream);
 }
 
 // Fragments per wave: the choice with the least padded MFMA work (ties: wider).
@@ -354,12 +405,42 @@ int pick_fnw(int ncols) {
   return best;
 }
 
+// Batches of fewer 32-token blocks than CUs, given an energy table: the groups
+// are split over workgroups (about two per CU), each writing its groups'
+// energies, and a second launch ranks.  Every sampled column's dot product and
+// every group's sum run in the same order as in the one-launch path, so the
+// selection is bitwise the same.
 template <typename T>
-hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int d_ff, int groups, int k,
-                    const int32_t* sub,
-                    int rpg, const float* bias, int32_t* idx, int32_t* counts, hipStream_t st) {
-  if (groups > 256)
-    return launch_select_t<T, 16, 8>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+hipError_t select_split(const SelArgs& a, float* ews, hipStream_t st) {
+  const int blocks = (a.tokens + 31) / 32;
+  const int want = std::max(1, (2 * compute_units() + blocks - 1) / blocks);
+  const int chunks0 = std::min(a.groups, want);
+  const int gpc = (a.groups + chunks0 - 1) / chunks0;
+  const int cols = gpc * a.rpg;  // sampled columns per workgroup
+  hipError_t e;
+  if (std::is_same<T, bf16_t>::value)
+    e = cols > 128 && cols <= 256 ? launch_select_t<T, 32, 4>(a, st, gpc, ews)
+                                  : launch_select_t<T, 32, 2>(a, st, gpc, ews);
+  else
+    switch (pick_fnw(cols)) {
+      case 2: e = launch_select_t<T, 32, 2>(a, st, gpc, ews); break;
+      case 4: e = launch_select_t<T, 32, 4>(a, st, gpc, ews); break;
+      case 6: e = launch_select_t<T, 32, 6>(a, st, gpc, ews); break;
+      default: e = launch_select_t<T, 32, 8>(a, st, gpc, ews); break;
+    }
+  if (e != hipSuccess) return e;
+  LaunchTimer timer("select_rank", st);
+  const size_t smem = (size_t)32 * (a.groups | 1) * 4 + (size_t)a.groups * 4;
+  hipLaunchKernelGGL(select_rank_kernel<32>, dim3(blocks), dim3(NT), smem, st, (const float*)ews, a.tokens,
+                     a.groups, a.k, a.idx, a.counts);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
+  const int groups = a.groups, rpg = a.rpg;
+  if (groups > 256) return launch_select_t<T, 16, 8>(a, st);
+  if (ews != nullptr && (a.tokens + 31) / 32 < compute_units()) return select_split<T>(a, ews, st);
   if (std::is_same<T, bf16_t>::value) {
     // direct-to-LDS: up to 256 sampled rows in one super-chunk of 4 fragments
     // per wave; beyond, super-chunks of 128 rows, whose small stages let two
@@ -369,36 +450,36 @@ hipError_t select_d(const void* x, const void* wg, int tokens, int d_model, int 
     // once per K step, and the larger block divides that over more tokens
     // (measured faster there; at 64 tokens per CU slower, since a CU then
     // holds one workgroup instead of two)
-    if (groups * rpg > 128 && groups * rpg <= 256)
-      return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
-    if (tokens >= 128 * compute_units() &&
+    if (groups * rpg > 128 && groups * rpg <= 256) return launch_select_t<T, 32, 4>(a, st);
+    if (a.tokens >= 128 * compute_units() &&
         SelCfg<T, 128, 2>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
-      return launch_select_t<T, 128, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
-    return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+      return launch_select_t<T, 128, 2>(a, st);
+    return launch_select_t<T, 32, 2>(a, st);
   }
   switch (pick_fnw(groups * rpg)) {
-    case 2: return launch_select_t<T, 32, 2>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
-    case 4: return launch_select_t<T, 32, 4>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
-    case 6: return launch_select_t<T, 32, 6>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
-    default: return launch_select_t<T, 32, 8>(x, wg, tokens, d_model, d_ff, groups, k, sub, rpg, bias, idx, counts, st);
+    case 2: return launch_select_t<T, 32, 2>(a, st);
+    case 4: return launch_select_t<T, 32, 4>(a, st);
+    case 6: return launch_select_t<T, 32, 6>(a, st);
+    default: return launch_select_t<T, 32, 8>(a, st);
   }
 }
 
 }  // namespace
 
+size_t select_energy_bytes(int tokens, int groups) { return (size_t)tokens * groups * sizeof(float); }
+
 hipError_t launch_select(int dtype, const void* x, const void* w_gate, int tokens, int d_model,
                          int groups, int k, const int32_t* sub, int rows_per_group, int group_size,
-                         const float* bias, int32_t* idx_out, int32_t* counts_out, hipStream_t stream) {
+                         const float* bias, int32_t* idx_out, int32_t* counts_out, float* energy_ws,
+                         hipStream_t stream) {
   if (counts_out) {
     hipError_t e = launch_fill_i32(counts_out, 0, (size_t)groups, stream);
     if (e != hipSuccess) return e;
   }
   if (tokens == 0) return hipSuccess;
-  const int d_ff = groups * group_size;
-  return dtype == 0 ? select_d<float>(x, w_gate, tokens, d_model, d_ff, groups, k, sub, rows_per_group, bias,
-                                      idx_out, counts_out, stream)
-                    : select_d<bf16_t>(x, w_gate, tokens, d_model, d_ff, groups, k, sub, rows_per_group, bias,
-                                       idx_out, counts_out, stream);
+  const SelArgs a{x, w_gate, tokens, d_model, groups * group_size, groups, k, sub, rows_per_group, bias, idx_out,
+                  counts_out};
+  return dtype == 0 ? select_d<float>(a, energy_ws, stream) : select_d<bf16_t>(a, energy_ws, stream);
 }
 
 }  // namespace esg

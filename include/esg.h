@@ -101,6 +101,24 @@ int esg_grouped_topk_select(const void* x, const void* w_gate, int dtype, int to
                             const float* bias, int32_t* idx_out, int32_t* counts_out, void* stream);
 
 /*
+ * The same selection (same definition as above, bitwise the same idx_out and
+ * counts_out) with a device workspace of at least
+ * esg_grouped_topk_select_workspace_size() bytes (16-byte aligned; the
+ * library's use of it ends with the call's work on `stream`).  Batches too
+ * small to give every CU a 32-token workgroup then spread each token block's
+ * groups over several workgroups, which write an fp32 [tokens, G] energy
+ * table there, and rank in a second launch (decode-sized batches).  A NULL or
+ * too small workspace selects exactly as esg_grouped_topk_select.
+ * Errors as esg_grouped_topk_select; ESG_ERR_INVALID_ARG for a misaligned
+ * workspace.
+ */
+int esg_grouped_topk_select_workspace_size(int tokens, int d_ff, int group_size, size_t* workspace_bytes);
+int esg_grouped_topk_select_ws(const void* x, const void* w_gate, int dtype, int tokens, int d_model,
+                               int d_ff, int group_size, int k, const int32_t* sub, int samples_per_group,
+                               const float* bias, int32_t* idx_out, int32_t* counts_out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Deterministic CSR bucketing of routed (token, slot) pairs by group (the
  * eugen_sparse README, "Pitfalls and limitations", states that the CSR
  * bucketing is deterministic).  Pairs are ordered by (group, token):

@@ -84,6 +84,18 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.esg_grouped_topk_select(8, 32, 1, 16, 64, 128, 32, 2, None, 0, None, 64, None, None) == 1
     assert lib.esg_grouped_topk_select(32, 32, 1, 16, 64, 128, 32, 5, None, 0, None, 64, None, None) == 2
     assert lib.esg_grouped_topk_select(32, 32, 1, 16, 64, 128, 32, 2, 64, 40, None, 64, None, None) == 2
+    # the workspace variant: same checks, plus a misaligned workspace
+    assert lib.esg_grouped_topk_select_ws(None, None, 1, 16, 64, 128, 32, 2, None, 0, None, None, None, None, 0,
+                                          None) == 1
+    assert lib.esg_grouped_topk_select_ws(32, 32, 1, 16, 64, 128, 32, 2, None, 0, None, 64, None, 8, 4096,
+                                          None) == 1
+    assert lib.esg_grouped_topk_select_ws(32, 32, 1, 16, 64, 128, 32, 5, None, 0, None, 64, None, 64, 4096,
+                                          None) == 2
+    need = ctypes.c_size_t()
+    assert lib.esg_grouped_topk_select_workspace_size(64, 5504, 128, ctypes.byref(need)) == 0
+    assert need.value == 64 * 43 * 4                      # an fp32 [tokens, G] energy table
+    assert lib.esg_grouped_topk_select_workspace_size(64, 5504, 100, ctypes.byref(need)) == 1
+    assert E.select_workspace_size(0, 2048, 64) == 0
     assert lib.esg_sparse_swiglu_fwd(32, 32, 32, 32, 1, 16, 64, 128, 32, 2, 64, 64, 64, 0, 64, 0, None, None) == 3
     assert lib.esg_sparse_swiglu_fwd(32, None, 32, 32, 1, 16, 64, 128, 32, 2, 64, 64, 64, 1 << 30, 64, 1 << 30,
                                      None, None) == 1

@@ -98,3 +98,36 @@ def test_select_skewed_bias():
     oidx, scores = _oracle(inp, 8)
     check_selection(idx.cpu().numpy(), oidx, scores, 8)
     assert counts[:4].cpu().tolist() == [4096] * 4
+
+
+SPLIT_CASES = [
+    # name, T, d, F, gs, k, dtype, spg, bias: batches with fewer 32-token blocks than CUs
+    ("decode64_1p3b", 64, 2048, 5504, 128, 11, "bf16", 16, True),
+    ("prefill4096_1p3b", 4096, 2048, 5504, 128, 11, "bf16", 16, True),
+    ("t1000_128m", 1000, 768, 2048, 64, 8, "bf16", 8, True),
+    ("one_token", 1, 64, 256, 16, 3, "bf16", 4, True),
+    ("spg12_straddling", 333, 128, 1024, 32, 3, "bf16", 12, True),
+    ("g100_200rows", 200, 64, 1600, 16, 4, "bf16", 2, True),
+    ("g256", 300, 64, 4096, 16, 7, "bf16", 5, False),
+    ("f32_full_rows", 150, 96, 1024, 64, 4, "f32", None, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_select_workspace_split_is_bitwise_the_one_launch_selection(case):
+    """With the energy table the groups of a token block are spread over
+    workgroups; the result is bitwise that of the one-launch selection, and
+    both match the oracle."""
+    require_gpu()
+    name, T, d, F, gs, k, dtype, spg, bias = case
+    note(f"select split {name}")
+    inp = inputs(T, d, F, gs, dtype, seed=6, bias=bias, spg=spg)
+    ws = torch.empty(E.select_workspace_size(T, F, gs), dtype=torch.uint8, device="cuda")
+    a, ca = _select(inp, k, workspace=False)
+    b, cb = _select(inp, k, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ca, cb)
+    rows = None if T <= 1024 else np.sort(np.random.default_rng(3).choice(T, 512, replace=False))
+    oidx, scores = _oracle(inp, k, rows)
+    b_h = b.cpu().numpy()
+    check_selection(b_h if rows is None else b_h[rows], oidx, scores, k)
