@@ -105,6 +105,9 @@ EDGE = [
     ("d208_gs128", 150, 208, 512, 128, 2, "bf16"),
     ("d1040_gs64_k3", 700, 1040, 640, 64, 3, "bf16"),
     ("d400_gs128_k3", 333, 400, 1024, 128, 3, "bf16"),  # ragged 256-d weight-gradient block
+    # 128 groups: enough tiles (>= 128) for 128-neuron blocks; fewer tiles run 64-neuron blocks
+    ("gs128_blocks_d208", 300, 208, 16384, 128, 4, "bf16"),
+    ("gs128_blocks_d400_k3", 333, 400, 16384, 128, 3, "bf16"),
 ]
 
 
