@@ -265,15 +265,17 @@ __device__ __forceinline__ void issue_chunk(const DmaSrc& rk, const DmaSrc& ru, 
 }
 
 // DMA of a [64 tokens][128] bf16 head slice (Q or dO) into two K-row sub-tiles:
-// 16 instructions, 16/NW per wave.
-template <int NW = MB_NW>
+// 16 instructions, 16/NW per wave.  SWZ2: in the second swizzle (krow_swz2).
+template <int NW = MB_NW, bool SWZ2 = false>
 __device__ __forceinline__ void issue_tokens(const DmaSrc& src, ESG_LDS char* dst, int w, int lane, int t0,
                                              int tokens, uint32_t qrow, int h) {
-  const int c8 = (lane & 7) ^ (lane >> 3);
 #pragma unroll
   for (int i = 0; i < 16 / NW; ++i) {
     const int ii = w * (16 / NW) + i;
     const int sb = ii >> 3, row = (ii & 7) * 8 + (lane >> 3);
+    // position lane & 7 of the row takes chunk (lane & 7) ^ swizzle(row); row
+    // bit 3 is ii & 1
+    const int c8 = (lane & 7) ^ (lane >> 3) ^ (SWZ2 ? (ii & 1) * 5 : 0);
     const int t = t0 + row;
     dma16(src, dst + sb * MB_TSUB + (ii & 7) * 1024,
           t < tokens ? (uint32_t)t * qrow + (uint32_t)h * MH_DH * 2 + sb * 128 + c8 * 16 : kOOB);
@@ -506,8 +508,8 @@ __global__ __launch_bounds__(64 * MBW_NW, 1) void mhffn_bwd_dw_kernel(
   const int tok0 = tg * 16, tl = tok0 + (lane & 15);
   auto issue = [&](ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int t0 = s * MB_TM;
-    issue_tokens<MBW_NW>(rq, st, w, lane, t0, tokens, qrow, h);
-    issue_tokens<MBW_NW>(ro, st + 2 * MB_TSUB, w, lane, t0, tokens, qrow, h);
+    issue_tokens<MBW_NW, true>(rq, st, w, lane, t0, tokens, qrow, h);
+    issue_tokens<MBW_NW, true>(ro, st + 2 * MB_TSUB, w, lane, t0, tokens, qrow, h);
     // router weights of token group tg: lanes 0..15 of the waves of the first
     // neuron half, 4 bytes each (the other waves issue an empty load into the
     // sink, so that every wave counts the same loads)
@@ -542,8 +544,8 @@ __global__ __launch_bounds__(64 * MBW_NW, 1) void mhffn_bwd_dw_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int c = kb * 4 + (lane >> 4);
-        const uint4 bq = frag_krow(qs + sub * MB_TSUB, tl, c);
-        const uint4 bo = frag_krow(os + sub * MB_TSUB, tl, c);
+        const uint4 bq = frag_krow2(qs + sub * MB_TSUB, tl, c);
+        const uint4 bo = frag_krow2(os + sub * MB_TSUB, tl, c);
 #pragma unroll
         for (int f = 0; f < 6; ++f) mma_bf16(acc1[f], wf[sub][kb][f], f < 4 ? bq : bo);
       }
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(64 * MBW_NW, 1) void mhffn_bwd_dw_kernel(
     for (int p = 0; p < 2; ++p) {
       const ChunkGrads cg = chunk_grads<32>(acc1, p, rw);
       const int n = nh * 32 + p * 16 + (lane >> 4) * 4;
-      const int o = krow_off(tl, n >> 3) + (n & 7) * 2;
+      const int o = krow_off2(tl, n >> 3) + (n & 7) * 2;
       lds_write8(t_dh1 + o, cg.dh1[0], cg.dh1[1]);
       lds_write8(t_dh2 + o, cg.dh2[0], cg.dh2[1]);
       lds_write8(t_ra + o, cg.ra[0], cg.ra[1]);
@@ -565,15 +567,15 @@ __global__ __launch_bounds__(64 * MBW_NW, 1) void mhffn_bwd_dw_kernel(
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf) {
         const int j0 = tg * 32 + jf * 16;
-        aq[jf] = frag_krow_t(qs + (j0 >> 6) * MB_TSUB, kb, j0 & 63, lane);
-        ao[jf] = frag_krow_t(os + (j0 >> 6) * MB_TSUB, kb, j0 & 63, lane);
+        aq[jf] = frag_krow_t2(qs + (j0 >> 6) * MB_TSUB, kb, j0 & 63, lane);
+        ao[jf] = frag_krow_t2(os + (j0 >> 6) * MB_TSUB, kb, j0 & 63, lane);
       }
 #pragma unroll
       for (int nf = 0; nf < 2; ++nf) {
         const int c0 = nh * 32 + nf * 16;
-        b1[nf] = frag_krow_t(t_dh1, kb, c0, lane);
-        b2[nf] = frag_krow_t(t_dh2, kb, c0, lane);
-        br[nf] = frag_krow_t(t_ra, kb, c0, lane);
+        b1[nf] = frag_krow_t2(t_dh1, kb, c0, lane);
+        b2[nf] = frag_krow_t2(t_dh2, kb, c0, lane);
+        br[nf] = frag_krow_t2(t_ra, kb, c0, lane);
       }
 #pragma unroll
       for (int jf = 0; jf < 2; ++jf)

@@ -94,6 +94,22 @@ __device__ __forceinline__ uint4 frag_krow(const ESG_LDS char* t, int r, int c) 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A second K-row swizzle: chunk c of row r at position c ^ krow_swz2(r), XOR 5
+// in rows whose bit 3 is set.  A transposed read (frag_krow_t2) takes rows
+// q*8 + 0..3 (q = lane / 16), two adjacent chunks per row; with the plain
+// swizzle rows r and r + 8 hit the same banks (2-way conflicts when 32 lanes
+// are serviced together), and so do 16 rows read or written along a chunk by
+// 16 lanes.  With XOR 5 (bit 0: the 16-row case, bit 2: the chunk pairs of
+// the transposed read) a bank model of these accesses finds no conflict for
+// groups of 8, 16 or 32 lanes.
+__device__ __forceinline__ int krow_swz2(int r) { return (r & 7) ^ (((r >> 3) & 1) * 5); }
+__device__ __forceinline__ int krow_off2(int r, int c) { return r * 128 + ((c ^ krow_swz2(r)) << 4); }
+
+__device__ __forceinline__ uint4 frag_krow2(const ESG_LDS char* t, int r, int c) {
+  const u32x4_t v = *(const ESG_LDS u32x4_t*)(t + krow_off2(r, c));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 8-byte LDS write of four bf16 (two packed dwords).
 __device__ __forceinline__ void lds_write8(ESG_LDS char* p, uint32_t lo, uint32_t hi) {
   *(ESG_LDS u32x2_t*)p = (u32x2_t){lo, hi};
@@ -146,6 +162,18 @@ __device__ __forceinline__ uint4 frag_krow_t(const ESG_LDS char* t, int kb, int 
   const int c = colb >> 4, half = colb & 15;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + krow_off(row, c) + half));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + krow_off(row + 4, c) + half));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// frag_krow_t on a tile in the second swizzle (krow_off2).
+__device__ __forceinline__ uint4 frag_krow_t2(const ESG_LDS char* t, int kb, int m0, int lane) {
+  const int q = lane >> 4, i = lane & 15;
+  const int row = kb * 32 + q * 8 + (i >> 2);
+  const int colb = m0 * 2 + (i & 3) * 8;
+  const int c = colb >> 4, half = colb & 15;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + krow_off2(row, c) + half));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + krow_off2(row + 4, c) + half));
   const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   return make_uint4(a.x, a.y, b.x, b.y);
 }
