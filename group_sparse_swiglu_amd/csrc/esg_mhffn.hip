@@ -218,13 +218,15 @@ __global__ __launch_bounds__(MH_NT, 1) void mhffn_fwd_kernel(const bf16_t* __res
 // 64-column K-row sub-tiles):
 //   per token:   a = SiLU(h1) h2;  dR[t,e] = sum_n a g;  da = R g;
 //                dh2 = da SiLU(h1);  dh1 = da h2 SiLU'(h1)
-//   dQ/dR kernel (per head and 64 tokens; four wavefronts of 16 tokens;
-//                chunks of 32 neurons through a three-stage ring):
+//   dQ/dR kernel (per head and 128 tokens; eight wavefronts; chunks of 32
+//                neurons, with the router column of their sub-network,
+//                through a three-stage ring):
 //                dQ^T += [K; U]^T [dh1 dh2]^T, the stage's K and U rows read
 //                transposed (rows = neuron = the K index, columns = d_h),
-//                each wave a 32-wide d_h slice for all 64 tokens; dQ
-//                accumulates in registers, dR in LDS, both over all chunks
-//   dW kernel    (per head, sub-network and 48-neuron chunk held in LDS, all tokens in
+//                each wave a 16-wide d_h slice for all 128 tokens; dQ
+//                accumulates in registers over all chunks, each token's dR
+//                over its sub-network's chunks
+//   dW kernel    (per head, sub-network and 64-neuron chunk held in LDS, all tokens in
 //                steps of 64): dK^T += Q^T dh1, dU^T += Q^T dh2,
 //                dV^T += dO^T (R a), the Q / dO tiles and the per-step
 //                [token][neuron] tiles read transposed
@@ -264,20 +266,22 @@ __device__ __forceinline__ void issue_chunk(const DmaSrc& rk, const DmaSrc& ru, 
   }
 }
 
-// DMA of a [64 tokens][128] bf16 head slice (Q or dO) into two K-row sub-tiles:
-// 16 instructions, 16/NW per wave.  SWZ2: in the second swizzle (krow_swz2).
-template <int NW = MB_NW, bool SWZ2 = false>
+// DMA of a [TM tokens][128] bf16 head slice (Q or dO) into two K-row sub-tiles
+// of TM * 128 bytes: TM/4 instructions, TM/4/NW per wave.  SWZ2: in the second
+// swizzle (krow_swz2).
+template <int NW = MB_NW, bool SWZ2 = false, int TM = MB_TM>
 __device__ __forceinline__ void issue_tokens(const DmaSrc& src, ESG_LDS char* dst, int w, int lane, int t0,
                                              int tokens, uint32_t qrow, int h) {
+  constexpr int PER = TM / 8;  // instructions per sub-tile
 #pragma unroll
-  for (int i = 0; i < 16 / NW; ++i) {
-    const int ii = w * (16 / NW) + i;
-    const int sb = ii >> 3, row = (ii & 7) * 8 + (lane >> 3);
+  for (int i = 0; i < TM / 4 / NW; ++i) {
+    const int ii = w * (TM / 4 / NW) + i;
+    const int sb = ii / PER, row = (ii % PER) * 8 + (lane >> 3);
     // position lane & 7 of the row takes chunk (lane & 7) ^ swizzle(row); row
     // bit 3 is ii & 1
     const int c8 = (lane & 7) ^ (lane >> 3) ^ (SWZ2 ? (ii & 1) * 5 : 0);
     const int t = t0 + row;
-    dma16(src, dst + sb * MB_TSUB + (ii & 7) * 1024,
+    dma16(src, dst + sb * (TM * 128) + (ii % PER) * 1024,
           t < tokens ? (uint32_t)t * qrow + (uint32_t)h * MH_DH * 2 + sb * 128 + c8 * 16 : kOOB);
   }
 }
@@ -307,7 +311,7 @@ __device__ __forceinline__ void chunk_phase1(const ESG_LDS char* st, const ESG_L
 // Phase 1 of 16 of a chunk's neurons (fragment p of each of K, U, V) for the
 // 16 tokens [tok0, +16): acc = {h1, h2, g} of those neurons (the layout of a
 // 16-neuron chunk, so chunk_grads<16> applies).
-template <int NC>
+template <int NC, int TSUB = MB_TSUB>
 __device__ __forceinline__ void chunk_phase1_part(const ESG_LDS char* st, const ESG_LDS char* qt,
                                                   const ESG_LDS char* dot, int tok0, int p, int lane,
                                                   f32x4 (&acc)[3]) {
@@ -319,8 +323,8 @@ __device__ __forceinline__ void chunk_phase1_part(const ESG_LDS char* st, const 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int c = kb * 4 + (lane >> 4);
-      const uint4 bq = frag_krow(qt + sub * MB_TSUB, tok0 + (lane & 15), c);
-      const uint4 bo = frag_krow(dot + sub * MB_TSUB, tok0 + (lane & 15), c);
+      const uint4 bq = frag_krow(qt + sub * TSUB, tok0 + (lane & 15), c);
+      const uint4 bo = frag_krow(dot + sub * TSUB, tok0 + (lane & 15), c);
 #pragma unroll
       for (int m = 0; m < 3; ++m) {
         const uint4 a = frag_krow(st + sub * C::HALF, (m * F1 + p) * 16 + (lane & 15), c);
@@ -367,90 +371,118 @@ __device__ __forceinline__ ChunkGrads chunk_grads(const f32x4 (&acc)[Chunk<NC>::
 // resident; wider chunks mean fewer passes over the tokens)
 constexpr int MBQ_NC = 32, MBW_NC = 64;
 
-// Eight waves: for phase 1 wave w takes tokens [(w%4)*16, +16) and neurons
-// [(w/4)*16, +16) of the chunk (the two neuron halves' dR partials are added
-// in a fixed order through LDS); for phase 2 it takes d_h [w*16, +16) for all
-// 64 tokens.  Two waves per SIMD: one's epilogue overlaps the other's MFMAs.
+// Eight waves for the dQ/dR kernel.
 constexpr int MBQ_NW = 8;
+
+// dQ/dR over 128-token tiles (eight waves): phase 1 wave w takes tokens
+// [(w%4)*32, +32) (two 16-token fragments) and neurons [(w/4)*16, +16) of the
+// 32-neuron chunk; phase 2 d_h [w*16, +16) for all 128 tokens, so each
+// barrier pair carries twice the MFMA work of a 64-token tile and each chunk's
+// weights serve twice the tokens.  The router column of the chunk's
+// sub-network rides in the ring stage (a 4-byte DMA per token), and each
+// token's dR for the current sub-network accumulates in a register of its
+// writer lane (the same chunk order as a per-tile table), stored after the
+// sub-network's last chunk.
+constexpr int MBQ2_TM = 128, MBQ2_TSUB = MBQ2_TM * 128;
 __global__ __launch_bounds__(64 * MBQ_NW, 1) void mhffn_bwd_dq_kernel(
     const bf16_t* __restrict__ dout, const bf16_t* __restrict__ q, const float* __restrict__ r,
     const bf16_t* __restrict__ kw, const bf16_t* __restrict__ uw, const bf16_t* __restrict__ vw, int tokens,
     int heads, int subnets, int d_sub, bf16_t* __restrict__ dq, float* __restrict__ dr) {
-  constexpr int NTQ = 64 * MBQ_NW;
   using C = Chunk<MBQ_NC, MBQ_NW>;
-  static_assert(MBQ_NC == 32 && MBQ_NW == 8, "two neuron halves of 16 x four token groups");
-  __shared__ __attribute__((aligned(1024))) char ring_[3 * C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char qt_[2 * MB_TSUB];
-  __shared__ __attribute__((aligned(1024))) char dot_[2 * MB_TSUB];
-  __shared__ __attribute__((aligned(1024))) char dh_[MB_TSUB];  // [token][dh1 (32) | dh2 (32)]
-  __shared__ float rtab[MB_TM * MH_MAXE];
-  __shared__ float drtab[MB_TM * MH_MAXE];
-  __shared__ float drpart[2][MB_TM];  // the step's dR sums of each neuron half
+  static_assert(MBQ_NC == 32 && MBQ_NW == 8, "two neuron halves of 16 x four token groups of 32");
+  // chunk rows, the router column (128 x 4 B), a sink for the other waves' empty router loads
+  constexpr int R_OFF = C::STAGE, SINK_OFF = C::STAGE + 512, RSTAGE = C::STAGE + 1024;
+  constexpr int L = C::LW + 1;  // loads per lane per stage
+  __shared__ __attribute__((aligned(1024))) char ring_[3 * RSTAGE];
+  __shared__ __attribute__((aligned(1024))) char qt_[2 * MBQ2_TSUB];
+  __shared__ __attribute__((aligned(1024))) char dot_[2 * MBQ2_TSUB];
+  __shared__ __attribute__((aligned(1024))) char dh_[MBQ2_TSUB];  // [token][dh1 (32) | dh2 (32)]
+  __shared__ float drpart[2][MBQ2_TM];                            // the step's dR sums of each neuron half
   ESG_LDS char* ring = (ESG_LDS char*)ring_;
   ESG_LDS char* qt = (ESG_LDS char*)qt_;
   ESG_LDS char* dot = (ESG_LDS char*)dot_;
   ESG_LDS char* dh = (ESG_LDS char*)dh_;
 
-  const int h = blockIdx.y, t0 = blockIdx.x * MB_TM;
+  const int h = blockIdx.y, t0 = blockIdx.x * MBQ2_TM;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int nchunks = (d_sub + MBQ_NC - 1) / MBQ_NC;
   const uint32_t qrow = (uint32_t)heads * MH_DH * 2;
   const uint32_t wbytes_he = (uint32_t)d_sub * MH_DH * 2;
   const uint32_t wtotal = (uint32_t)heads * subnets * wbytes_he;
   const DmaSrc rk = make_dma_src(kw, wtotal), ru = make_dma_src(uw, wtotal), rv = make_dma_src(vw, wtotal);
+  const DmaSrc rr = make_dma_src(r, (uint32_t)tokens * heads * subnets * 4);
 
-  for (int i = threadIdx.x; i < MB_TM * subnets; i += NTQ) {
-    const int t = t0 + i / subnets;
-    rtab[i] = t < tokens ? r[((size_t)t * heads + h) * subnets + i % subnets] : 0.0f;
-    drtab[i] = 0.0f;
-  }
-  issue_tokens<MBQ_NW>(make_dma_src(q, (uint32_t)tokens * qrow), qt, w, lane, t0, tokens, qrow, h);
-  issue_tokens<MBQ_NW>(make_dma_src(dout, (uint32_t)tokens * qrow), dot, w, lane, t0, tokens, qrow, h);
+  issue_tokens<MBQ_NW, false, MBQ2_TM>(make_dma_src(q, (uint32_t)tokens * qrow), qt, w, lane, t0, tokens, qrow, h);
+  issue_tokens<MBQ_NW, false, MBQ2_TM>(make_dma_src(dout, (uint32_t)tokens * qrow), dot, w, lane, t0, tokens, qrow,
+                                       h);
 
-  const int nh = w >> 2;                                 // neuron half of phase 1
-  const int tok0 = (w & 3) * 16, tl = tok0 + (lane & 15);  // the wave's tokens; this lane's token
-  f32x4 acc1[3];
-  f32x4 acc2[4];  // dQ^T: d_h [w*16, +16) x the tile's 4 token fragments
+  const int nh = w >> 2;         // neuron half of phase 1
+  const int tg = (w & 3) * 32;   // the wave's 32 tokens (two fragments)
+  f32x4 acc1[2][3];
+  f32x4 acc2[8];  // dQ^T: d_h [w*16, +16) x the tile's 8 token fragments
   zero_acc(acc2);
+  float dracc[2] = {0.0f, 0.0f};  // writer lanes (nh == 0, lane < 16): tokens tg + i*16 + lane
   auto issue = [&](ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int e = s / nchunks, n0 = (s % nchunks) * MBQ_NC;
     issue_chunk<MBQ_NC, MBQ_NW>(rk, ru, rv, st, w, lane, (uint32_t)(h * subnets + e) * wbytes_he, n0, d_sub);
+    // router column of sub-network e: waves 0 and 1 load tokens [w*64, +64),
+    // the others an empty load into the sink (every wave counts L loads)
+    const int t = t0 + w * 64 + lane;
+    dma4(rr, st + (w < 2 ? R_OFF + w * 256 : SINK_OFF),
+         (w < 2 && t < tokens) ? ((uint32_t)t * heads + h) * subnets * 4 + e * 4 : kOOB);
   };
   auto compute = [&](const ESG_LDS char* st, int s) __attribute__((always_inline)) {
     const int e = s / nchunks;
-    chunk_phase1_part<MBQ_NC>(st, qt, dot, tok0, nh, lane, acc1);
-    const float rw = rtab[tl * subnets + e];
-    const ChunkGrads cg = chunk_grads<16>(acc1, 0, rw);
-    const int n = nh * 16 + (lane >> 4) * 4;  // dh1 column n, dh2 column 32 + n
-    lds_write8(dh + krow_off(tl, n >> 3) + (n & 7) * 2, cg.dh1[0], cg.dh1[1]);
-    const int n2 = MBQ_NC + n;
-    lds_write8(dh + krow_off(tl, n2 >> 3) + (n2 & 7) * 2, cg.dh2[0], cg.dh2[1]);
-    float drp = cg.dr;
-    drp += __shfl_xor(drp, 16);
-    drp += __shfl_xor(drp, 32);
-    if (lane < 16) drpart[nh][tl] = drp;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) chunk_phase1_part<MBQ_NC, MBQ2_TSUB>(st, qt, dot, tg + i * 16, nh, lane, acc1[i]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tl = tg + i * 16 + (lane & 15);
+      const float rw = *(const ESG_LDS float*)(st + R_OFF + tl * 4);
+      const ChunkGrads cg = chunk_grads<16>(acc1[i], 0, rw);
+      const int n = nh * 16 + (lane >> 4) * 4;  // dh1 column n, dh2 column 32 + n
+      lds_write8(dh + krow_off(tl, n >> 3) + (n & 7) * 2, cg.dh1[0], cg.dh1[1]);
+      const int n2 = MBQ_NC + n;
+      lds_write8(dh + krow_off(tl, n2 >> 3) + (n2 & 7) * 2, cg.dh2[0], cg.dh2[1]);
+      float drp = cg.dr;
+      drp += __shfl_xor(drp, 16);
+      drp += __shfl_xor(drp, 32);
+      if (lane < 16) drpart[nh][tl] = drp;
+    }
     wait_lgkm0();
     barrier();  // every wave's dh rows and dR halves are written
-    if (nh == 0 && lane < 16) drtab[tl * subnets + e] += drpart[0][tl] + drpart[1][tl];  // one writer per row
+    if (nh == 0 && lane < 16) {  // one writer per token
+      const bool last = s % nchunks == nchunks - 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int tl = tg + i * 16 + lane;
+        dracc[i] += drpart[0][tl] + drpart[1][tl];
+        if (last) {
+          const int t = t0 + tl;
+          if (t < tokens) dr[((size_t)t * heads + h) * subnets + e] = dracc[i];
+          dracc[i] = 0.0f;
+        }
+      }
+    }
     // dQ^T += [K; U]^T [dh1 dh2]^T  (K index = the 64 K and U neuron rows of the
-    // stage); wave w takes d_h [w*16, +16) for all 64 tokens
+    // stage); wave w takes d_h [w*16, +16) for all 128 tokens
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint4 a = frag_krow_t(st + (w >> 2) * C::HALF, kb, (w & 3) * 16, lane);
-      uint4 b[4];
+      uint4 b[8];
 #pragma unroll
-      for (int tf = 0; tf < 4; ++tf) b[tf] = frag_krow(dh, tf * 16 + (lane & 15), kb * 4 + (lane >> 4));
+      for (int tf = 0; tf < 8; ++tf) b[tf] = frag_krow(dh, tf * 16 + (lane & 15), kb * 4 + (lane >> 4));
 #pragma unroll
-      for (int tf = 0; tf < 4; ++tf) mma_bf16(acc2[tf], a, b[tf]);
+      for (int tf = 0; tf < 8; ++tf) mma_bf16(acc2[tf], a, b[tf]);
     }
   };
   // the Q and dO tiles' loads are older than the ring's: the first wait covers them
-  kloop<3, C::LW, 0>(subnets * nchunks, ring, ring + C::STAGE, ring + 2 * C::STAGE, issue, compute);
+  kloop<3, L, 0>(subnets * nchunks, ring, ring + RSTAGE, ring + 2 * RSTAGE, issue, compute);
   wait_lgkm0();
   barrier();
 
 #pragma unroll
-  for (int tf = 0; tf < 4; ++tf) {
+  for (int tf = 0; tf < 8; ++tf) {
     const int t = t0 + tf * 16 + (lane & 15);
     if (t < tokens) {
       const int j = w * 16 + (lane >> 4) * 4;
@@ -459,10 +491,6 @@ __global__ __launch_bounds__(64 * MBQ_NW, 1) void mhffn_bwd_dq_kernel(
       for (int x = 0; x < 4; ++x) v[x] = acc2[tf][x];
       Quad<bf16_t>::store(dq + ((size_t)t * heads + h) * MH_DH + j, v);
     }
-  }
-  for (int i = threadIdx.x; i < MB_TM * subnets; i += NTQ) {
-    const int tt = t0 + i / subnets;
-    if (tt < tokens) dr[((size_t)tt * heads + h) * subnets + i % subnets] = drtab[i];
   }
 }
 
@@ -624,9 +652,8 @@ hipError_t launch_mhffn_bwd(const void* dout, const void* q, const float* r, con
                             void* dk, void* du, void* dv, hipStream_t stream) {
   if (tokens > 0) {
     LaunchTimer timer("mhffn_bwd_dq", stream);
-    hipLaunchKernelGGL(mhffn_bwd_dq_kernel, dim3((tokens + MB_TM - 1) / MB_TM, heads), dim3(64 * MBQ_NW), 0,
-                       stream,
-                       (const bf16_t*)dout, (const bf16_t*)q, r, (const bf16_t*)k, (const bf16_t*)u,
+    hipLaunchKernelGGL(mhffn_bwd_dq_kernel, dim3((tokens + MBQ2_TM - 1) / MBQ2_TM, heads), dim3(64 * MBQ_NW), 0,
+                       stream, (const bf16_t*)dout, (const bf16_t*)q, r, (const bf16_t*)k, (const bf16_t*)u,
                        (const bf16_t*)v, tokens, heads, subnets, d_sub, (bf16_t*)dq, dr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
