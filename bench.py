@@ -587,9 +587,9 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # Per-kernel durations: the same steps launched eagerly, each kernel bracketed by HIP events on its stream.
-    kernels = ["select", "select_rank", "fill", "bucket_single", "bucket_count", "bucket_scan", "bucket_scatter", "fwd_grouped",
-               "rowsum", "bwd_dh_dx", "bwd_dw", "bias_update", "dense_fwd", "dense_route", "dense_rec", "dense_dx",
-               "dense_dw"]
+    kernels = ["select", "select_rank", "fill", "bucket_single", "bucket_count", "bucket_place", "bucket_scan",
+               "bucket_scatter", "fwd_grouped", "rowsum", "bwd_dh_dx", "bwd_dw", "bias_update", "dense_fwd",
+               "dense_route", "dense_rec", "dense_dx", "dense_dw"]
     timing = not args.no_kernel_timing
     eager_ms = None
     if timing:

@@ -14,7 +14,9 @@
 //           order, a ballot over the wavefront's tokens gives each token its
 //           rank among the block's tokens that chose the group (ascending
 //           token), which plus the block base is its bucket position.
-// Up to 64 tokens (one block) a single workgroup does all three in one launch.
+// Up to 64 tokens (one block) a single workgroup does all three in one launch;
+// while the [blocks, G] count table is small, scan and scatter share a launch
+// (each workgroup reads the whole table).
 //
 // All loads of a pass are issued together (the ids of a block are one
 // contiguous slab of 64*k ints, read coalesced), so a pass costs a couple of
@@ -363,6 +365,130 @@ __global__ __launch_bounds__(TB) void bucket_scatter_kernel(const int32_t* __res
                     lane);
 }
 
+constexpr int PW = 4;          // blocks (wavefronts) per placement workgroup
+constexpr int PNT = PW * TB;   // 256 threads
+constexpr int PU = 16;         // block counts loaded per batch
+constexpr int kPlaceMaxTable = 32768;  // count-table entries a placement workgroup reads whole
+
+// Scan and scatter in one pass, for count tables small enough that every
+// workgroup reads the whole of bc[nblocks][groups]: workgroup p places blocks
+// [PW*p, PW*p + PW), one wavefront each.  Per group it sums the total and the
+// prefix over the blocks before its own (integer sums: any order gives the same
+// result), scans the totals into group and tile offsets (wavefront 0), and
+// wavefront w adds the counts of the workgroup's blocks before its own; then
+// the scatter above.  Workgroup 0 also writes offsets, tile_off, tile_group
+// and the padding rows.
+__global__ __launch_bounds__(PNT) void bucket_place_kernel(const int32_t* __restrict__ idx, int tokens, int k,
+                                                           int groups, int tile_rows, int max_tiles, int nblocks,
+                                                           const int32_t* __restrict__ bc, BucketOut out) {
+  extern __shared__ uint32_t sm[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gw = (groups + 31) >> 5, ms = mask_stride(groups), rs = row_stride(k);
+  const int slices = groups >= PNT ? 1 : PNT / groups;
+  int* tot = (int*)sm;                    // [groups]
+  int* pre = tot + groups;                // [groups]
+  int* g_off = pre + groups;              // [groups + 1]
+  int* g_toff = g_off + groups + 1;       // [groups + 1]
+  int* part = g_toff + groups + 1;        // [2][slices][groups]
+  const int fixed_words = 2 * groups + 2 * (groups + 1) + 2 * slices * groups;
+  char* wbase = (char*)sm + (((size_t)fixed_words * 4 + 15) & ~(size_t)15);  // per-wavefront regions
+  const size_t wbytes = ((size_t)2 * groups * 4 + (size_t)TB * ms * 4 + (size_t)TB * rs * 2 + (size_t)TB * k + 15) &
+                        ~(size_t)15;
+  char* mine = wbase + w * wbytes;
+  int* sbase = (int*)mine;                             // [2][groups]: CSR, padded
+  uint32_t* masks = (uint32_t*)(sbase + 2 * groups);   // [TB][ms]
+  int16_t* srow = (int16_t*)(masks + TB * ms);         // [TB][rs]
+  uint8_t* rk = (uint8_t*)(srow + TB * rs);            // [TB][k]
+
+  const int b0 = blockIdx.x * PW;
+  const int per = (nblocks + slices - 1) / slices;
+  for (int i = tid; i < slices * groups; i += PNT) {
+    const int g = i % groups, sl = i / groups;
+    const int lo = min(nblocks, sl * per), hi = min(nblocks, lo + per);
+    int sp = 0, st = 0;
+    for (int b = lo; b < hi; b += PU) {
+      int v[PU];
+#pragma unroll
+      for (int u = 0; u < PU; ++u) v[u] = b + u < hi ? bc[(size_t)(b + u) * groups + g] : 0;
+#pragma unroll
+      for (int u = 0; u < PU; ++u) {
+        st += v[u];
+        if (b + u < b0) sp += v[u];
+      }
+    }
+    part[sl * groups + g] = sp;
+    part[(slices + sl) * groups + g] = st;
+  }
+  __syncthreads();
+  for (int g = tid; g < groups; g += PNT) {
+    int sp = 0, st = 0;
+    for (int sl = 0; sl < slices; ++sl) {
+      sp += part[sl * groups + g];
+      st += part[(slices + sl) * groups + g];
+    }
+    pre[g] = sp;
+    tot[g] = st;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int carry = 0, tcarry = 0;
+    for (int c = 0; c < groups; c += TB) {
+      const int g = c + lane;
+      const int n = g < groups ? tot[g] : 0;
+      const int ntl = (n + tile_rows - 1) / tile_rows;
+      const int io = wave_inclusive_scan(n, lane), it = wave_inclusive_scan(ntl, lane);
+      if (g < groups) {
+        g_off[g] = carry + io - n;
+        g_toff[g] = tcarry + it - ntl;
+      }
+      carry += __shfl(io, 63);
+      tcarry += __shfl(it, 63);
+    }
+    if (lane == 0) {
+      g_off[groups] = carry;
+      g_toff[groups] = tcarry;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int g = tid; g <= groups; g += PNT) {
+      if (out.offsets) out.offsets[g] = g_off[g];
+      if (out.tile_off) out.tile_off[g] = g_toff[g];
+    }
+    if (out.tile_group) write_tile_groups(g_toff, groups, max_tiles, out.tile_group, tid, PNT);
+    if (out.ptoken) write_padding(g_off, g_toff, groups, tile_rows, out.ptoken, w, PW, lane);
+  }
+  // this wavefront's block: its bases, then the scatter
+  const int b = b0 + w;
+  const bool active = b < nblocks;
+  const size_t t0 = (size_t)b * TB;
+  const int nt = active ? min(TB, tokens - (int)t0) : 0;
+  if (active)
+    for (int g = lane; g < groups; g += TB) {
+      int run = pre[g];
+      for (int j = 0; j < w; ++j) run += bc[(size_t)(b0 + j) * groups + g];
+      sbase[g] = g_off[g] + run;
+      sbase[groups + g] = g_toff[g] * tile_rows + run;
+    }
+  int bits = 0;  // reported by the count pass
+  if (active) stage_ids<TB>(idx, t0, nt, k, groups, srow, rs, lane, bits);
+  __syncthreads();
+  mark_slots(srow + lane * rs, lane < nt ? k : 0, masks + lane * ms, gw, nullptr, bits);
+  __syncthreads();
+  block_ranks(masks, ms, gw, k, rk, lane);
+  __syncthreads();
+  block_outputs<TB>(srow, rs, masks, ms, rk, t0, nt, k, sbase, sbase + groups, 1, out.perm_token, out.inv,
+                    out.ptoken, out.pinv, lane);
+}
+
+size_t place_smem(int groups, int k) {
+  const int slices = groups >= PNT ? 1 : PNT / groups;
+  const size_t fixed = (size_t)(2 * groups + 2 * (groups + 1) + 2 * slices * groups) * 4;
+  const size_t wbytes = ((size_t)2 * groups * 4 + (size_t)TB * mask_stride(groups) * 4 +
+                         (size_t)TB * row_stride(k) * 2 + (size_t)TB * k + 15) & ~(size_t)15;
+  return ((fixed + 15) & ~(size_t)15) + PW * wbytes;
+}
+
 constexpr int SINGLE_NT = 1024;
 
 // All three passes for at most 64 tokens in one workgroup: every thread loads
@@ -455,6 +581,14 @@ hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int 
                        out.status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  // a count table every workgroup can read whole: scan and scatter in one pass
+  const size_t psmem = place_smem(groups, k);
+  if ((size_t)nb * groups <= (size_t)kPlaceMaxTable && psmem <= 64 * 1024) {
+    LaunchTimer timer("bucket_place", stream);
+    hipLaunchKernelGGL(bucket_place_kernel, dim3((nb + PW - 1) / PW), dim3(PNT), psmem, stream, idx, tokens, k,
+                       groups, tile_rows, mt, nb, (const int32_t*)bc, out);
+    return hipGetLastError();
   }
   {
     LaunchTimer timer("bucket_scan", stream);
