@@ -344,9 +344,21 @@ __global__ __launch_bounds__(NT) void select_rank_kernel(const float* __restrict
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * BM;
   for (int i = tid; i < groups; i += NT) cnt[i] = 0;
-  for (int p = tid; p < BM * groups; p += NT) {
-    const int r = p / groups, g = p % groups;
-    E[r * ES + g] = t0 + r < tokens ? e_in[(size_t)(t0 + r) * groups + g] : 0.0f;
+  // the block's rows are one contiguous run of the table: all loads in flight
+  // before the stores (8 per thread per batch)
+  const int n = BM * groups;
+  for (int p0 = 0; p0 < n; p0 += 8 * NT) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * NT + tid;
+      v[u] = p < n && t0 + p / groups < tokens ? e_in[(size_t)t0 * groups + p] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * NT + tid;
+      if (p < n) E[(p / groups) * ES + p % groups] = v[u];
+    }
   }
   __syncthreads();
   rank_topk<BM>(E, ES, cnt, t0, tokens, groups, k, idx_out, counts);
