@@ -307,17 +307,22 @@ __global__ __launch_bounds__(64 * REC_NW, 1) void dense_rec_kernel(const bf16_t*
 
 // dx[t0 + tile*128 + m, d-block] = sum over blocks of dg W_g + du W_u.
 // C^T (d x tokens) = W^T (d x K) . [dg du]^T (K x tokens): the weights come in
-// as N-row tiles (K = neuron rows, d contiguous), dg/du as K-row tiles.
-// Eight waves (one workgroup per CU): wave (wm, wn) owns d [wm*32, +32) x
+// as N-row tiles (K = neuron rows, d contiguous), dg/du as K-row tiles.  A
+// workgroup's block is 128 tokens x 256 d: the weight rows as two 128-d N-row
+// sub-tiles, so each staged dg/du tile feeds twice the MFMAs of a 128-d block.
+// Eight waves (one workgroup per CU): wave (wm, wn) owns d [wm*64, +64) x
 // tokens [wn*64, +64) of the block; every wave issues IA + IB loads per stage.
 struct DDx {
   static constexpr int NW = 8;
-  static constexpr int A_BYTES = 64 * 256;  // 64 neuron rows x 128 d
-  static constexpr int B_BYTES = BM * 128;  // 128 tokens x 64 neurons
+  static constexpr int DW = 256;                // d per block
+  static constexpr int SUBA = 64 * 256;         // one sub-tile: 64 neuron rows x 128 d
+  static constexpr int A_BYTES = (DW / 128) * SUBA;
+  static constexpr int B_BYTES = BM * 128;      // 128 tokens x 64 neurons
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int IA = A_BYTES / 1024 / NW, IB = B_BYTES / 1024 / NW;
   static constexpr int L = IA + IB;
-  static constexpr int WM = NW / 2, FM = 128 / WM / 16, FN = 4;
+  static constexpr int WM = NW / 2, FM = DW / WM / 16, FN = 4;
+  static_assert(IA * 1024 * NW == A_BYTES && IB * 1024 * NW == B_BYTES, "whole DMA instructions");
 };
 
 __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t* __restrict__ wg,
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t*
   ESG_LDS char* st1 = (ESG_LDS char*)st1_;
   ESG_LDS char* st2 = (ESG_LDS char*)st2_;
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int tile = blockIdx.x, db0 = blockIdx.y * 128;
+  const int tile = blockIdx.x, db0 = blockIdx.y * C::DW;
   const int nblk = (F + NB - 1) / NB;
   const uint32_t kbytes = (uint32_t)d * 2;
   const DmaSrc rg = make_dma_src(wg, (uint32_t)F * kbytes);
@@ -339,10 +344,11 @@ __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t*
   const DmaSrc rdg = make_dma_src(dg, pbytes);
   const DmaSrc rdu = make_dma_src(du, pbytes);
 
-  // A: neuron row kr = (w*IA + i)*4 + lane/16 of the stage, 16-byte chunk jz
+  // A: instruction ii = w*IA + i fills sub-tile ii/16 (d from db0 + 128*(ii/16)),
+  // neuron row kr = (ii%16)*4 + lane/16, 16-byte chunk jz
   int jz[C::IA];
 #pragma unroll
-  for (int i = 0; i < C::IA; ++i) jz[i] = (lane & 15) ^ mn_swz<16>((w * C::IA + i) * 4 + (lane >> 4));
+  for (int i = 0; i < C::IA; ++i) jz[i] = (lane & 15) ^ mn_swz<16>(((w * C::IA + i) & 15) * 4 + (lane >> 4));
   // B: packed row (w*IB + i)*8 + lane/8, chunk c_lane
   const int c_lane = (lane & 7) ^ (lane >> 3);
   // stage kt: block kt/4, half (kt/2)&1 (0: dg with W_g, 1: du with W_u), 64-neuron sub-block kt&1
@@ -351,10 +357,10 @@ __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t*
     const int n0 = blk * NB + sb * 64;
 #pragma unroll
     for (int i = 0; i < C::IA; ++i) {
-      const int kr = (w * C::IA + i) * 4 + (lane >> 4);
-      const bool ok = n0 + kr < F && db0 + jz[i] * 8 < d;
-      dma16(h ? ru : rg, st + (w * C::IA + i) * 1024,
-            ok ? (uint32_t)(n0 + kr) * kbytes + (uint32_t)db0 * 2 + jz[i] * 16 : kOOB);
+      const int ii = w * C::IA + i;
+      const int kr = (ii & 15) * 4 + (lane >> 4), dsub = db0 + (ii >> 4) * 128;
+      const bool ok = n0 + kr < F && dsub + jz[i] * 8 < d;
+      dma16(h ? ru : rg, st + ii * 1024, ok ? (uint32_t)(n0 + kr) * kbytes + (uint32_t)dsub * 2 + jz[i] * 16 : kOOB);
     }
     const uint32_t rbase = ((uint32_t)blk * tc_pad + (uint32_t)tile * BM) * (NB * 2) + sb * 128 + c_lane * 16;
 #pragma unroll
@@ -371,7 +377,10 @@ __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t*
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) a[kb][i] = frag_nrow<16>(st, kb, wm * (128 / C::WM) + i * 16, lane);
+      for (int i = 0; i < C::FM; ++i) {
+        const int dl = wm * (C::DW / C::WM) + i * 16;  // d within the block: sub-tile dl/128
+        a[kb][i] = frag_nrow<16>(st + (dl >> 7) * C::SUBA, kb, dl & 127, lane);
+      }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       uint4 b[C::FN];
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t*
   kloop<3, C::L, 0>(nblk * 4, st0, st1, st2, issue, compute);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    const int dd = db0 + wm * (128 / C::WM) + i * 16 + (lane >> 4) * 4;
+    const int dd = db0 + wm * (C::DW / C::WM) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int m = tile * BM + wn * 64 + j * 16 + (lane & 15);
@@ -505,7 +514,8 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
     }
     {
       LaunchTimer timer("dense_dx", stream);
-      hipLaunchKernelGGL(dense_dx_kernel, dim3(tiles, (d + 127) / 128), dim3(64 * DDx::NW), 0, stream, (const bf16_t*)wg,
+      hipLaunchKernelGGL(dense_dx_kernel, dim3(tiles, (d + DDx::DW - 1) / DDx::DW), dim3(64 * DDx::NW), 0, stream,
+                         (const bf16_t*)wg,
                          (const bf16_t*)wu, d, F, t0, tc, L.tc, dg, du, (bf16_t*)dx);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
