@@ -212,9 +212,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   const int kbytes = d_model * (int)sizeof(T);
   const int nk = (kbytes + KC * 16 - 1) / (KC * 16);
 
-  for (int i = tid; i < BM * ES; i += NT) {
-    const int g = i % ES;
-    E[i] = (bias != nullptr && g < groups) ? bias[g] : 0.0f;
+  // every row of the score table starts at the bias: one load per column
+  for (int g = tid; g < ES; g += NT) {
+    const float b = (bias != nullptr && g < groups) ? bias[g] : 0.0f;
+#pragma unroll 8
+    for (int r = 0; r < BM; ++r) E[r * ES + g] = b;
   }
   for (int i = tid; i < groups; i += NT) cnt[i] = 0;
 
