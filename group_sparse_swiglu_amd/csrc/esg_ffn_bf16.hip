@@ -49,13 +49,14 @@ constexpr int dw_subtiles() {
   return GSB >= 128 ? 2 : 1;
 }
 
-template <int GSB, int CPOL>
-__global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void fwd2_kernel(
+// NW: waves (fwd_waves<GSB>(); 8 for 64-neuron blocks when the grid leaves each
+// workgroup alone on its CU)
+template <int GSB, int CPOL, int NW>
+__global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
     const bf16_t* __restrict__ wd, int tokens, int d, int F, int gs, const int32_t* __restrict__ tile_group,
     const int32_t* __restrict__ ptoken, uint32_t rows_total, bf16_t* __restrict__ hg_saved,
     bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials) {
-  constexpr int NW = fwd_waves<GSB>();
   using C = Fwd2<GSB, NW>;
   constexpr int NS = stages_for<GSB>();
   // with two stages a third W_down buffer follows them
@@ -390,8 +391,12 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
                   const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg, void* hu,
                   void* partials, hipStream_t stream) {
   LaunchTimer timer("fwd_grouped", stream);
-  auto kern = partials_nontemporal(s, ntiles_max) ? fwd2_kernel<GSB, kCpolNontemporal> : fwd2_kernel<GSB, 0>;
-  hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * fwd_waves<GSB>()), 0, stream, (const bf16_t*)x,
+  constexpr int NW = fwd_waves<GSB>();
+  // a grid of at most one workgroup per CU: eight waves issue the loads
+  const bool alone = NW == 4 && (long long)ntiles_max * s.nsub() <= compute_units();
+  auto kern = partials_nontemporal(s, ntiles_max) ? fwd2_kernel<GSB, kCpolNontemporal, NW>
+                                                  : (alone ? fwd2_kernel<GSB, 0, 8> : fwd2_kernel<GSB, 0, NW>);
+  hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * (alone ? 8 : NW)), 0, stream, (const bf16_t*)x,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
                      (bf16_t*)partials);
