@@ -527,7 +527,6 @@ def main():
     BIAS = (bias if bias is not None else torch.zeros(G)).to(dev)
     EMA = torch.full((G,), w.k / G, dtype=torch.float32, device=dev)
     IDX = torch.empty(w.tokens, w.k, dtype=torch.int32, device=dev)
-    CNT = torch.empty(G, dtype=torch.int32, device=dev)
     Y = torch.empty_like(X)
     GRADS = (torch.empty_like(X), torch.empty_like(WG), torch.empty_like(WU), torch.empty_like(WD))
     # the selection's energy table (used by batches too small to fill the CUs)
@@ -550,13 +549,15 @@ def main():
             saved[0] = ctx.saved
             E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
             return
-        E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, return_counts=True,
-                              out=IDX, counts_out=CNT, workspace=SELWS)
+        # the bias update takes its per-group counts from the routing the forward
+        # saved, so the selection runs without counts
+        E.grouped_topk_select(X, WG, w.group_size, w.k, SUB, w.spg, BIAS if w.bias else None, out=IDX,
+                              workspace=SELWS)
         _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, saved=saved[0])
         saved[0] = ctx.saved
         E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
         if w.bias_update:
-            E.update_load_balance_bias_from_counts(BIAS, EMA, CNT, w.tokens, w.k / G, 1e-3, 0.5, 0.99)
+            E.update_load_balance_bias_from_routing(BIAS, EMA, ctx, w.k / G, 1e-3, 0.5, 0.99)
 
     for _ in range(args.warmup):
         step()

@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "ESG_F32", "ESG_BF16", "EsgError", "lib", "library_path", "make_subsample_index", "grouped_topk_select",
     "select_workspace_size", "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn",
-    "update_load_balance_bias",
+    "update_load_balance_bias", "update_load_balance_bias_from_routing",
     "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
     "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
     "leaky_mlp_workspace_size", "leaky_mlp_fwd", "leaky_mlp_bwd", "leaky_mlp_saved_views",
@@ -67,6 +67,8 @@ _SIGNATURES = {
     "esg_update_load_balance_bias": (_c_int, [_c_vp, _c_vp, _c_vp, _c_f, _c_f, _c_f, _c_f, _c_int, _c_vp]),
     "esg_update_load_balance_bias_from_counts": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_f, _c_f, _c_f, _c_f,
                                                           _c_int, _c_vp]),
+    "esg_update_load_balance_bias_from_routing": (_c_int, [_c_vp, _c_vp, _c_vp, _c_size, _c_int, _c_int, _c_int,
+                                                           _c_int, _c_int, _c_int, _c_f, _c_f, _c_f, _c_f, _c_vp]),
     "esg_leaky_mlp_workspace_size": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_size),
                                               ctypes.POINTER(_c_size)]),
     "esg_leaky_mlp_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -217,11 +219,16 @@ def workspace_size(tokens, d_model, d_ff, group_size, k, dtype_code, dense=False
 
 @dataclass
 class FfnContext:
-    """What the backward needs from the forward (caller-owned buffers)."""
+    """What the backward needs from the forward (caller-owned buffers), and the
+    forward's shape (for the bias update from its routing)."""
     saved: torch.Tensor
     idx: Optional[torch.Tensor]
     group_size: int
     k: int
+    tokens: int = 0
+    d_model: int = 0
+    d_ff: int = 0
+    dtype_code: int = ESG_BF16
 
 
 def _ws(nbytes: int, dev, cache: Optional[dict], key: str) -> torch.Tensor:
@@ -263,7 +270,7 @@ def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, statu
         saved.numel() if saved is not None else 0,
         _dev(scratch, "scratch"), scratch.numel(), _dev(status, "status", torch.int32), _stream(dev)),
         "sparse_swiglu_fwd")
-    return y, FfnContext(saved, group_idx, group_size, k)
+    return y, FfnContext(saved, group_idx, group_size, k, T, d, F, code)
 
 
 def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=None, outs=None):
@@ -327,6 +334,17 @@ def update_load_balance_bias_from_counts(bias, freq_ema, counts, tokens: int, ta
         _dev(bias, "bias", torch.float32), _dev(freq_ema, "freq_ema", torch.float32),
         _dev(counts, "counts", torch.int32), tokens, target_freq, gamma, bias_max, momentum, G,
         _stream(bias.device)), "update_load_balance_bias_from_counts")
+
+
+def update_load_balance_bias_from_routing(bias, freq_ema, ctx: FfnContext, target_freq: float, gamma: float,
+                                          bias_max: float, momentum: float):
+    """Bias update with the per-group counts of the routing a training forward saved in ``ctx``."""
+    if ctx.saved is None or ctx.idx is None:
+        raise EsgError("the context holds no saved routing (inference or dense forward)")
+    _check(lib().esg_update_load_balance_bias_from_routing(
+        _dev(bias, "bias", torch.float32), _dev(freq_ema, "freq_ema", torch.float32), _dev(ctx.saved, "saved"),
+        ctx.saved.numel(), ctx.tokens, ctx.d_model, ctx.d_ff, ctx.group_size, ctx.k, ctx.dtype_code, target_freq,
+        gamma, bias_max, momentum, _stream(bias.device)), "update_load_balance_bias_from_routing")
 
 
 def leaky_mlp_workspace_size(tokens: int, d_model: int, d_ff: int):

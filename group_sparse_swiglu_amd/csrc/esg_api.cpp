@@ -356,8 +356,8 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
 int esg_update_load_balance_bias(float* bias, float* freq_ema, const float* current_freq, float target_freq,
                                  float gamma, float bias_max, float momentum, int groups, void* stream) {
   if (bias == nullptr || freq_ema == nullptr || current_freq == nullptr || groups < 0) return ESG_ERR_INVALID_ARG;
-  return hip_status(launch_bias_update(bias, freq_ema, current_freq, nullptr, 1, target_freq, gamma, bias_max,
-                                       momentum, groups, (hipStream_t)stream));
+  return hip_status(launch_bias_update(bias, freq_ema, current_freq, nullptr, nullptr, 1, target_freq, gamma,
+                                       bias_max, momentum, groups, (hipStream_t)stream));
 }
 
 int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const int32_t* counts, int tokens,
@@ -365,8 +365,23 @@ int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const
                                              int groups, void* stream) {
   if (bias == nullptr || freq_ema == nullptr || counts == nullptr || groups < 0 || tokens <= 0)
     return ESG_ERR_INVALID_ARG;
-  return hip_status(launch_bias_update(bias, freq_ema, nullptr, counts, tokens, target_freq, gamma, bias_max,
-                                       momentum, groups, (hipStream_t)stream));
+  return hip_status(launch_bias_update(bias, freq_ema, nullptr, counts, nullptr, tokens, target_freq, gamma,
+                                       bias_max, momentum, groups, (hipStream_t)stream));
+}
+
+int esg_update_load_balance_bias_from_routing(float* bias, float* freq_ema, const void* saved, size_t saved_bytes,
+                                              int tokens, int d_model, int d_ff, int group_size, int k, int dtype,
+                                              float target_freq, float gamma, float bias_max, float momentum,
+                                              void* stream) {
+  int st = check_shape(dtype, tokens, d_model, d_ff, group_size, k);
+  if (st != ESG_OK) return st;
+  if (bias == nullptr || freq_ema == nullptr || saved == nullptr || tokens <= 0) return ESG_ERR_INVALID_ARG;
+  if (k > kMaxK) return ESG_ERR_UNSUPPORTED;
+  const FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
+  const Layout L = make_layout(s);
+  if (saved_bytes < L.saved) return ESG_ERR_WORKSPACE;
+  return hip_status(launch_bias_update(bias, freq_ema, nullptr, nullptr, at<int32_t>(saved, L.offsets), tokens,
+                                       target_freq, gamma, bias_max, momentum, s.groups(), (hipStream_t)stream));
 }
 
 namespace {

@@ -111,8 +111,8 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
 
 // ---- bias update / fills -------------------------------------------------------
 hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts,
-                              int tokens, float target, float gamma, float bias_max, float momentum,
-                              int groups, hipStream_t stream);
+                              const int32_t* offsets, int tokens, float target, float gamma, float bias_max,
+                              float momentum, int groups, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stream);
 
 // ---- LeakyReLU(0.5)^2 MLP (esg_mlp.hip), bf16 ------------------------------------

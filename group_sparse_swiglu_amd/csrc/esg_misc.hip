@@ -12,13 +12,16 @@
 namespace esg {
 namespace {
 
+// The current frequency of group g: freq[g], or counts[g] / tokens, or (from
+// the CSR group offsets of a routing) (offsets[g+1] - offsets[g]) / tokens.
 __global__ void bias_update_kernel(float* __restrict__ bias, float* __restrict__ ema,
                                    const float* __restrict__ freq, const int32_t* __restrict__ counts,
-                                   int tokens, float target, float gamma, float bias_max, float momentum,
-                                   int groups) {
+                                   const int32_t* __restrict__ offsets, int tokens, float target, float gamma,
+                                   float bias_max, float momentum, int groups) {
 #pragma clang fp contract(off)
   for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += gridDim.x * blockDim.x) {
-    const float cur = freq ? freq[g] : (float)counts[g] / (float)tokens;
+    const int n = counts ? counts[g] : (offsets ? offsets[g + 1] - offsets[g] : 0);
+    const float cur = freq ? freq[g] : (float)n / (float)tokens;
     const float e = ema[g];
     const float om = 1.0f - momentum;
     const float ne = e + om * (cur - e);
@@ -38,15 +41,15 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t v, size_t n) {
 
 }  // namespace
 
-hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts, int tokens,
-                              float target, float gamma, float bias_max, float momentum, int groups,
-                              hipStream_t stream) {
+hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const int32_t* counts,
+                              const int32_t* offsets, int tokens, float target, float gamma, float bias_max,
+                              float momentum, int groups, hipStream_t stream) {
   if (groups == 0) return hipSuccess;
   const int threads = 256;
   const int blocks = (groups + threads - 1) / threads;
   LaunchTimer timer("bias_update", stream);
-  hipLaunchKernelGGL(bias_update_kernel, dim3(blocks), dim3(threads), 0, stream, bias, ema, freq, counts, tokens,
-                     target, gamma, bias_max, momentum, groups);
+  hipLaunchKernelGGL(bias_update_kernel, dim3(blocks), dim3(threads), 0, stream, bias, ema, freq, counts, offsets,
+                     tokens, target, gamma, bias_max, momentum, groups);
   return hipGetLastError();
 }
 

@@ -219,6 +219,22 @@ int esg_update_load_balance_bias_from_counts(float* bias, float* freq_ema, const
                                              void* stream);
 
 /*
+ * The same update with the counts taken from the routing a training forward
+ * stored in `saved` (esg_sparse_swiglu_fwd with a non-NULL `saved`): its CSR
+ * group offsets give count[g] = offsets[g+1] - offsets[g], the number of valid
+ * (token, group) pairs routed to g, equal to the selection's counts when the
+ * routing came from esg_grouped_topk_select.  A training step that updates the
+ * bias can then select without counts (no counts fill, no count atomics).
+ * Shape arguments as given to that forward; saved_bytes at least its
+ * saved size.  Errors: ESG_ERR_INVALID_ARG (NULL pointers, tokens <= 0),
+ * ESG_ERR_UNSUPPORTED (shape rules), ESG_ERR_WORKSPACE (saved too small).
+ */
+int esg_update_load_balance_bias_from_routing(float* bias, float* freq_ema, const void* saved, size_t saved_bytes,
+                                              int tokens, int d_model, int d_ff, int group_size, int k, int dtype,
+                                              float target_freq, float gamma, float bias_max, float momentum,
+                                              void* stream);
+
+/*
  * LeakyReLU(0.5)-squared MLP with a stored activation gradient (parameter-golf
  * pull request 1105, "1. Fused MLP Kernels"; architecture table A.7: d_model
  * 512, width 3.5 x 512 = 1792).  bf16 tensors, fp32 accumulation:

@@ -110,6 +110,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
                                      16, None) == 3   # dense backward scratch too small
     assert lib.esg_update_load_balance_bias(None, 64, 64, 0.25, 1e-3, 0.5, 0.99, 4, None) == 1
     assert lib.esg_update_load_balance_bias_from_counts(64, 64, 64, 0, 0.25, 1e-3, 0.5, 0.99, 4, None) == 1
+    # bias update from a saved routing: NULL saved, bad shape, saved too small
+    assert lib.esg_update_load_balance_bias_from_routing(64, 64, None, 1 << 20, 64, 64, 256, 32, 2, 1, 0.25, 1e-3,
+                                                         0.5, 0.99, None) == 1
+    assert lib.esg_update_load_balance_bias_from_routing(64, 64, 64, 1 << 20, 64, 60, 256, 32, 2, 1, 0.25, 1e-3,
+                                                         0.5, 0.99, None) == 2
+    assert lib.esg_update_load_balance_bias_from_routing(64, 64, 64, 16, 64, 64, 256, 32, 2, 1, 0.25, 1e-3, 0.5,
+                                                         0.99, None) == 3
     need = ctypes.c_size_t()
     assert lib.esg_bucket_workspace_size(100, 200, 300, ctypes.byref(need)) == 2   # k above the bucket limit
     assert lib.esg_bucket_workspace_size(100, 4, 2000, ctypes.byref(need)) == 2   # G above 1024

@@ -45,3 +45,27 @@ def test_bias_update_from_counts_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(b_d.cpu().numpy(), bias)
     assert np.array_equal(e_d.cpu().numpy(), ema)
+
+
+@pytest.mark.parametrize("T,d,F,gs,k", [(8192, 768, 2048, 64, 8), (333, 96, 640, 64, 3), (64, 2048, 5504, 128, 11)])
+def test_bias_update_from_routing_equals_from_counts(T, d, F, gs, k):
+    """The bias update from a training forward's saved routing reproduces the
+    update from the selection's counts bit for bit."""
+    require_gpu()
+    note(f"bias from routing T={T} G={F // gs} k={k}")
+    from gpu_common import inputs, to_dev
+    inp = inputs(T, d, F, gs, "bf16", seed=9, bias=True, spg=min(8, gs))
+    x, wg, wu, wd = (to_dev(inp[n]) for n in ("x", "wg", "wu", "wd"))
+    idx, counts = E.grouped_topk_select(x, wg, gs, k, to_dev(inp["sub"]), inp["spg"], to_dev(inp["bias"]),
+                                        return_counts=True)
+    _, ctx = E.sparse_swiglu_fwd(x, wg, wu, wd, idx, gs)
+    G = F // gs
+    rng = np.random.default_rng(T)
+    bias0 = torch.from_numpy(rng.uniform(-0.1, 0.1, G).astype(np.float32))
+    ema0 = torch.from_numpy(rng.uniform(0.0, 2.0 * k / G, G).astype(np.float32))
+    b1, e1 = bias0.to(DEV), ema0.to(DEV)
+    b2, e2 = bias0.to(DEV), ema0.to(DEV)
+    E.update_load_balance_bias_from_counts(b1, e1, counts, T, k / G, 1e-3, 0.5, 0.99)
+    E.update_load_balance_bias_from_routing(b2, e2, ctx, k / G, 1e-3, 0.5, 0.99)
+    torch.cuda.synchronize()
+    assert torch.equal(b1, b2) and torch.equal(e1, e2)
