@@ -91,8 +91,35 @@ __device__ void stage_ids(const int32_t* __restrict__ idx, size_t t0, int nt, in
 
 // One lane walks its token's ids in slot order: the first occurrence of an id
 // sets its bit in the token's group mask (and counts it in `hist` if given);
-// a repeat is rewritten to -1 (status bit 2).
+// a repeat is rewritten to -1 (status bit 2).  Up to 64 groups the mask lives
+// in two registers and the ids are read 16 at a time (no dependent LDS round
+// trip per slot); beyond, the mask is updated in LDS.
 __device__ void mark_slots(int16_t* r, int k, uint32_t* m, int gw, int* hist, int& bits) {
+  if (gw <= 2) {
+    uint32_t m0 = 0, m1 = 0;
+    for (int j0 = 0; j0 < k; j0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = j0 + u < k ? r[j0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int g = v[u];
+        if (g < 0) continue;
+        const uint32_t bit = 1u << (g & 31);
+        const uint32_t mw = g >= 32 ? m1 : m0;
+        if (mw & bit) {
+          r[j0 + u] = -1;
+          bits |= 2;
+        } else {
+          if (g >= 32) m1 |= bit; else m0 |= bit;
+          if (hist) atomicAdd(&hist[g], 1);
+        }
+      }
+    }
+    m[0] = m0;
+    if (gw > 1) m[1] = m1;
+    return;
+  }
   for (int i = 0; i < gw; ++i) m[i] = 0;
   for (int j = 0; j < k; ++j) {
     const int g = r[j];
