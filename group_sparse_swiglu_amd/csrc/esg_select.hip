@@ -443,10 +443,13 @@ hipError_t select_split(const SelArgs& a, float* ews, hipStream_t st) {
       default: e = launch_select_t<T, 32, 8>(a, st, gpc, ews); break;
     }
   if (e != hipSuccess) return e;
+  // ranking in 8-token workgroups: four times the workgroups of the 32-token
+  // blocks, two tokens (or one pair) per wave
+  constexpr int RBM = 8;
   LaunchTimer timer("select_rank", st);
-  const size_t smem = (size_t)32 * (a.groups | 1) * 4 + (size_t)a.groups * 4;
-  hipLaunchKernelGGL(select_rank_kernel<32>, dim3(blocks), dim3(NT), smem, st, (const float*)ews, a.tokens,
-                     a.groups, a.k, a.idx, a.counts);
+  const size_t smem = (size_t)RBM * (a.groups | 1) * 4 + (size_t)a.groups * 4;
+  hipLaunchKernelGGL(select_rank_kernel<RBM>, dim3((a.tokens + RBM - 1) / RBM), dim3(NT), smem, st,
+                     (const float*)ews, a.tokens, a.groups, a.k, a.idx, a.counts);
   return hipGetLastError();
 }
 
