@@ -429,7 +429,9 @@ hipError_t select_split(const SelArgs& a, float* ews, hipStream_t st) {
   const int blocks = (a.tokens + 31) / 32;
   const int want = std::max(1, (2 * compute_units() + blocks - 1) / blocks);
   const int chunks0 = std::min(a.groups, want);
-  const int gpc = (a.groups + chunks0 - 1) / chunks0;
+  // at most 128 sampled rows per workgroup (one super-chunk of the small-stage
+  // configuration, two workgroups per CU)
+  const int gpc = std::min((a.groups + chunks0 - 1) / chunks0, std::max(1, 128 / a.rpg));
   const int cols = gpc * a.rpg;  // sampled columns per workgroup
   hipError_t e;
   if (std::is_same<T, bf16_t>::value)
