@@ -25,6 +25,7 @@ namespace {
 constexpr int NT = 256;
 constexpr int KC = 4;  // chunks per K stage
 constexpr size_t kSelLds = 160 * 1024;
+constexpr int kSel128Waves = 8;
 
 // BM tokens per workgroup; each wave owns FNW 16-column fragments of a
 // super-chunk of 4*FNW*16 sampled rows, interleaved across the waves, so the
@@ -33,18 +34,25 @@ constexpr size_t kSelLds = 160 * 1024;
 // into K-row tiles (64 K per stage, DMA_NS stages); other cases stage through
 // registers.  Every workgroup streams all sampled rows once per K step, so a
 // larger BM divides that traffic over more tokens.
-template <typename T, int BM, int FNW, bool USE_DMA = true>
+// NW = 8 (128-token blocks): the four column groups each split their rows in
+// two halves, two waves per SIMD.
+template <typename T, int BM, int FNW, bool USE_DMA = true, int NW = 4>
 struct SelCfg {
+  static constexpr int NTH = 64 * NW;
   static constexpr int NSC = 4 * FNW * 16;  // sampled rows per super-chunk
   static constexpr int FM = BM / 16;
+  static constexpr int RH = NW / 4;         // row halves
+  static constexpr int FMW = FM / RH;       // row fragments per wave
   static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && (BM == 32 || BM == 128) && FNW <= 4;
-  static constexpr int IA = BM / 32;  // x rows loads per lane per stage (8 rows per wave each)
+  static constexpr int IA = BM / (8 * NW);  // x rows loads per lane per stage (8 rows each)
+  static constexpr int IB = NSC / (8 * NW);
+  static_assert(NW == 4 || (DMA && IA * 8 * NW == BM && IB * 8 * NW == NSC), "eight waves: whole DMA loads");
   static constexpr int PA = Plane<BM>::BYTES;
   static constexpr int PB = Plane<NSC>::BYTES;
   static constexpr int A_BYTES = DMA ? BM * 128 : KC * PA;
   static constexpr int B_BYTES = DMA ? NSC * 128 : KC * PB;
   static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES) <= 112 * 1024 ? 3 : 2;
-  static constexpr int DMA_L = IA + NSC / 32;  // loads per lane per stage
+  static constexpr int DMA_L = IA + IB;  // loads per lane per stage
   static constexpr int STAGES = (DMA ? DMA_NS : 2) * (A_BYTES + B_BYTES);
   static constexpr int S_STRIDE = NSC + 1;  // odd float stride: conflict-free column walks
   static constexpr int S_BYTES = BM * S_STRIDE * 4;
@@ -53,17 +61,18 @@ struct SelCfg {
 
 // |SiLU| of one super-chunk's accumulators into S, then per (token, group)
 // sums over the super-chunk's columns, in column order, added to E.
-template <class C, int FM, int FNW>
-__device__ __forceinline__ void select_energy(const f32x4 (&acc)[FM][FNW], float* S, float* E, int ES, int n0,
-                                              int ncols, int rpg, int groups, int lane, const int (&brow)[FNW]) {
-  constexpr int BM = FM * 16;
+template <class C, int FMW, int FNW>
+__device__ __forceinline__ void select_energy(const f32x4 (&acc)[FMW][FNW], float* S, float* E, int ES, int n0,
+                                              int ncols, int rpg, int groups, int lane, const int (&brow)[FNW],
+                                              int rh) {
+  constexpr int BM = C::FM * 16;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FMW; ++i)
 #pragma unroll
     for (int j = 0; j < FNW; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = i * 16 + (lane >> 4) * 4 + e;
+        const int r = (rh * FMW + i) * 16 + (lane >> 4) * 4 + e;
         const float h = acc[i][j][e];
         S[r * C::S_STRIDE + brow[j]] = fabsf(h * sigmoid_f(h));
       }
@@ -71,7 +80,7 @@ __device__ __forceinline__ void select_energy(const f32x4 (&acc)[FM][FNW], float
   const int g_lo = n0 / rpg;
   const int g_hi = min(groups - 1, (min(n0 + C::NSC, ncols) - 1) / rpg);
   const int ng = g_hi - g_lo + 1;
-  for (int p = threadIdx.x; p < BM * ng; p += NT) {
+  for (int p = threadIdx.x; p < BM * ng; p += C::NTH) {
     const int r = p % BM, g = g_lo + p / BM;
     const int c0 = max(n0, g * rpg) - n0, c1 = min(n0 + C::NSC, (g + 1) * rpg) - n0;
     float sum = E[r * ES + g];
@@ -82,8 +91,8 @@ __device__ __forceinline__ void select_energy(const f32x4 (&acc)[FM][FNW], float
 
 // Top-k of the BM tokens whose scores are E[r * ES + g] (LDS), written to
 // idx_out in ascending group id; per-group counts through the LDS table cnt
-// (zeroed by the caller) when counts is given.  256 threads.
-template <int BM>
+// (zeroed by the caller) when counts is given.  NW waves.
+template <int BM, int NW = 4>
 __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int t0, int tokens, int groups, int k,
                                           int32_t* __restrict__ idx_out, int32_t* __restrict__ counts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,27 +103,27 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
   if (groups <= 32) {
     // the two half-waves rank two tokens at a time: lane l holds group l % 32
     // of token half l / 32; a token's other scores are broadcast reads
-    constexpr int TPW = BM / 8;  // token pairs per wave
+    constexpr int TPW = BM / (2 * NW);  // token pairs per wave
     const int hf = lane >> 5, g = lane & 31;
     float sg[TPW];
     int beat[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int r = wave + 4 * (2 * i + hf);
+      const int r = wave + NW * (2 * i + hf);
       sg[i] = g < groups ? E[r * ES + g] : 0.0f;
       beat[i] = 0;
     }
     for (int q = 0; q < groups; ++q) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
-        const float sq = E[(wave + 4 * (2 * i + hf)) * ES + q];
+        const float sq = E[(wave + NW * (2 * i + hf)) * ES + q];
         beat[i] += (sq > sg[i]) || (sq == sg[i] && q < g);
       }
     }
     const uint64_t half = hf ? 0xffffffff00000000ull : 0x00000000ffffffffull;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int t = t0 + wave + 4 * (2 * i + hf);
+      const int t = t0 + wave + NW * (2 * i + hf);
       const bool sel = g < groups && beat[i] < k;
       const uint64_t m = __ballot(sel) & half;
       const int pos = __popcll(m & lt);
@@ -124,26 +133,26 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
       }
     }
   } else if (groups <= 64) {
-    // lane g holds group g of the wave's BM/4 tokens at once; every other
+    // lane g holds group g of the wave's BM/NW tokens at once; every other
     // group's score comes as a broadcast LDS read (same address in all lanes)
-    constexpr int TPW = BM / 4;
+    constexpr int TPW = BM / NW;
     float sg[TPW];
     int beat[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      sg[i] = lane < groups ? E[(wave + 4 * i) * ES + lane] : 0.0f;
+      sg[i] = lane < groups ? E[(wave + NW * i) * ES + lane] : 0.0f;
       beat[i] = 0;
     }
     for (int q = 0; q < groups; ++q) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
-        const float sq = E[(wave + 4 * i) * ES + q];
+        const float sq = E[(wave + NW * i) * ES + q];
         beat[i] += (sq > sg[i]) || (sq == sg[i] && q < lane);
       }
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int t = t0 + wave + 4 * i;
+      const int t = t0 + wave + NW * i;
       const bool sel = lane < groups && beat[i] < k;
       const uint64_t m = __ballot(sel);
       const int pos = __popcll(m & lt);
@@ -153,7 +162,7 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
       }
     }
   } else {
-    for (int r = wave; r < BM; r += 4) {
+    for (int r = wave; r < BM; r += NW) {
       const int t = t0 + r;
       if (t >= tokens) break;
       const float* row = E + r * ES;
@@ -182,20 +191,21 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
   }
   if (counts) {
     __syncthreads();
-    for (int g = tid; g < groups; g += NT)
+    for (int g = tid; g < groups; g += 64 * NW)
       if (cnt[g]) atomicAdd(&counts[g], cnt[g]);
   }
 }
 
-template <typename T, int BM, int FNW, bool USE_DMA>
-__global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, const T* __restrict__ wg,
+template <typename T, int BM, int FNW, bool USE_DMA, int NW>
+__global__ __launch_bounds__(64 * NW) void select_kernel(const T* __restrict__ x, const T* __restrict__ wg,
                                                      int tokens, int d_model, int d_ff, int groups, int k,
                                                      const int32_t* __restrict__ sub, int rpg,
                                                      const float* __restrict__ bias,
                                                      int32_t* __restrict__ idx_out,
                                                      int32_t* __restrict__ counts, int gpc,
                                                      float* __restrict__ e_out) {
-  using C = SelCfg<T, BM, FNW, USE_DMA>;
+  using C = SelCfg<T, BM, FNW, USE_DMA, NW>;
+  static_assert(NW == 4 || C::DMA, "the register-staged path runs four waves");
   extern __shared__ __align__(16) char smem[];
   auto la = [&](int i_) -> char* { return smem + i_ * C::A_BYTES; };
   auto lb = [&](int i_) -> char* { return smem + 2 * C::A_BYTES + i_ * C::B_BYTES; };
@@ -213,18 +223,21 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
   const int nk = (kbytes + KC * 16 - 1) / (KC * 16);
 
   // every row of the score table starts at the bias: one load per column
-  for (int g = tid; g < ES; g += NT) {
+  for (int g = tid; g < ES; g += C::NTH) {
     const float b = (bias != nullptr && g < groups) ? bias[g] : 0.0f;
 #pragma unroll 8
     for (int r = 0; r < BM; ++r) E[r * ES + g] = b;
   }
-  for (int i = tid; i < groups; i += NT) cnt[i] = 0;
+  for (int i = tid; i < groups; i += C::NTH) cnt[i] = 0;
 
-  int arow[C::FM], brow[FNW];
+  // wave -> column group cg (FNW fragments interleaved over the four groups)
+  // and row half rh (eight waves)
+  const int cg = wave & 3, rh = wave >> 2;
+  int arow[C::FMW], brow[FNW];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) arow[i] = i * 16 + (lane & 15);
+  for (int i = 0; i < C::FMW; ++i) arow[i] = (rh * C::FMW + i) * 16 + (lane & 15);
 #pragma unroll
-  for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + wave) * 16 + (lane & 15);
+  for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + cg) * 16 + (lane & 15);
 
   if constexpr (C::DMA) {
     ESG_LDS char* st0 = (ESG_LDS char*)smem;
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
       const int xr = (w * C::IA + i) * 8 + (lane >> 3);
       voffA[i] = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
     }
-    constexpr int IB = C::NSC / 32;
+    constexpr int IB = C::IB;
     for (int n0 = c_begin; n0 < ncols; n0 += C::NSC) {
       uint32_t voffB[IB];
 #pragma unroll
@@ -257,19 +270,19 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
         for (int i = 0; i < IB; ++i)
           dma16(rwg, st + C::A_BYTES + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
       };
-      f32x4 acc[C::FM][FNW];
+      f32x4 acc[C::FMW][FNW];
       zero_acc(acc);
       auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int cc = kb * 4 + (lane >> 4);
-          uint4 a[C::FM], b[FNW];
+          uint4 a[C::FMW], b[FNW];
 #pragma unroll
-          for (int i = 0; i < C::FM; ++i) a[i] = frag_krow(st, arow[i], cc);
+          for (int i = 0; i < C::FMW; ++i) a[i] = frag_krow(st, arow[i], cc);
 #pragma unroll
           for (int j = 0; j < FNW; ++j) b[j] = frag_krow(st + C::A_BYTES, brow[j], cc);
 #pragma unroll
-          for (int i = 0; i < C::FM; ++i)
+          for (int i = 0; i < C::FMW; ++i)
 #pragma unroll
             for (int j = 0; j < FNW; ++j) mma_bf16(acc[i][j], a[i], b[j]);
         }
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
       tiles::kloop<C::DMA_NS, C::DMA_L, 0>((kbytes + 127) / 128, st0, st0 + SB, st0 + 2 * SB, issue, compute);
       wait_lgkm0();
       barrier();  // every wave is done with the stages before S overwrites them
-      select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
+      select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow, rh);
     }
   } else {
   RowKLoader<BM, KC, NT> ldA;
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
       }
       __syncthreads();
     }
-    select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow);
+    select_energy<C>(acc, S, E, ES, n0, ncols, rpg, groups, lane, brow, rh);
     // the next super-chunk's first __syncthreads orders these before S is reused
   }
   }
@@ -324,13 +337,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const T* __restrict__ x, con
 
   // energies only: the ranking runs in select_rank_kernel over the whole table
   if (e_out != nullptr) {
-    for (int p = tid; p < BM * (g_end - g_begin); p += NT) {
+    for (int p = tid; p < BM * (g_end - g_begin); p += C::NTH) {
       const int r = p / (g_end - g_begin), g = g_begin + p % (g_end - g_begin);
       if (t0 + r < tokens) e_out[(size_t)(t0 + r) * groups + g] = E[r * ES + g];
     }
     return;
   }
-  rank_topk<BM>(E, ES, cnt, t0, tokens, groups, k, idx_out, counts);
+  rank_topk<BM, NW>(E, ES, cnt, t0, tokens, groups, k, idx_out, counts);
 }
 
 // Top-k from an energy table e_in [tokens, groups] (bias included) written by
@@ -378,30 +391,30 @@ struct SelArgs {
 };
 
 // gpc groups per workgroup along y; e_out != NULL: energies only (no ranking).
-template <typename T, int BM, int FNW, bool USE_DMA>
+template <typename T, int BM, int FNW, bool USE_DMA, int NW>
 hipError_t launch_select_v(const SelArgs& a, int gpc, float* e_out, hipStream_t stream) {
-  using C = SelCfg<T, BM, FNW, USE_DMA>;
+  using C = SelCfg<T, BM, FNW, USE_DMA, NW>;
   const size_t smem = C::FIXED + (size_t)BM * (a.groups | 1) * 4 + (size_t)a.groups * 4;
-  static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW, USE_DMA>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)select_kernel<T, BM, FNW, USE_DMA, NW>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kSelLds);
   if (attr != hipSuccess) return attr;
   const dim3 grid((a.tokens + BM - 1) / BM, (a.groups + gpc - 1) / gpc);
   LaunchTimer timer("select", stream);
-  hipLaunchKernelGGL((select_kernel<T, BM, FNW, USE_DMA>), grid, dim3(NT), smem, stream, (const T*)a.x,
+  hipLaunchKernelGGL((select_kernel<T, BM, FNW, USE_DMA, NW>), grid, dim3(C::NTH), smem, stream, (const T*)a.x,
                      (const T*)a.wg, a.tokens, a.d_model, a.d_ff, a.groups, a.k, a.sub, a.rpg, a.bias,
                      e_out ? nullptr : a.idx, e_out ? nullptr : a.counts, gpc, e_out);
   return hipGetLastError();
 }
 
 // The direct-to-LDS path addresses x and w_gate through 32-bit buffer offsets.
-// (the register-staged fallback keeps BM = 32)
-template <typename T, int BM, int FNW>
+// (the register-staged fallback keeps BM = 32 and four waves)
+template <typename T, int BM, int FNW, int NW = 4>
 hipError_t launch_select_t(const SelArgs& a, hipStream_t stream, int gpc = 0, float* e_out = nullptr) {
   if (gpc <= 0) gpc = a.groups;
   const unsigned long long kb = (unsigned long long)a.d_model * sizeof(T);
   if ((unsigned long long)a.tokens * kb < (1ull << 31) && (unsigned long long)a.d_ff * kb < (1ull << 31))
-    return launch_select_v<T, BM, FNW, true>(a, gpc, e_out, stream);
-  return launch_select_v<T, (BM < 32 ? BM : 32), FNW, false>(a, gpc, e_out, stream);
+    return launch_select_v<T, BM, FNW, true, NW>(a, gpc, e_out, stream);
+  return launch_select_v<T, (BM < 32 ? BM : 32), FNW, false, 4>(a, gpc, e_out, stream);
 }
 
 // Fragments per wave: the choice with the least padded MFMA work (ties: wider).
@@ -460,7 +473,7 @@ hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
   const int groups = a.groups, rpg = a.rpg;
   if (groups > 256) return launch_select_t<T, 16, 8>(a, st);
   if (ews != nullptr && (a.tokens + 31) / 32 < compute_units()) return select_split<T>(a, ews, st);
-  if (std::is_same<T, bf16_t>::value) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
     // direct-to-LDS: up to 256 sampled rows in one super-chunk of 4 fragments
     // per wave; beyond, super-chunks of 128 rows, whose small stages let two
     // workgroups share a CU (more waves issuing loads; measured faster than
@@ -470,16 +483,18 @@ hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
     // (measured faster there; at 64 tokens per CU slower, since a CU then
     // holds one workgroup instead of two)
     if (groups * rpg > 128 && groups * rpg <= 256) return launch_select_t<T, 32, 4>(a, st);
+    // (128-token blocks run eight waves: one workgroup per CU, two waves per SIMD)
     if (a.tokens >= 128 * compute_units() &&
         SelCfg<T, 128, 2>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
-      return launch_select_t<T, 128, 2>(a, st);
+      return launch_select_t<T, 128, 2, kSel128Waves>(a, st);
     return launch_select_t<T, 32, 2>(a, st);
-  }
-  switch (pick_fnw(groups * rpg)) {
-    case 2: return launch_select_t<T, 32, 2>(a, st);
-    case 4: return launch_select_t<T, 32, 4>(a, st);
-    case 6: return launch_select_t<T, 32, 6>(a, st);
-    default: return launch_select_t<T, 32, 8>(a, st);
+  } else {
+    switch (pick_fnw(groups * rpg)) {
+      case 2: return launch_select_t<T, 32, 2>(a, st);
+      case 4: return launch_select_t<T, 32, 4>(a, st);
+      case 6: return launch_select_t<T, 32, 6>(a, st);
+      default: return launch_select_t<T, 32, 8>(a, st);
+    }
   }
 }
 
