@@ -34,26 +34,31 @@ constexpr int kSel128Waves = 8;
 // into K-row tiles (64 K per stage, DMA_NS stages); other cases stage through
 // registers.  Every workgroup streams all sampled rows once per K step, so a
 // larger BM divides that traffic over more tokens.
-// NW = 8 (128-token blocks): the four column groups each split their rows in
-// two halves, two waves per SIMD.
+// Eight waves (NW = 8): 128-token blocks keep four column groups and split
+// their rows in two halves; 32-token blocks take eight column groups (the x
+// tile's four load instructions then come from four waves, the other four
+// issue an empty load into a sink so that every wave counts the same loads).
 template <typename T, int BM, int FNW, bool USE_DMA = true, int NW = 4>
 struct SelCfg {
   static constexpr int NTH = 64 * NW;
-  static constexpr int NSC = 4 * FNW * 16;  // sampled rows per super-chunk
+  static constexpr int CG = NW == 8 && BM == 32 ? 8 : 4;  // column groups
+  static constexpr int RH = NW / CG;                        // row parts
+  static constexpr int NSC = CG * FNW * 16;  // sampled rows per super-chunk
   static constexpr int FM = BM / 16;
-  static constexpr int RH = NW / 4;         // row halves
-  static constexpr int FMW = FM / RH;       // row fragments per wave
+  static constexpr int FMW = FM / RH;        // row fragments per wave
   static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && (BM == 32 || BM == 128) && FNW <= 4;
-  static constexpr int IA = BM / (8 * NW);  // x rows loads per lane per stage (8 rows each)
+  static constexpr int IA = BM >= 8 * NW ? BM / (8 * NW) : 1;  // x load instructions per lane per stage
   static constexpr int IB = NSC / (8 * NW);
-  static_assert(NW == 4 || (DMA && IA * 8 * NW == BM && IB * 8 * NW == NSC), "eight waves: whole DMA loads");
+  static constexpr int SINK = BM < 8 * NW ? 1024 : 0;  // where the empty x loads land
+  static_assert(NW == 4 || (DMA && IB * 8 * NW == NSC && (IA * 8 * NW == BM || (IA == 1 && BM % 8 == 0))),
+                "eight waves: whole DMA loads");
   static constexpr int PA = Plane<BM>::BYTES;
   static constexpr int PB = Plane<NSC>::BYTES;
   static constexpr int A_BYTES = DMA ? BM * 128 : KC * PA;
   static constexpr int B_BYTES = DMA ? NSC * 128 : KC * PB;
-  static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES) <= 112 * 1024 ? 3 : 2;
+  static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES + SINK) <= 112 * 1024 ? 3 : 2;
   static constexpr int DMA_L = IA + IB;  // loads per lane per stage
-  static constexpr int STAGES = (DMA ? DMA_NS : 2) * (A_BYTES + B_BYTES);
+  static constexpr int STAGES = (DMA ? DMA_NS : 2) * (A_BYTES + B_BYTES + SINK);
   static constexpr int S_STRIDE = NSC + 1;  // odd float stride: conflict-free column walks
   static constexpr int S_BYTES = BM * S_STRIDE * 4;
   static constexpr int FIXED = STAGES > S_BYTES ? STAGES : S_BYTES;
@@ -230,14 +235,14 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const T* __restrict__ x
   }
   for (int i = tid; i < groups; i += C::NTH) cnt[i] = 0;
 
-  // wave -> column group cg (FNW fragments interleaved over the four groups)
-  // and row half rh (eight waves)
-  const int cg = wave & 3, rh = wave >> 2;
+  // wave -> column group cg (FNW fragments interleaved over the CG groups)
+  // and row part rh
+  const int cg = wave % C::CG, rh = wave / C::CG;
   int arow[C::FMW], brow[FNW];
 #pragma unroll
   for (int i = 0; i < C::FMW; ++i) arow[i] = (rh * C::FMW + i) * 16 + (lane & 15);
 #pragma unroll
-  for (int j = 0; j < FNW; ++j) brow[j] = (j * 4 + cg) * 16 + (lane & 15);
+  for (int j = 0; j < FNW; ++j) brow[j] = (j * C::CG + cg) * 16 + (lane & 15);
 
   if constexpr (C::DMA) {
     ESG_LDS char* st0 = (ESG_LDS char*)smem;
@@ -248,8 +253,8 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const T* __restrict__ x
     uint32_t voffA[C::IA];
 #pragma unroll
     for (int i = 0; i < C::IA; ++i) {
-      const int xr = (w * C::IA + i) * 8 + (lane >> 3);
-      voffA[i] = t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
+      const int xr = (w * C::IA + i) * 8 + (lane >> 3);  // rows >= BM: an empty load into the sink
+      voffA[i] = xr < BM && t0 + xr < tokens ? (uint32_t)(t0 + xr) * kbytes + c_lane * 16 : kOOB;
     }
     constexpr int IB = C::IB;
     for (int n0 = c_begin; n0 < ncols; n0 += C::NSC) {
@@ -264,8 +269,11 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const T* __restrict__ x
         const uint32_t kb = (uint32_t)kt * 128;
         const bool kin = kb + c_lane * 16 < (uint32_t)kbytes;
 #pragma unroll
-        for (int i = 0; i < C::IA; ++i)
-          dma16(rx, st + (w * C::IA + i) * 1024, (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
+        for (int i = 0; i < C::IA; ++i) {
+          const bool real = (w * C::IA + i) * 8 < BM;  // wave-uniform
+          dma16(rx, real ? st + (w * C::IA + i) * 1024 : st + C::A_BYTES + C::B_BYTES,
+                (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
+        }
 #pragma unroll
         for (int i = 0; i < IB; ++i)
           dma16(rwg, st + C::A_BYTES + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const T* __restrict__ x
       };
       wait_lgkm0();
       barrier();  // the previous super-chunk's S reads (S aliases the stages) are done
-      constexpr int SB = C::A_BYTES + C::B_BYTES;
+      constexpr int SB = C::A_BYTES + C::B_BYTES + C::SINK;
       tiles::kloop<C::DMA_NS, C::DMA_L, 0>((kbytes + 127) / 128, st0, st0 + SB, st0 + 2 * SB, issue, compute);
       wait_lgkm0();
       barrier();  // every wave is done with the stages before S overwrites them
@@ -482,12 +490,14 @@ hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
     // once per K step, and the larger block divides that over more tokens
     // (measured faster there; at 64 tokens per CU slower, since a CU then
     // holds one workgroup instead of two)
-    if (groups * rpg > 128 && groups * rpg <= 256) return launch_select_t<T, 32, 4>(a, st);
+    // (one 256-row super-chunk: eight waves in eight column groups, two waves
+    // per SIMD at one workgroup per CU; 128M select 19 -> 16 us)
+    if (groups * rpg > 128 && groups * rpg <= 256) return launch_select_t<T, 32, 2, 8>(a, st);
     // (128-token blocks run eight waves: one workgroup per CU, two waves per SIMD)
     if (a.tokens >= 128 * compute_units() &&
         SelCfg<T, 128, 2>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
       return launch_select_t<T, 128, 2, kSel128Waves>(a, st);
-    return launch_select_t<T, 32, 2>(a, st);
+    return launch_select_t<T, 32, 2>(a, st);  // (eight waves measured slower here: 16 waves per CU)
   } else {
     switch (pick_fnw(groups * rpg)) {
       case 2: return launch_select_t<T, 32, 2>(a, st);
