@@ -457,6 +457,7 @@ hipError_t select_split(const SelArgs& a, float* ews, hipStream_t st) {
   hipError_t e;
   if (std::is_same<T, bf16_t>::value)
     e = cols > 128 && cols <= 256 ? launch_select_t<T, 32, 4>(a, st, gpc, ews)
+        : cols <= 64              ? launch_select_t<T, 32, 1>(a, st, gpc, ews)  // fewer empty loads
                                   : launch_select_t<T, 32, 2>(a, st, gpc, ews);
   else
     switch (pick_fnw(cols)) {
