@@ -48,7 +48,7 @@ struct Layout {
   int mt = 0;            // maximum tiles
   size_t rows = 0;       // padded positions
   size_t offsets = 0, tile_off = 0, tile_group = 0, ptoken = 0, pinv = 0, hg = 0, hu = 0, saved = 0;
-  size_t f_bucket = 0, f_part = 0, f_route = 0, fwd = 0;
+  size_t f_bucket = 0, f_part = 0, f_route = 0, f_act = 0, fwd = 0;
   size_t b_dg = 0, b_du = 0, b_act = 0, b_part = 0, bwd = 0;
 };
 
@@ -73,6 +73,7 @@ Layout make_layout(const FfnShape& s) {
   L.f_bucket = o;   o = align256(o + bucket_scratch_bytes(s.tokens, G));
   L.f_part = o;     o = align256(o + part_bytes);
   L.f_route = o;    o = align256(o + L.hg);  // the routing arrays of `saved`, for saved = NULL (inference)
+  L.f_act = o;      o = align256(o + (fwd_split(s, L.mt) ? act_bytes : 0));  // `a` tiles of a split forward
   L.fwd = o;
   o = 0;
   L.b_dg = o;       o = align256(o + act_bytes);
@@ -281,7 +282,7 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
   char* hu = train ? at<char>(saved, L.hu) : nullptr;
   e = bf16_pipelined(s, L.mt)
           ? launch_fwd2(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, hg, hu,
-                        at<char>(scratch, L.f_part), stream_h)
+                        at<char>(scratch, L.f_part), at<char>(scratch, L.f_act), stream_h)
           : launch_fwd_grouped(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, hg, hu,
                                at<char>(scratch, L.f_part), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;

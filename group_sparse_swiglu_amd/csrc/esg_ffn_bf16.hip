@@ -17,6 +17,8 @@
 // Orientation: the MFMA M side is the neuron or d index, so each lane's four
 // accumulator rows are four consecutive neurons / d values and every epilogue
 // store is one 8-byte write.
+#include <algorithm>
+
 #include "esg_internal.hpp"
 #include "esg_tiles.hpp"
 
@@ -50,13 +52,22 @@ constexpr int dw_subtiles() {
 }
 
 // NW: waves (fwd_waves<GSB>(); 8 for 64-neuron blocks when the grid leaves each
-// workgroup alone on its CU)
-template <int GSB, int CPOL, int NW>
+// workgroup alone on its CU).
+// MODE 0: both phases.  With few tiles the two phases run as two launches, so
+// that phase 2 (one d-block after another, a third of the fused kernel's time)
+// spreads over more CUs than there are tiles:
+//   MODE 1: phase 1 and the epilogue, then the tile's `a` (the LDS K-row tile,
+//           ACT_BYTES) copied to act_buf[blockIdx.y][tile];
+//   MODE 2: `a` copied back into LDS, then phase 2 over the d-blocks of range
+//           blockIdx.z (gridDim.z ranges of equal length).
+// Phase 2 runs the same MFMA sequence on the same bf16 `a` in every mode, so
+// the partial rows are bitwise those of MODE 0.
+template <int GSB, int CPOL, int NW, int MODE = 0>
 __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
     const bf16_t* __restrict__ wd, int tokens, int d, int F, int gs, const int32_t* __restrict__ tile_group,
     const int32_t* __restrict__ ptoken, uint32_t rows_total, bf16_t* __restrict__ hg_saved,
-    bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials) {
+    bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials, bf16_t* __restrict__ act_buf) {
   using C = Fwd2<GSB, NW>;
   constexpr int NS = stages_for<GSB>();
   // with two stages a third W_down buffer follows them
@@ -84,18 +95,25 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   using RS = RowStore<DB, C::NTH>;
   const uint32_t psub = (uint32_t)s * rows_total * d * 2;
   uint32_t row_off[RS::IT];
+  if constexpr (MODE != 1) {
 #pragma unroll
-  for (int it = 0; it < RS::IT; ++it) {
-    const int r = RS::row(it, threadIdx.x);
-    row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
+    for (int it = 0; it < RS::IT; ++it) {
+      const int r = RS::row(it, threadIdx.x);
+      row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
+    }
   }
+  ESG_LDS char* act = st0;
+  u32x4_t* const act_g = (u32x4_t*)((char*)act_buf + ((size_t)s * gridDim.x + tile) * C::ACT_BYTES);
+  if constexpr (MODE == 2) {
+    // the tile's `a` from the first launch; the ring's first barrier publishes it
+    for (int i = threadIdx.x; i < C::ACT_BYTES / 16; i += C::NTH) *(ESG_LDS u32x4_t*)(act + i * 16) = act_g[i];
+  } else {
   f32x4 acc[2 * C::FMP][C::FN];
   gateup_tile<GSB, NS, NW>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, acc);
   wait_lgkm0();
   barrier();  // every wave is done with the stages
 
   // ---- epilogue: hg, hu saved; a = SiLU(hg)*hu -> LDS K-row tile [position][neuron] ----
-  ESG_LDS char* act = st0;
   const uint32_t sv_bytes = gridDim.y * rows_total * GSB * 2;
   const rsrc_t rsv_g = make_rsrc(hg_saved, sv_bytes);
   const rsrc_t rsv_u = make_rsrc(hu_saved, sv_bytes);
@@ -122,8 +140,20 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
                  pack_bf16x2(a[2], a[3]));
     }
   }
+  if constexpr (MODE == 1) {
+    wait_lgkm0();
+    barrier();  // the whole tile is in LDS
+    for (int i = threadIdx.x; i < C::ACT_BYTES / 16; i += C::NTH) act_g[i] = *(const ESG_LDS u32x4_t*)(act + i * 16);
+    return;
+  }
+  }  // MODE != 2
 
   // ---- phase 2: P^T = W_down[d-block, nb0 .. nb0+GSB) . a^T ----
+  // d-blocks [blk0, blk0 + nblk): all of them, or range blockIdx.z (MODE 2)
+  const int nblk_all = (d + DB - 1) / DB;
+  const int per = MODE == 2 ? (nblk_all + gridDim.z - 1) / gridDim.z : nblk_all;
+  const int blk0 = MODE == 2 ? blockIdx.z * per : 0;
+  const int nblk = min(per, nblk_all - blk0);
   const int c_lane = (lane & 7) ^ (lane >> 3);
   const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
   const rsrc_t rp = make_rsrc(partials, gridDim.y * rows_total * (uint32_t)d * 2);
@@ -134,7 +164,7 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
     voffW[i] = (uint32_t)r * F * 2 + (uint32_t)nb0 * 2 + c_lane * 16;
   }
   auto issueW = [&](ESG_LDS char* st, int blk) __attribute__((always_inline)) {
-    const int db0 = blk * DB;
+    const int db0 = (blk0 + blk) * DB;
 #pragma unroll
     for (int sb = 0; sb < C::KSUB; ++sb)
 #pragma unroll
@@ -179,14 +209,14 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
       }
     wait_lgkm0();
     barrier();  // the whole block is staged
-    RS::template flush<CPOL>(out0, out1, rp, row_off, blk * DB, d);
+    RS::template flush<CPOL>(out0, out1, rp, row_off, (blk0 + blk) * DB, d);
   };
   // the stages after st0 are free (the barrier above); the first step's wait
   // covers the epilogue stores (they precede every W_down load), and its
   // barrier publishes the act tile.  The two W_down buffers: st1 and the last
   // stage (three stages) or the region after st1 (two)
   ESG_LDS char* const wbuf[2] = {st1, NS == 2 ? st1 + C::STAGE : st[NS - 1]};
-  kloop_ring<2, C::KSUB * C::IW2, C::STORES2>((d + DB - 1) / DB, wbuf, issueW, compute2);
+  kloop_ring<2, C::KSUB * C::IW2, C::STORES2>(nblk, wbuf, issueW, compute2);
 }
 
 // ===========================================================================
@@ -389,9 +419,26 @@ bool partials_nontemporal(const FfnShape& s, int ntiles_max) {
 template <int GSB>
 hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
                   const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg, void* hu,
-                  void* partials, hipStream_t stream) {
+                  void* partials, void* act, hipStream_t stream) {
   LaunchTimer timer("fwd_grouped", stream);
   constexpr int NW = fwd_waves<GSB>();
+  if constexpr (GSB == 64) {
+    if (act != nullptr) {  // fwd_split: phase 1 alone on its CUs, then phase 2 over d-block ranges
+      const int tiles = ntiles_max * s.nsub(), nblk = (s.d_model + DB - 1) / DB;
+      int nz = std::max(1, std::min(nblk, 2 * compute_units() / std::max(1, tiles)));  // two per CU
+      const int per = (nblk + nz - 1) / nz;
+      nz = (nblk + per - 1) / per;  // no empty range; the kernel derives the same `per`
+      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, 8, 1>), dim3(ntiles_max, s.nsub()), dim3(64 * 8), 0, stream,
+                         (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
+                         s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
+                         (bf16_t*)hu, (bf16_t*)partials, (bf16_t*)act);
+      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, NW, 2>), dim3(ntiles_max, s.nsub(), nz), dim3(64 * NW), 0, stream,
+                         (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
+                         s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
+                         (bf16_t*)hu, (bf16_t*)partials, (bf16_t*)act);
+      return hipGetLastError();
+    }
+  }
   // a grid of at most one workgroup per CU: eight waves issue the loads
   const bool alone = NW == 4 && (long long)ntiles_max * s.nsub() <= compute_units();
   auto kern = partials_nontemporal(s, ntiles_max) ? fwd2_kernel<GSB, kCpolNontemporal, NW>
@@ -399,7 +446,7 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
   hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * (alone ? 8 : NW)), 0, stream, (const bf16_t*)x,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
-                     (bf16_t*)partials);
+                     (bf16_t*)partials, nullptr);
   return hipGetLastError();
 }
 
@@ -441,14 +488,20 @@ bool bf16_pipelined(const FfnShape& s, int ntiles_max) {
          (unsigned long long)s.nsub() * rows * s.gsb() * 2 < lim;
 }
 
+bool fwd_split(const FfnShape& s, int ntiles_max) {
+  return bf16_pipelined(s, ntiles_max) && s.gsb() == 64 && (long long)ntiles_max * s.nsub() <= kFwdSplitTiles &&
+         !partials_nontemporal(s, ntiles_max);
+}
+
 hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
                        const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg_saved,
-                       void* hu_saved, void* partials, hipStream_t stream) {
+                       void* hu_saved, void* partials, void* act, hipStream_t stream) {
   if (ntiles_max == 0) return hipSuccess;
+  if (!fwd_split(s, ntiles_max)) act = nullptr;
   return s.gsb() == 64 ? fwd2_t<64>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, partials,
-                                    stream)
+                                    act, stream)
                        : fwd2_t<128>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, partials,
-                                     stream);
+                                     act, stream);
 }
 
 hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const void* wu, const void* wd,
