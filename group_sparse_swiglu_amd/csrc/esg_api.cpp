@@ -73,7 +73,7 @@ Layout make_layout(const FfnShape& s) {
   L.f_bucket = o;   o = align256(o + bucket_scratch_bytes(s.tokens, G));
   L.f_part = o;     o = align256(o + part_bytes);
   L.f_route = o;    o = align256(o + L.hg);  // the routing arrays of `saved`, for saved = NULL (inference)
-  L.f_act = o;      o = align256(o + (fwd_split(s, L.mt) ? act_bytes : 0));  // `a` tiles of a split forward
+  L.f_act = o;      o = align256(o + fwd_split_bytes(s, L.mt));  // [hg; hu] partials of a split forward
   L.fwd = o;
   o = 0;
   L.b_dg = o;       o = align256(o + act_bytes);

@@ -54,20 +54,22 @@ constexpr int dw_subtiles() {
 // NW: waves (fwd_waves<GSB>(); 8 for 64-neuron blocks when the grid leaves each
 // workgroup alone on its CU).
 // MODE 0: both phases.  With few tiles the two phases run as two launches, so
-// that phase 2 (one d-block after another, a third of the fused kernel's time)
-// spreads over more CUs than there are tiles:
-//   MODE 1: phase 1 and the epilogue, then the tile's `a` (the LDS K-row tile,
-//           ACT_BYTES) copied to act_buf[blockIdx.y][tile];
-//   MODE 2: `a` copied back into LDS, then phase 2 over the d-blocks of range
-//           blockIdx.z (gridDim.z ranges of equal length).
-// Phase 2 runs the same MFMA sequence on the same bf16 `a` in every mode, so
-// the partial rows are bitwise those of MODE 0.
+// that each spreads over more CUs than there are tiles:
+//   MODE 1: phase 1 over the K stages of range blockIdx.z (gridDim.z ranges of
+//           equal length), its fp32 [hg; hu] stored position-major
+//           [BM][2*GSB] in part_buf[blockIdx.y][tile][blockIdx.z];
+//   MODE 2: the kparts K ranges summed in range order, the epilogue (hg, hu
+//           saved by range 0 of the d-blocks), then phase 2 over the d-blocks
+//           of range blockIdx.z.
+// The sum over K ranges rounds differently from one accumulation over all of
+// K; every launch of a shape takes the same split, so results stay
+// reproducible.
 template <int GSB, int CPOL, int NW, int MODE = 0>
 __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
     const bf16_t* __restrict__ wd, int tokens, int d, int F, int gs, const int32_t* __restrict__ tile_group,
     const int32_t* __restrict__ ptoken, uint32_t rows_total, bf16_t* __restrict__ hg_saved,
-    bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials, bf16_t* __restrict__ act_buf) {
+    bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials, float* __restrict__ part_buf, int kparts) {
   using C = Fwd2<GSB, NW>;
   constexpr int NS = stages_for<GSB>();
   // with two stages a third W_down buffer follows them
@@ -103,21 +105,58 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
     }
   }
   ESG_LDS char* act = st0;
-  u32x4_t* const act_g = (u32x4_t*)((char*)act_buf + ((size_t)s * gridDim.x + tile) * C::ACT_BYTES);
+  const uint32_t sv_bytes = gridDim.y * rows_total * GSB * 2;
+  const rsrc_t rsv_g = make_rsrc(hg_saved, sv_bytes);
+  const rsrc_t rsv_u = make_rsrc(hu_saved, sv_bytes);
+  const uint32_t sub_off = (uint32_t)s * rows_total * GSB * 2;
+  constexpr int PART = BM * 2 * GSB;  // floats of one K range's [hg; hu]
+  float* const part = part_buf + ((size_t)s * gridDim.x + tile) * kFwdSplitK * PART;
   if constexpr (MODE == 2) {
-    // the tile's `a` from the first launch; the ring's first barrier publishes it
-    for (int i = threadIdx.x; i < C::ACT_BYTES / 16; i += C::NTH) *(ESG_LDS u32x4_t*)(act + i * 16) = act_g[i];
+    // ---- K ranges summed, then the epilogue, 4 neurons of one position per step;
+    // the ring's first barrier publishes the act tile ----
+    for (int i = threadIdx.x; i < BM * GSB / 4; i += C::NTH) {
+      const int r = i / (GSB / 4), n = (i % (GSB / 4)) * 4;
+      f32x4 g4 = *(const f32x4*)(part + r * 2 * GSB + n);
+      f32x4 u4 = *(const f32x4*)(part + r * 2 * GSB + GSB + n);
+      for (int z = 1; z < kparts; ++z) {
+        g4 += *(const f32x4*)(part + (size_t)z * PART + r * 2 * GSB + n);
+        u4 += *(const f32x4*)(part + (size_t)z * PART + r * 2 * GSB + GSB + n);
+      }
+      float hg[4], hu[4], a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hg[e] = g4[e];
+        hu[e] = u4[e];
+        a[e] = hg[e] * sigmoid_f(hg[e]) * hu[e];
+      }
+      if (hg_saved != nullptr && blockIdx.z == 0) {
+        const uint32_t so = sub_off + ((prow0 + r) * GSB + n) * 2;
+        store8(rsv_g, so, hg);
+        store8(rsv_u, so, hu);
+      }
+      lds_write8(act + (n >> 6) * BM * 128 + krow_off(r, (n & 63) >> 3) + (n & 7) * 2, pack_bf16x2(a[0], a[1]),
+                 pack_bf16x2(a[2], a[3]));
+    }
   } else {
   f32x4 acc[2 * C::FMP][C::FN];
+  if constexpr (MODE == 1) {
+    const int nkt_all = (d + 63) / 64, per = (nkt_all + gridDim.z - 1) / gridDim.z;
+    const int kt0 = blockIdx.z * per;
+    gateup_tile<GSB, NS, NW>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, acc, kt0, min(per, nkt_all - kt0));
+    float* const mine = part + (size_t)blockIdx.z * PART;
+#pragma unroll
+    for (int p = 0; p < 2 * C::FMP; ++p) {
+      const int n = (p < C::FMP ? 0 : GSB) + wm * (GSB / C::WM) + (p % C::FMP) * 16 + (lane >> 4) * 4;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) *(f32x4*)(mine + brow[j] * 2 * GSB + n) = acc[p][j];
+    }
+    return;
+  }
   gateup_tile<GSB, NS, NW>(x, wg, wu, tokens, d, F, nb0, ptoken, prow0, st, acc);
   wait_lgkm0();
   barrier();  // every wave is done with the stages
 
   // ---- epilogue: hg, hu saved; a = SiLU(hg)*hu -> LDS K-row tile [position][neuron] ----
-  const uint32_t sv_bytes = gridDim.y * rows_total * GSB * 2;
-  const rsrc_t rsv_g = make_rsrc(hg_saved, sv_bytes);
-  const rsrc_t rsv_u = make_rsrc(hu_saved, sv_bytes);
-  const uint32_t sub_off = (uint32_t)s * rows_total * GSB * 2;
 #pragma unroll
   for (int p = 0; p < C::FMP; ++p) {
     const int n = wm * (GSB / C::WM) + p * 16 + (lane >> 4) * 4;  // 4 consecutive neurons
@@ -140,13 +179,7 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
                  pack_bf16x2(a[2], a[3]));
     }
   }
-  if constexpr (MODE == 1) {
-    wait_lgkm0();
-    barrier();  // the whole tile is in LDS
-    for (int i = threadIdx.x; i < C::ACT_BYTES / 16; i += C::NTH) act_g[i] = *(const ESG_LDS u32x4_t*)(act + i * 16);
-    return;
-  }
-  }  // MODE != 2
+  }  // MODE 0
 
   // ---- phase 2: P^T = W_down[d-block, nb0 .. nb0+GSB) . a^T ----
   // d-blocks [blk0, blk0 + nblk): all of them, or range blockIdx.z (MODE 2)
@@ -423,19 +456,24 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
   LaunchTimer timer("fwd_grouped", stream);
   constexpr int NW = fwd_waves<GSB>();
   if constexpr (GSB == 64) {
-    if (act != nullptr) {  // fwd_split: phase 1 alone on its CUs, then phase 2 over d-block ranges
-      const int tiles = ntiles_max * s.nsub(), nblk = (s.d_model + DB - 1) / DB;
-      int nz = std::max(1, std::min(nblk, 2 * compute_units() / std::max(1, tiles)));  // two per CU
-      const int per = (nblk + nz - 1) / nz;
-      nz = (nblk + per - 1) / per;  // no empty range; the kernel derives the same `per`
-      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, 8, 1>), dim3(ntiles_max, s.nsub()), dim3(64 * 8), 0, stream,
+    if (act != nullptr) {  // fwd_split: phase 1 over K ranges, then phase 2 over d-block ranges
+      const int tiles = std::max(1, ntiles_max * s.nsub());
+      // ranges of equal length, none empty (the kernels derive the same length)
+      auto ranges = [](int n, int want) {
+        want = std::max(1, std::min(n, want));
+        const int per = (n + want - 1) / want;
+        return (n + per - 1) / per;
+      };
+      const int kz = ranges((s.d_model + 63) / 64, std::min(kFwdSplitK, compute_units() / tiles));  // one per CU
+      const int nz = ranges((s.d_model + DB - 1) / DB, 2 * compute_units() / tiles);              // two per CU
+      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, 8, 1>), dim3(ntiles_max, s.nsub(), kz), dim3(64 * 8), 0, stream,
                          (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
                          s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
-                         (bf16_t*)hu, (bf16_t*)partials, (bf16_t*)act);
+                         (bf16_t*)hu, (bf16_t*)partials, (float*)act, kz);
       hipLaunchKernelGGL((fwd2_kernel<GSB, 0, NW, 2>), dim3(ntiles_max, s.nsub(), nz), dim3(64 * NW), 0, stream,
                          (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
                          s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
-                         (bf16_t*)hu, (bf16_t*)partials, (bf16_t*)act);
+                         (bf16_t*)hu, (bf16_t*)partials, (float*)act, kz);
       return hipGetLastError();
     }
   }
@@ -446,7 +484,7 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
   hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * (alone ? 8 : NW)), 0, stream, (const bf16_t*)x,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
-                     (bf16_t*)partials, nullptr);
+                     (bf16_t*)partials, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -85,13 +85,18 @@ hipError_t launch_bwd_dw(const FfnShape& s, const void* x, const void* dy, const
 // Its saved activations are row-major [sub][pos][gsb]; the generic path above
 // uses [sub][pos/EPC][gsb][EPC].  Forward and backward pick the same path.
 bool bf16_pipelined(const FfnShape& s, int ntiles_max);
-// The bf16 forward as two launches (phase 1; phase 2 over d-block ranges) when
-// the tiles of 64-neuron blocks number at most kFwdSplitTiles: the fused kernel
-// would leave most CUs idle.  A shape rule (no device query), so the forward
-// scratch can hold the `[nsub][rows][gsb]` bf16 `a` tiles exactly when needed.
+// The bf16 forward as two launches (phase 1 over up to kFwdSplitK K ranges;
+// phase 2 over d-block ranges) when the tiles of 64-neuron blocks number at
+// most kFwdSplitTiles: the one-launch kernel would leave most CUs idle.  A
+// shape rule (no device query), so the forward scratch holds the fp32 [hg; hu]
+// partials, fwd_split_bytes, exactly when needed.
 constexpr int kFwdSplitTiles = 128;
+constexpr int kFwdSplitK = 4;
 bool fwd_split(const FfnShape& s, int ntiles_max);
-// act: the `a` tiles for fwd_split shapes (ignored otherwise)
+inline size_t fwd_split_bytes(const FfnShape& s, int ntiles_max) {
+  return fwd_split(s, ntiles_max) ? (size_t)s.nsub() * ntiles_max * kFwdSplitK * kTileRows * 2 * s.gsb() * 4 : 0;
+}
+// act: the fwd_split_bytes partials for fwd_split shapes (ignored otherwise)
 hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
                        const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg_saved,
                        void* hu_saved, void* partials, void* act, hipStream_t stream);

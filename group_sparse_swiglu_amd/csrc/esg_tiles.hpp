@@ -163,12 +163,14 @@ struct Fwd2 {
 // rows, then up rows) against the 128 bucket positions from prow0, whose token
 // ids come from ptoken (-1 = padding, reads zeros).  K = d in 64-wide stages.
 // acc[p][j] (p < FMP: gate, p >= FMP: up) follows the wave mapping below.
+// kt0, nkt: the K stages [kt0, kt0 + nkt) only (nkt < 0: all of K).
 template <int GSB, int NS, int NW = 4>
 __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
                                             const bf16_t* __restrict__ wu, int tokens, int d, int F, int nb0,
                                             const int32_t* __restrict__ ptoken, uint32_t prow0,
                                             ESG_LDS char* const (&st)[NS],
-                                            f32x4 (&acc)[2 * Fwd2<GSB, NW>::FMP][Fwd2<GSB, NW>::FN]) {
+                                            f32x4 (&acc)[2 * Fwd2<GSB, NW>::FMP][Fwd2<GSB, NW>::FN],
+                                            int kt0 = 0, int nkt = -1) {
   using C = Fwd2<GSB, NW>;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t kbytes = (uint32_t)d * 2;
@@ -193,7 +195,7 @@ __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const 
     voffB[i] = t >= 0 ? (uint32_t)t * kbytes + c_lane * 16 : kOOB;
   }
   auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
-    const uint32_t kb = (uint32_t)kt * 128;
+    const uint32_t kb = (uint32_t)(kt0 + kt) * 128;
     const bool kin = kb + c_lane * 16 < kbytes;
 #pragma unroll
     for (int i = 0; i < C::IA; ++i) {
@@ -231,7 +233,7 @@ __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const 
         for (int j = 0; j < C::FN; ++j) mma_bf16(acc[i][j], a[i], b[j]);
     }
   };
-  kloop_ring<NS, C::L, 0>((int)((kbytes + 127) / 128), st, issue, compute);
+  kloop_ring<NS, C::L, 0>(nkt < 0 ? (int)((kbytes + 127) / 128) : nkt, st, issue, compute);
 }
 
 // ===========================================================================
