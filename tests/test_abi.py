@@ -77,6 +77,24 @@ def test_workspace_sizes_and_shape_rules():
     assert _sizes(256, 2064, 512, 32, 16, E.ESG_BF16, 1)[0] == 2       # d_model above 2048
 
 
+def test_forward_scratch_holds_split_partials_exactly_under_the_tile_limit():
+    # 16 groups of 64, k = 2, d = 80: tiles are bounded by floor((T*k + 16*127)/128),
+    # 128 at 7239 tokens (two-launch forward: fp32 [hg; hu] of up to 4 K ranges,
+    # 4 * 128 * 128 * 4 bytes per tile) and 129 at 7240 (one launch, no such
+    # buffer), so the scratch shrinks across the limit by about 32 MB.
+    st0, _, fw_split, _ = _sizes(7239, 80, 1024, 64, 2, E.ESG_BF16, 0)
+    st1, _, fw_one, _ = _sizes(7240, 80, 1024, 64, 2, E.ESG_BF16, 0)
+    assert st0 == 0 and st1 == 0
+    partial_bytes = 128 * 4 * 128 * 128 * 4
+    assert partial_bytes - 4096 <= fw_split - fw_one + 128 * 80 * 2 <= partial_bytes + 4096
+    # one tile below the limit both sizes hold the buffer
+    assert _sizes(7238, 80, 1024, 64, 2, E.ESG_BF16, 0)[2] <= fw_split
+    # fp32 launches never split
+    _, _, f32_a, _ = _sizes(7239, 80, 1024, 64, 2, E.ESG_F32, 0)
+    _, _, f32_b, _ = _sizes(7240, 80, 1024, 64, 2, E.ESG_F32, 0)
+    assert f32_a <= f32_b < f32_a + 64 * 1024
+
+
 def test_entry_points_reject_bad_arguments_before_launch():
     lib = E.lib()
     # NULL weights / misaligned pointers / bad shapes return before any HIP call

@@ -129,14 +129,14 @@ def test_ffn_edge_shapes(case):
 
 
 # The bf16 forward runs as two launches (phase 1 over K ranges, phase 2 over
-# d-block ranges) while the tile bound ceil((T*k + G*127)/128) of 64-neuron
-# blocks is at most 128, else as one.  With G = 16, k = 2: 7176 tokens give 128
-# tiles, 7177 give 129; d = 80 leaves a ragged K stage and d-block.
-@pytest.mark.parametrize("tokens", [7176, 7177])
+# d-block ranges) while the tile bound floor((T*k + G*127)/128) of 64-neuron
+# blocks is at most 128, else as one.  With G = 16, k = 2: 7239 tokens give 128
+# tiles, 7240 give 129; d = 80 leaves a ragged K stage and d-block.
+@pytest.mark.parametrize("tokens", [7239, 7240])
 def test_ffn_forward_split_boundary(tokens):
     require_gpu()
     G, gs, k, d = 16, 64, 2, 80
-    assert -(-(tokens * k + G * 127) // 128) == (128 if tokens == 7176 else 129)
+    assert (tokens * k + G * 127) // 128 == (128 if tokens == 7239 else 129)
     note(f"split boundary T={tokens} d={d} G={G}x{gs} k={k}")
     inp = inputs(tokens, d, G * gs, gs, "bf16", seed=tokens, bias=True, spg=16)
     _full_compare(inp, _oracle_routing(inp, k), "bf16")
