@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   const rsrc_t rsv_u = make_rsrc(hu_saved, sv_bytes);
   const uint32_t sub_off = (uint32_t)s * rows_total * GSB * 2;
   constexpr int PART = BM * 2 * GSB;  // floats of one K range's [hg; hu]
-  float* const part = part_buf + ((size_t)s * gridDim.x + tile) * kFwdSplitK * PART;
+  float* const part = MODE == 0 ? nullptr : part_buf + ((size_t)s * gridDim.x + tile) * kFwdSplitK * PART;
   if constexpr (MODE == 2) {
     // ---- K ranges summed, then the epilogue, 4 neurons of one position per step;
     // the ring's first barrier publishes the act tile ----
