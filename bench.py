@@ -15,7 +15,10 @@ of eagerly launched steps (the headline steps replay one captured HIP graph).
 the CPU oracle timed on this host's cores on a bounded slice of the same
 workload.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload s128m_bf16]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload s1p3b_bf16]
+    python bench.py --k-sweep          # tokens/s against the active fraction k*gs/d_ff
+    python bench.py --skew             # 4 groups made hot by the bias
+    python bench.py --peak             # measured bf16 MFMA and GEMM rates
 """
 from __future__ import annotations
 
@@ -42,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="s128m_bf16")
+    ap.add_argument("--workload", default="s1p3b_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel HIP events")
@@ -56,9 +59,20 @@ def parse():
                     help="time the LeakyReLU(0.5)^2 MLP fwd+bwd on an MLP workload (leaky_mlp_d512) instead")
     ap.add_argument("--mhffn", default=None, metavar="WORKLOAD",
                     help="time the FlashFFN multi-head sub-network core (mhffn1p3b) instead")
+    ap.add_argument("--k-sweep", default=None, nargs="?", const="1,4,8,11,22,43", metavar="KS",
+                    help="time the step of --workload's shape for each k in KS (comma list)")
+    ap.add_argument("--skew", action="store_true",
+                    help="the load-balance bias makes 4 groups hot (+10 on groups 0, G/4, G/2, 3G/4)")
+    ap.add_argument("--peak", action="store_true", help="only measure the bf16 MFMA probe and a bf16 GEMM")
+    ap.add_argument("--no-peak-probe", action="store_true", help="skip the MFMA probe in the main line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (reference for the HBM counters)")
     return ap.parse_args()
+
+
+def dataclasses_replace(obj, **kw):
+    import dataclasses
+    return dataclasses.replace(obj, **kw)
 
 
 def kernel_source_digest(kernel: str) -> str:
@@ -104,47 +118,122 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
+def host_threads() -> int:
+    """The host cores this process may use; numpy's BLAS and torch are pinned
+    to that many threads for the CPU baseline."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        import torch
+        torch.set_num_threads(n)
+    except Exception:  # pragma: no cover
+        pass
+    return n
+
+
 def cpu_baseline(w, inp, seconds):
-    """The CPU oracle (as it stands) on consecutive token slices of the same
-    inputs, until `seconds` have passed: selection, forward, backward and the
-    bias update per slice."""
+    """The CPU oracle (as it stands) in float32, dense-masked, on consecutive
+    token slices of the same inputs until `seconds` have passed: selection,
+    forward, backward and the bias update per slice, with numpy's BLAS on all
+    the host cores this process may use."""
     import numpy as np
     from oracle import esg_oracle as O
+    cores = host_threads()
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 0) for p in threadpool_info()] or [0]) or os.cpu_count()
+        from threadpoolctl import threadpool_limits
+        limits = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        limits = None
     x, wg, wu, wd, dy, bias, sub = inp
-    f64 = lambda t: t.float().numpy().astype(np.float64)
-    W = (f64(wg), f64(wu), f64(wd))
+    f32 = lambda t: t.float().numpy()
+    W = (f32(wg), f32(wu), f32(wd))
     subn = None if sub is None else sub.numpy()
     biasn = None if bias is None else bias.numpy()
     G = w.groups
     slice_tokens = min(1024, w.tokens)
-    ema = np.full(G, w.k / G)
-    b = np.zeros(G) if biasn is None else biasn.astype(np.float64)
+    ema = np.full(G, w.k / G, dtype=np.float32)
+    b = np.zeros(G, dtype=np.float32) if biasn is None else biasn.astype(np.float32)
     done, t0 = 0, time.perf_counter()
     while True:
         s0 = done % w.tokens
-        xs, dys = f64(x[s0:s0 + slice_tokens]), f64(dy[s0:s0 + slice_tokens])
+        xs, dys = f32(x[s0:s0 + slice_tokens]), f32(dy[s0:s0 + slice_tokens])
         if w.dense:
             idx = np.tile(np.arange(G, dtype=np.int32), (xs.shape[0], 1))
         else:
-            idx, _ = O.grouped_topk_select(xs, W[0], w.group_size, w.k, subn, w.spg, b)
-        O.sparse_swiglu_forward(xs, *W, idx, w.group_size)
-        O.sparse_swiglu_backward(dys, xs, *W, idx, w.group_size)
+            idx, _ = O.grouped_topk_select(xs, W[0], w.group_size, w.k, subn, w.spg, b, dtype=np.float32)
+        O.sparse_swiglu_forward(xs, *W, idx, w.group_size, dtype=np.float32)
+        O.sparse_swiglu_backward(dys, xs, *W, idx, w.group_size, dtype=np.float32)
         if w.bias_update:
-            cur = O.frequency_from_counts(O.group_counts(idx, G), xs.shape[0])
-            b, ema = O.update_load_balance_bias(b, ema, cur, w.k / G, 1e-3, 0.5, 0.99)
+            cur = O.frequency_from_counts(O.group_counts(idx, G), xs.shape[0], np.float32)
+            b, ema = O.update_load_balance_bias(b, ema, cur, w.k / G, 1e-3, 0.5, 0.99, np.float32)
         done += xs.shape[0]
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    if limits is not None:
+        limits.restore_original_limits()
     return {"value": done / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} tokens of {w.name} in slices of {slice_tokens} (fp64 dense-masked "
+            "sample": f"{done} tokens of {w.name} in slices of {slice_tokens} (fp32 dense-masked "
                       f"{'fwd+bwd' if w.dense else 'select+fwd+bwd'}"
-                      f"{'+bias update' if w.bias_update else ''}), {el:.1f} s"}
+                      f"{'+bias update' if w.bias_update else ''}, numpy BLAS on {cores} threads), {el:.1f} s"}
+
+
+def mfma_probe_tflops(dev, reps: int = 5) -> float:
+    """Measured bf16 matrix-core rate: the library's probe kernel (eight
+    independent 16x16x32 MFMAs per wave and iteration, register operands, no
+    memory traffic) over 2048 workgroups of 4 waves, best of `reps` runs."""
+    import torch
+    import group_sparse_swiglu_amd as E
+    blocks, iters = 2048, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    E.mfma_rate_probe(blocks, 100, out)   # warm-up
+    torch.cuda.synchronize()
+    flops = float(blocks) * 4 * iters * 8 * 16 * 16 * 32 * 2
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        E.mfma_rate_probe(blocks, iters, out)
+        b.record()
+        b.synchronize()
+        best = max(best, flops / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return best
+
+
+def gemm_tflops(dev, n: int = 8192, reps: int = 20) -> float:
+    """bf16 GEMM rate of the platform library (torch.matmul -> hipBLASLt),
+    [n, n] x [n, n], average over `reps` calls after a warm-up."""
+    import torch
+    g = torch.Generator(device="cpu").manual_seed(0)
+    A = torch.randn(n, n, generator=g).to(dev, torch.bfloat16)
+    B = torch.randn(n, n, generator=g).to(dev, torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(A, B)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.matmul(A, B)
+    b.record()
+    b.synchronize()
+    return 2.0 * n ** 3 * reps / (a.elapsed_time(b) * 1e-3) / 1e12
+
+
+def peak_main(args):
+    import torch
+    import group_sparse_swiglu_amd as E
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    E.lib()
+    probe = mfma_probe_tflops(dev)
+    gemm = gemm_tflops(dev)
+    print(json.dumps({"metric": "measured bf16 MFMA rate", "value": round(probe, 1), "unit": "TFLOP/s",
+                      "spec_peak": PEAK_TFLOPS["bf16"], "probe_frac_of_spec": round(probe / PEAK_TFLOPS["bf16"], 4),
+                      "hipblaslt_gemm_8192_tflops": round(gemm, 1),
+                      "gemm_frac_of_spec": round(gemm / PEAK_TFLOPS["bf16"], 4),
+                      "probe": "2048 workgroups x 4 waves x 20000 iterations x 8 v_mfma_f32_16x16x32_bf16, "
+                               "register operands, best of 5", "n_gpus": 1}), flush=True)
 
 
 def routing_cpu_baseline(logits, bias, k, scaling, seconds):
@@ -506,6 +595,12 @@ def main():
     if args.mhffn:
         mhffn_main(args)
         return
+    if args.peak:
+        peak_main(args)
+        return
+    if args.k_sweep:
+        sweep_main(args)
+        return
 
     import torch
     import esg_inputs as I
@@ -517,8 +612,58 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     E.lib()
+    line = measure(args, w, dev)
+    print(json.dumps(line), flush=True)
+
+
+def skew_groups(G: int):
+    """The 4 groups the skewed load makes hot (spread over the group range)."""
+    return sorted({0, G // 4, G // 2, (3 * G) // 4})
+
+
+def sweep_main(args):
+    """Tokens/s of the step of --workload's shape for each k in --k-sweep: the
+    scaling with the active-group fraction k*gs/d_ff (eugen_sparse README,
+    "Parameters and how to choose them").  One JSON line with the table."""
+    import dataclasses
+    import torch
+    import esg_inputs as I
+    import group_sparse_swiglu_amd as E
+    base = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    E.lib()
+    rows = []
+    for k in [int(v) for v in args.k_sweep.split(",")]:
+        w = dataclasses.replace(base, k=k, name=f"{base.name}_k{k}")
+        print(f"[sweep] k={k}", file=sys.stderr, flush=True)
+        line = measure(args, w, dev, cpu=False)
+        rows.append({"k": k, "active_fraction": round(k * w.group_size / w.d_ff, 4),
+                     "tokens_per_s": line["value"], "ms_per_step": line["ms_per_step"],
+                     "active_tflops": line["active_tflops"], "active_mfma_frac": line["active_mfma_frac"],
+                     "kernels_us_per_step": line.get("kernels_us_per_step")})
+    print(json.dumps({"metric": "sparse SwiGLU fwd+bwd tokens/s against the active-group fraction",
+                      "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "dtype": base.dtype, "data": "synthetic",
+                      "config": {"workload": base.name, "tokens": base.tokens, "d_model": base.d_model,
+                                 "d_ff": base.d_ff, "group_size": base.group_size,
+                                 "samples_per_group": base.spg, "bias": base.bias},
+                      "sweep": rows}), flush=True)
+
+
+def measure(args, w, dev, cpu=True):
+    """One bench line for workload `w` (see the module docstring)."""
+    import torch
+    import esg_inputs as I
+    import group_sparse_swiglu_amd as E
 
     x, wg, wu, wd, dy, bias = I.make_workload_inputs(w, seed=0)
+    hot = None
+    if args.skew and not w.dense:
+        bias = (bias if bias is not None else torch.zeros(w.groups)).clone()
+        hot = skew_groups(w.groups)
+        bias[hot] += 10.0   # far above the energy spread: every token takes the hot groups
+        w = dataclasses_replace(w, bias=True, name=w.name + "_skew")
     sub = E.make_subsample_index(w.d_ff, w.group_size, w.spg, 0)[0] if w.spg else None
     host_inputs = (x, wg, wu, wd, dy, bias, sub)
     X, WG, WU, WD, DY = (t.to(dev) for t in (x, wg, wu, wd, dy))
@@ -534,6 +679,9 @@ def main():
                         device=dev)
     ws = {}
     saved = [None]
+    # a second stream for the weight gradients beside the dx sum (the library
+    # creates none of its own)
+    AUX = torch.cuda.Stream(device=dev)
 
     def step():
         if args.inference:
@@ -555,7 +703,7 @@ def main():
                               workspace=SELWS)
         _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, saved=saved[0])
         saved[0] = ctx.saved
-        E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS)
+        E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS, aux_stream=AUX)
         if w.bias_update:
             E.update_load_balance_bias_from_routing(BIAS, EMA, ctx, w.k / G, 1e-3, 0.5, 0.99)
 
@@ -671,9 +819,20 @@ def main():
     if per_kernel:
         line["kernels_us_per_step"] = {k: round(v["us_per_step"], 2) for k, v in per_kernel.items()}
         line["kernels_algorithmic_tflops"] = {k: round(v, 1) for k, v in line_kernel_flops.items()}
-    if not args.no_cpu_baseline and not args.inference:
+    if hot is not None:
+        counts = torch.bincount(IDX.flatten().long(), minlength=G).cpu()
+        line["config"]["skew"] = {"hot_groups": hot, "hot_bias": 10.0,
+                                  "hot_load_share": round(float(counts[hot].sum()) / float(counts.sum()), 4),
+                                  "max_group_tokens": int(counts.max()), "min_group_tokens": int(counts.min())}
+    if not getattr(args, "no_peak_probe", False) and cpu:
+        peak_meas = mfma_probe_tflops(dev)
+        line["mfma_peak_measured_tflops"] = round(peak_meas, 1)
+        line["active_frac_of_measured_peak"] = round(line["active_tflops"] / peak_meas, 4)
+        if line.get("roofline"):
+            line["roofline"]["frac_of_measured_peak"] = round(line["roofline"]["achieved"] / peak_meas, 4)
+    if cpu and not args.no_cpu_baseline and not args.inference:
         line["cpu_baseline"] = cpu_baseline(w, host_inputs, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":

@@ -26,7 +26,7 @@ __all__ = [
     "ESG_F32", "ESG_BF16", "EsgError", "lib", "library_path", "make_subsample_index", "grouped_topk_select",
     "select_workspace_size", "bucket_by_group", "sparse_swiglu_fwd", "sparse_swiglu_bwd", "sparse_swiglu_ffn",
     "update_load_balance_bias", "update_load_balance_bias_from_routing",
-    "update_load_balance_bias_from_counts", "workspace_size", "timing_enable", "timing_reset", "timing_read",
+    "update_load_balance_bias_from_counts", "workspace_size", "mfma_rate_probe", "timing_enable", "timing_reset", "timing_read",
     "FfnContext", "EXPORTED_SYMBOLS", "sigmoid_topk_supported", "sigmoid_topk_routing",
     "leaky_mlp_workspace_size", "leaky_mlp_fwd", "leaky_mlp_bwd", "leaky_mlp_saved_views",
     "mhffn_supported", "mhffn_fwd", "mhffn_bwd",
@@ -64,6 +64,9 @@ _SIGNATURES = {
     "esg_sparse_swiglu_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_vp, _c_vp, _c_size, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
                                        _c_vp]),
+    "esg_sparse_swiglu_bwd_overlap": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int,
+                                               _c_int, _c_int, _c_vp, _c_vp, _c_size, _c_vp, _c_vp, _c_vp, _c_vp,
+                                               _c_vp, _c_size, _c_vp, _c_vp]),
     "esg_update_load_balance_bias": (_c_int, [_c_vp, _c_vp, _c_vp, _c_f, _c_f, _c_f, _c_f, _c_int, _c_vp]),
     "esg_update_load_balance_bias_from_counts": (_c_int, [_c_vp, _c_vp, _c_vp, _c_int, _c_f, _c_f, _c_f, _c_f,
                                                           _c_int, _c_vp]),
@@ -81,6 +84,7 @@ _SIGNATURES = {
     "esg_sigmoid_topk_supported": (_c_int, [_c_int, _c_int]),
     "esg_sigmoid_topk_routing": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _c_vp, _c_vp,
                                           _c_vp]),
+    "esg_mfma_rate_probe": (_c_int, [_c_int, _c_int, _c_vp, _c_vp]),
     "esg_timing_enable": (_c_int, [_c_int]),
     "esg_timing_reset": (_c_int, []),
     "esg_timing_read": (_c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_int)]),
@@ -273,8 +277,12 @@ def sparse_swiglu_fwd(x, w_gate, w_up, w_down, group_idx, group_size: int, statu
     return y, FfnContext(saved, group_idx, group_size, k, T, d, F, code)
 
 
-def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=None, outs=None):
-    """Backward -> (dx, dW_gate, dW_up, dW_down), all overwritten."""
+def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=None, outs=None, aux_stream=None):
+    """Backward -> (dx, dW_gate, dW_up, dW_down), all overwritten.
+
+    ``aux_stream``: an optional second torch stream on which the weight
+    gradients run beside the dx sum (esg_sparse_swiglu_bwd_overlap); every
+    result is ordered on the current stream on return."""
     if ctx.saved is None and ctx.idx is not None:
         raise EsgError("the forward ran with for_backward=False: nothing was saved for a backward")
     T, d = x.shape
@@ -288,11 +296,12 @@ def sparse_swiglu_bwd(dy, x, w_gate, w_up, w_down, ctx: FfnContext, workspace=No
     if outs is None:
         outs = (torch.empty_like(x), torch.empty_like(w_gate), torch.empty_like(w_up), torch.empty_like(w_down))
     dx, dwg, dwu, dwd = outs
-    _check(lib().esg_sparse_swiglu_bwd(
+    _check(lib().esg_sparse_swiglu_bwd_overlap(
         _dev(dy, "dy"), _dev(x, "x"), _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), _dev(w_down, "w_down"), code, T,
         d, F, ctx.group_size, ctx.k, _dev(ctx.idx, "group_idx", torch.int32), _dev(ctx.saved, "saved"),
-        ctx.saved.numel() if ctx.saved is not None else 0, _dev(dx, "dx"), _dev(dwg, "dw_gate"), _dev(dwu, "dw_up"), _dev(dwd, "dw_down"),
-        _dev(scratch, "scratch"), scratch.numel(), _stream(dev)), "sparse_swiglu_bwd")
+        ctx.saved.numel() if ctx.saved is not None else 0, _dev(dx, "dx"), _dev(dwg, "dw_gate"), _dev(dwu, "dw_up"),
+        _dev(dwd, "dw_down"), _dev(scratch, "scratch"), scratch.numel(), _stream(dev),
+        None if aux_stream is None else aux_stream.cuda_stream), "sparse_swiglu_bwd")
     return dx, dwg, dwu, dwd
 
 
@@ -467,6 +476,15 @@ def sigmoid_topk_routing(logits, expert_bias, topk: int, scaling_factor: Optiona
         _dev(probs, "probs", torch.float32), _dev(indices, "indices", torch.int64), _stream(logits.device)),
         "sigmoid_topk_routing")
     return probs, indices
+
+
+def mfma_rate_probe(blocks: int, iters: int, out: torch.Tensor) -> None:
+    """Launch the bf16 matrix-core rate probe on the current stream (a
+    measurement helper): blocks * 4 waves * iters * 8 MFMAs of 16x16x32.
+    out: float32 device tensor of at least blocks * 256 elements."""
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < blocks * 256:
+        raise ValueError("out must be a float32 device tensor of blocks * 256 elements")
+    _check(lib().esg_mfma_rate_probe(blocks, iters, _dev(out, "out"), _stream(out.device)), "mfma_rate_probe")
 
 
 def timing_enable(on: bool = True) -> None:

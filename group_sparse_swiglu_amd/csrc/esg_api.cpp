@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <mutex>
 
 #include "esg_internal.hpp"
 
@@ -95,52 +94,6 @@ const P* at(const void* base, size_t off) {
 
 hipError_t zero_bytes(void* p, size_t bytes, hipStream_t st) {
   return launch_fill_i32((int32_t*)p, 0, bytes / 4, st);
-}
-
-// A second stream on the current device (default priority, non-blocking) for
-// work that may run beside the caller's stream.  Created on first use, never
-// destroyed; not created while `main` is being captured into a graph (then, and
-// on any failure, nullptr: the caller runs everything on its own stream).
-hipStream_t aux_stream(hipStream_t main) {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (streams[dev] == nullptr) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    hipStream_t s = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    streams[dev] = s;
-  }
-  return streams[dev];
-}
-
-// Runs a() on `main` and b() on a second stream, both after the work already
-// enqueued on `main`; `main` then waits for b.  Falls back to a() then b() on
-// `main` when no second stream or event is available.  Works under graph
-// capture (the event record / wait pair forks and joins the captured stream).
-template <class A, class B>
-hipError_t fork_join(hipStream_t main, A&& a, B&& b) {
-  hipStream_t aux = aux_stream(main);
-  hipEvent_t forked = nullptr, done = nullptr;
-  if (aux != nullptr && hipEventCreateWithFlags(&forked, hipEventDisableTiming) == hipSuccess) {
-    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) == hipSuccess) {
-      hipError_t e = hipEventRecord(forked, main);
-      if (e == hipSuccess) e = hipStreamWaitEvent(aux, forked, 0);
-      if (e == hipSuccess) e = b(aux);
-      if (e == hipSuccess) e = a(main);
-      if (e == hipSuccess) e = hipEventRecord(done, aux);
-      if (e == hipSuccess) e = hipStreamWaitEvent(main, done, 0);
-      (void)hipEventDestroy(forked);
-      (void)hipEventDestroy(done);
-      return e;
-    }
-    (void)hipEventDestroy(forked);
-  }
-  hipError_t e = a(main);
-  return e == hipSuccess ? b(main) : e;
 }
 
 }  // namespace
@@ -294,6 +247,16 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
                           int dtype, int tokens, int d_model, int d_ff, int group_size, int k, const int32_t* idx,
                           const void* saved, size_t saved_bytes, void* dx, void* dw_gate, void* dw_up,
                           void* dw_down, void* scratch, size_t scratch_bytes, void* stream) {
+  return esg_sparse_swiglu_bwd_overlap(dy, x, w_gate, w_up, w_down, dtype, tokens, d_model, d_ff, group_size, k, idx,
+                                       saved, saved_bytes, dx, dw_gate, dw_up, dw_down, scratch, scratch_bytes, stream,
+                                       nullptr);
+}
+
+int esg_sparse_swiglu_bwd_overlap(const void* dy, const void* x, const void* w_gate, const void* w_up,
+                                  const void* w_down, int dtype, int tokens, int d_model, int d_ff, int group_size,
+                                  int k, const int32_t* idx, const void* saved, size_t saved_bytes, void* dx,
+                                  void* dw_gate, void* dw_up, void* dw_down, void* scratch, size_t scratch_bytes,
+                                  void* stream, void* aux_stream) {
   int st = check_shape(dtype, tokens, d_model, d_ff, group_size, k);
   if (st != ESG_OK) return st;
   if (w_gate == nullptr || w_up == nullptr || w_down == nullptr || scratch == nullptr || dw_gate == nullptr ||
@@ -342,16 +305,36 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
                                        at<char>(saved, L.hu), at<char>(scratch, L.b_dg), at<char>(scratch, L.b_du),
                                        at<char>(scratch, L.b_act), at<char>(scratch, L.b_part), stream_h);
   if (e != hipSuccess) return ESG_ERR_HIP;
-  // the slot-order sum of dx and the weight gradients only read what dh+dx
-  // wrote: they run side by side
-  auto sum_dx = [&](hipStream_t st) { return launch_rowsum(s, at<char>(scratch, L.b_part), L.rows, pinv, dx, st); };
-  auto weights = [&](hipStream_t st) {
-    return v2 ? launch_dw2(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
-                           at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, st)
-              : launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
-                              at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, st);
-  };
-  return hip_status(fork_join(stream_h, sum_dx, weights));
+  // The slot-order sum of dx and the weight gradients only read what dh+dx
+  // wrote.  With a caller-supplied second stream the weight gradients run on
+  // it beside the sum (forked after dh+dx, joined back into `stream` by two
+  // events created and destroyed in this call); else one after the other.
+  hipStream_t aux = (hipStream_t)aux_stream;
+  hipEvent_t forked = nullptr, done = nullptr;
+  if (aux != nullptr && aux != stream_h) {
+    if (hipEventCreateWithFlags(&forked, hipEventDisableTiming) != hipSuccess) return ESG_ERR_HIP;
+    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipEventDestroy(forked);
+      return ESG_ERR_HIP;
+    }
+    e = hipEventRecord(forked, stream_h);
+    if (e == hipSuccess) e = hipStreamWaitEvent(aux, forked, 0);
+  } else {
+    aux = stream_h;
+  }
+  if (e == hipSuccess)
+    e = v2 ? launch_dw2(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
+                        at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, aux)
+           : launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
+                           at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, aux);
+  if (e == hipSuccess) e = launch_rowsum(s, at<char>(scratch, L.b_part), L.rows, pinv, dx, stream_h);
+  if (forked != nullptr) {
+    if (e == hipSuccess) e = hipEventRecord(done, aux);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream_h, done, 0);
+    (void)hipEventDestroy(forked);
+    (void)hipEventDestroy(done);
+  }
+  return hip_status(e);
 }
 
 int esg_update_load_balance_bias(float* bias, float* freq_ema, const float* current_freq, float target_freq,
@@ -487,6 +470,11 @@ int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int 
     return ESG_ERR_INVALID_ARG;
   return hip_status(launch_sigmoid_topk(logits, expert_bias, bias_stride, tokens, num_experts, topk, scaling_factor,
                                         apply_scaling, probs, indices, (hipStream_t)stream));
+}
+
+int esg_mfma_rate_probe(int blocks, int iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || out == nullptr) return ESG_ERR_INVALID_ARG;
+  return hip_status(launch_mfma_probe(blocks, iters, out, (hipStream_t)stream));
 }
 
 int esg_timing_enable(int on) {

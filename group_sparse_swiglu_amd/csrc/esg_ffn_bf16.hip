@@ -62,8 +62,11 @@ constexpr int dw_subtiles() {
 //           saved by range 0 of the d-blocks), then phase 2 over the d-blocks
 //           of range blockIdx.z.
 // The sum over K ranges rounds differently from one accumulation over all of
-// K; every launch of a shape takes the same split, so results stay
-// reproducible.
+// K.  The split is a function of the shape alone (the tile bound and the
+// nominal CU count), so every launch of a shape rounds the same way on every
+// device; a token's y can still round differently in batches of other sizes,
+// whose tile bounds choose another number of ranges (4 up to 64 tiles, then 3,
+// 2, and one launch above 128 tiles).
 template <int GSB, int CPOL, int NW, int MODE = 0>
 __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
@@ -95,13 +98,14 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
   // phase-2 output rows (read before phase 1, so the load latency hides behind it)
   using RS = RowStore<DB, C::NTH>;
-  const uint32_t psub = (uint32_t)s * rows_total * d * 2;
+  // the tile's own partial rows, addressed from a per-tile buffer base (offsets
+  // stay below BM*d*2 bytes however large the whole partial buffer is)
   uint32_t row_off[RS::IT];
   if constexpr (MODE != 1) {
 #pragma unroll
     for (int it = 0; it < RS::IT; ++it) {
       const int r = RS::row(it, threadIdx.x);
-      row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
+      row_off[it] = ptoken[prow0 + r] >= 0 ? (uint32_t)r * d * 2 : kOOB;
     }
   }
   ESG_LDS char* act = st0;
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   const int nblk = min(per, nblk_all - blk0);
   const int c_lane = (lane & 7) ^ (lane >> 3);
   const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
-  const rsrc_t rp = make_rsrc(partials, gridDim.y * rows_total * (uint32_t)d * 2);
+  const rsrc_t rp = make_rsrc(partials + ((size_t)s * rows_total + prow0) * d, (uint32_t)BM * d * 2);
   uint32_t voffW[C::IW2];
 #pragma unroll
   for (int i = 0; i < C::IW2; ++i) {
@@ -336,8 +340,8 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
   // ---- phase 2: Q^T = [Wg; Wu]^T[d-block] . [dg du]^T ----
   const DmaSrc rg = make_dma_src(wg, (uint32_t)F * kbytes);
   const DmaSrc ru = make_dma_src(wu, (uint32_t)F * kbytes);
-  const rsrc_t rp = make_rsrc(partials, gridDim.y * rows_total * (uint32_t)d * 2);
-  const uint32_t psub = (uint32_t)s * rows_total * d * 2;
+  // the tile's own partial rows from a per-tile buffer base (see the forward)
+  const rsrc_t rp = make_rsrc(partials + ((size_t)s * rows_total + prow0) * d, (uint32_t)BM * d * 2);
   uint32_t voffW[C::IW];
   int jW[C::IW];
 #pragma unroll
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
 #pragma unroll
   for (int it = 0; it < RS::IT; ++it) {
     const int r = RS::row(it, threadIdx.x);
-    row_off[it] = ptoken[prow0 + r] >= 0 ? psub + (prow0 + r) * (uint32_t)d * 2 : kOOB;
+    row_off[it] = ptoken[prow0 + r] >= 0 ? (uint32_t)r * d * 2 : kOOB;
   }
   // staging of the output block: st0 when the weight tiles use st1/st2, else the stage tails
   ESG_LDS char* out0 = NS == 3 ? st0 : st0 + C::W2_BYTES;
@@ -449,6 +453,9 @@ bool partials_nontemporal(const FfnShape& s, int ntiles_max) {
   return (unsigned long long)s.nsub() * ntiles_max * BM * s.d_model * 2 > kCachedPartialBytes;
 }
 
+// The split forward's range counts come from the shape and the fixed nominal
+// compute-unit count kNominalCUs, not from the device, so a shape rounds the
+// same way on every device and partition mode.
 template <int GSB>
 hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
                   const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg, void* hu,
@@ -464,8 +471,8 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
         const int per = (n + want - 1) / want;
         return (n + per - 1) / per;
       };
-      const int kz = ranges((s.d_model + 63) / 64, std::min(kFwdSplitK, compute_units() / tiles));  // one per CU
-      const int nz = ranges((s.d_model + DB - 1) / DB, 2 * compute_units() / tiles);              // two per CU
+      const int kz = ranges((s.d_model + 63) / 64, std::min(kFwdSplitK, kNominalCUs / tiles));  // one per CU
+      const int nz = ranges((s.d_model + DB - 1) / DB, 2 * kNominalCUs / tiles);              // two per CU
       hipLaunchKernelGGL((fwd2_kernel<GSB, 0, 8, 1>), dim3(ntiles_max, s.nsub(), kz), dim3(64 * 8), 0, stream,
                          (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
                          s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
@@ -478,7 +485,7 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
     }
   }
   // a grid of at most one workgroup per CU: eight waves issue the loads
-  const bool alone = NW == 4 && (long long)ntiles_max * s.nsub() <= compute_units();
+  const bool alone = NW == 4 && (long long)ntiles_max * s.nsub() <= kNominalCUs;
   auto kern = partials_nontemporal(s, ntiles_max) ? fwd2_kernel<GSB, kCpolNontemporal, NW>
                                                   : (alone ? fwd2_kernel<GSB, 0, 8> : fwd2_kernel<GSB, 0, NW>);
   hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * (alone ? 8 : NW)), 0, stream, (const bf16_t*)x,
@@ -517,12 +524,14 @@ hipError_t dw2_t(const FfnShape& s, const void* x, const void* dy, const int32_t
 
 }  // namespace
 
+// Buffers the tile kernels address with 32-bit offsets from one base: x / dy
+// (gathered rows), the weights and the compact activations.  The partial rows
+// are addressed per tile, so their total size is not limited.
 bool bf16_pipelined(const FfnShape& s, int ntiles_max) {
   if (s.dtype != 1 || (s.gsb() != 64 && s.gsb() != 128)) return false;
   const unsigned long long lim = 1ull << 31;
   const unsigned long long rows = (unsigned long long)ntiles_max * BM;
   return (unsigned long long)s.tokens * s.d_model * 2 < lim && (unsigned long long)s.d_ff * s.d_model * 2 < lim &&
-         (unsigned long long)s.nsub() * rows * s.d_model * 2 < lim &&
          (unsigned long long)s.nsub() * rows * s.gsb() * 2 < lim;
 }
 

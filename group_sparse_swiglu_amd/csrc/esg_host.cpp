@@ -54,9 +54,10 @@ struct TimedLaunch {
   std::string name;
   hipEvent_t start, stop;
 };
-bool g_timing = false;
-std::vector<TimedLaunch> g_launches;
-std::vector<hipEvent_t> g_pool;  // events reused across resets: no creation in timed loops
+// Per host thread: a thread times its own launches (no shared mutable state).
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_launches;
+thread_local std::vector<hipEvent_t> g_pool;  // events reused across resets: no creation in timed loops
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {

@@ -126,6 +126,9 @@ hipError_t launch_bias_update(float* bias, float* ema, const float* freq, const 
                               const int32_t* offsets, int tokens, float target, float gamma, float bias_max,
                               float momentum, int groups, hipStream_t stream);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stream);
+// bf16 matrix-core rate probe: blocks x 256 threads, 8 * 16*16*32 * 2 FLOPs
+// per wave and iteration; out holds blocks * 256 floats
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t stream);
 
 // ---- LeakyReLU(0.5)^2 MLP (esg_mlp.hip), bf16 ------------------------------------
 size_t mlp_partial_bytes(int tokens, int d_model, int d_ff);
@@ -152,7 +155,11 @@ hipError_t launch_sigmoid_topk(const float* logits, const float* bias, int bias_
                                float scaling, int apply_scaling, float* probs, int64_t* indices,
                                hipStream_t stream);
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device): for launch sizes
+// that do not change results.  Rules that decide how a sum is split (and so
+// its rounding) use kNominalCUs instead, so a shape rounds the same way on
+// every device and partition mode.
 int compute_units();
+constexpr int kNominalCUs = 256;  // MI355X
 
 }  // namespace esg

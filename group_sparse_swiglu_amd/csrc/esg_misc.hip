@@ -34,6 +34,30 @@ __global__ void bias_update_kernel(float* __restrict__ bias, float* __restrict__
   }
 }
 
+// Rate probe of the bf16 matrix cores: every wave runs `iters` rounds of
+// eight independent 16x16x32 bf16 MFMAs on register operands (no memory
+// traffic in the loop) and writes one sum per lane, so the work stays.
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __restrict__ out) {
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  const unsigned lane = threadIdx.x & 63;
+  // small normal bf16 values (about 2^-7), different per lane
+  const uint4 ua = make_uint4(0x3c003c00u + lane, 0x3c103c10u, 0x3c203c20u, 0x3c303c30u);
+  const uint4 ub = make_uint4(0x3c083c08u, 0x3c183c18u + lane, 0x3c283c28u, 0x3c383c38u);
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ua), b = __builtin_bit_cast(bf16x8, ub);
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t v, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
@@ -58,6 +82,11 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t stre
   const size_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
   LaunchTimer timer("fill", stream);
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, value, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, stream, iters, out);
   return hipGetLastError();
 }
 

@@ -356,7 +356,8 @@ hipError_t weight_grad(const char* name, const bf16_t* A, int lda, const bf16_t*
                        int tokens, float* part, bf16_t* out, hipStream_t stream) {
   GemmArgs g = args(A, lda, B, ldb, Q, P, tokens);
   const int tiles = ((Q + TQ - 1) / TQ) * ((P + GP - 1) / GP);
-  const int splits = dw_splits(tokens, tiles, compute_units() * TileCfg<TQ>::OCC, &g.k_split);
+  // the split count (and so the rounding of the sum) depends on the shape only
+  const int splits = dw_splits(tokens, tiles, kNominalCUs * TileCfg<TQ>::OCC, &g.k_split);
   g.part = part;
   hipError_t e = launch_gemm<TQ, NROW, NROW, EPI_PARTIAL>(name, g, splits, stream);
   if (e != hipSuccess) return e;

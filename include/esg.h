@@ -19,12 +19,10 @@
  *    [g*group_size, (g+1)*group_size): rows of w_gate / w_up, columns of
  *    w_down.
  *  - The caller owns every buffer.  The library allocates no device memory and
- *    keeps no state between calls (apart from optional kernel timing and one
- *    auxiliary stream per device, created by the first sparse backward call
- *    made outside graph capture, on which that call's weight gradients run
- *    beside the dx sum and are joined back into `stream`); all
- *    scratch comes from caller buffers whose sizes the *_workspace_size calls
- *    give.
+ *    keeps no state between calls (apart from the optional per-thread kernel
+ *    timing below); all scratch comes from caller buffers whose sizes the
+ *    *_workspace_size calls give.  Every launch goes to `stream`: the library
+ *    creates no stream and no event of its own outside timing.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    nothing synchronises.  Calls on one stream are ordered.
  *  - dtype is ESG_F32 or ESG_BF16 for x, dy, the weights and the outputs
@@ -158,8 +156,9 @@ int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int grou
  * x: [tokens, d_model]; idx: device int32 [tokens, k] (distinct ids per token;
  * see esg_bucket_by_group for what happens otherwise); y: [tokens, d_model]
  * overwritten.  The gated activation of a group never leaves the chip; the k
- * per-token contributions are summed in slot order without atomics, so the
- * result is bitwise reproducible.  status_dev: as in esg_bucket_by_group.
+ * per-token contributions are written as partial rows and summed in slot order
+ * in float32 without atomics, so the result is bitwise reproducible.
+ * status_dev: as in esg_bucket_by_group.
  * saved = NULL selects inference (forward only): nothing is kept for a
  * backward, the routing is held in the scratch instead (fwd_scratch_bytes
  * covers it), and y is bitwise the same as with saved given.
@@ -167,7 +166,9 @@ int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int grou
  * Dense limit: idx = NULL with k = G means every group is active, i.e. the
  * plain SwiGLU block (the README's layer with all groups selected).  It runs
  * a fused kernel in which the [tokens, d_ff] intermediate never exists in
- * device memory; saved and scratch are unused (may be NULL).  Supported for
+ * device memory (forward only: the dense backward below recomputes gate/up
+ * and holds dg, du, a of one token chunk in its scratch); saved and scratch
+ * are unused (may be NULL).  Supported for
  * bf16 with d_model <= 2048; other dense shapes return ESG_ERR_UNSUPPORTED,
  * and k != G with idx = NULL returns ESG_ERR_INVALID_ARG.
  */
@@ -197,6 +198,22 @@ int esg_sparse_swiglu_bwd(const void* dy, const void* x, const void* w_gate, con
                           int group_size, int k, const int32_t* idx, const void* saved,
                           size_t saved_bytes, void* dx, void* dw_gate, void* dw_up, void* dw_down,
                           void* scratch, size_t scratch_bytes, void* stream);
+/*
+ * The same backward with a caller-owned second stream: for the routed path,
+ * after dh and the dx partials, the weight gradients run on aux_stream while
+ * the slot-order sum of dx runs on `stream`; aux_stream waits for `stream`
+ * first and `stream` waits for aux_stream at the end (two events created and
+ * destroyed inside the call), so on return every result is ordered on
+ * `stream` as with esg_sparse_swiglu_bwd.  aux_stream NULL or equal to
+ * `stream`: identical to esg_sparse_swiglu_bwd.  Works under stream capture
+ * (the event pair forks and joins the captured stream).  Results are bitwise
+ * the same either way.
+ */
+int esg_sparse_swiglu_bwd_overlap(const void* dy, const void* x, const void* w_gate, const void* w_up,
+                                  const void* w_down, int dtype, int tokens, int d_model, int d_ff,
+                                  int group_size, int k, const int32_t* idx, const void* saved,
+                                  size_t saved_bytes, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                                  void* scratch, size_t scratch_bytes, void* stream, void* aux_stream);
 
 /*
  * Load-balance bias update (eugen_sparse README, "What it does",
@@ -338,11 +355,26 @@ int esg_sigmoid_topk_routing(const float* logits, const float* expert_bias, int 
                              int64_t* indices, void* stream);
 
 /*
+ * Measurement helper (not part of the method): a rate probe of the bf16
+ * matrix cores.  Launches `blocks` workgroups of 256 threads on `stream`;
+ * every wavefront runs `iters` rounds of eight independent
+ * v_mfma_f32_16x16x32_bf16 on register operands, i.e.
+ * blocks * 4 * iters * 8 * 16384 FLOPs with no memory traffic, and writes
+ * one float per thread to `out` (device, blocks * 256 floats, caller-owned).
+ * Time it with events on `stream` to measure the achievable MFMA peak.
+ * Returns ESG_ERR_INVALID_ARG for blocks or iters < 1 or out NULL.
+ */
+int esg_mfma_rate_probe(int blocks, int iters, float* out, void* stream);
+
+/*
  * Kernel timing (instrumentation, off by default).  When enabled, every
- * kernel the library launches is bracketed by HIP events recorded on the
- * launch stream.  esg_timing_read synchronises on the recorded events and
- * returns the summed duration in milliseconds and the launch count of the
- * kernel named `kernel` since the last reset.  Not thread-safe.
+ * kernel the library launches from the calling host thread is bracketed by
+ * HIP events recorded on its launch stream.  esg_timing_read synchronises on
+ * the recorded events and returns the summed duration in milliseconds and the
+ * launch count of the kernel named `kernel` since the last reset.  The state
+ * (on/off flag, recorded events) belongs to the calling host thread: threads
+ * time their own launches independently, and a thread that never enables
+ * timing pays one flag test per launch.
  */
 int esg_timing_enable(int on);
 int esg_timing_reset(void);

@@ -103,31 +103,33 @@ def group_rows(d_ff: int, group_size: int, sub=None, spg=None):
     return [sub[g * spg:(g + 1) * spg] for g in range(groups)]
 
 
-def group_energy(x, w_gate, group_size: int, sub=None, spg=None) -> np.ndarray:
-    """E[t, g] = sum over the group's rows r of |SiLU(x[t] . W_gate[r])|, fp64.
+def group_energy(x, w_gate, group_size: int, sub=None, spg=None, dtype=np.float64) -> np.ndarray:
+    """E[t, g] = sum over the group's rows r of |SiLU(x[t] . W_gate[r])|, fp64
+    (``dtype`` float32 gives the same steps in float32, for the timed CPU
+    baseline only; parity always uses float64).
 
     Reading taken: with a subsample the sum runs over the sampled rows only and
     is not rescaled (the README defines the energy as this sum and says the
     subsample estimates it; a uniform rescale would not change the ranking
     without a bias, and the unscaled sum is the plain reading)."""
-    x = np.asarray(x, dtype=np.float64)
-    w_gate = np.asarray(w_gate, dtype=np.float64)
+    x = np.asarray(x, dtype=dtype)
+    w_gate = np.asarray(w_gate, dtype=dtype)
     rows = group_rows(w_gate.shape[0], group_size, sub, spg)
-    energy = np.empty((x.shape[0], len(rows)), dtype=np.float64)
+    energy = np.empty((x.shape[0], len(rows)), dtype=dtype)
     for g, r in enumerate(rows):
         h = x @ w_gate[r].T
         energy[:, g] = np.abs(silu(h)).sum(axis=1)
     return energy
 
 
-def selection_scores(x, w_gate, group_size: int, sub=None, spg=None, bias=None) -> np.ndarray:
+def selection_scores(x, w_gate, group_size: int, sub=None, spg=None, bias=None, dtype=np.float64) -> np.ndarray:
     """s = E + bias.  Reading taken: the balancing bias re-weights the ranking
     additively and is used for the selection only (DeepSeek-V3 style, as the
     README names it; the Megatron-Core sigmoid_topk page likewise adds its
     expert bias to the key and not to the probabilities)."""
-    s = group_energy(x, w_gate, group_size, sub, spg)
+    s = group_energy(x, w_gate, group_size, sub, spg, dtype)
     if bias is not None:
-        s = s + np.asarray(bias, dtype=np.float64)[None, :]
+        s = s + np.asarray(bias, dtype=dtype)[None, :]
     return s
 
 
@@ -139,7 +141,7 @@ def topk_from_scores(scores: np.ndarray, k: int) -> np.ndarray:
     torch.topk gives equal keys, as the Megatron-Core sigmoid_topk page
     describes it); the output order within a token is ascending group id,
     because the FFN sum does not depend on it."""
-    scores = np.asarray(scores, dtype=np.float64)
+    scores = np.asarray(scores)
     T, G = scores.shape
     if not 1 <= k <= G:
         raise ValueError("k must be in 1..G")
@@ -148,9 +150,10 @@ def topk_from_scores(scores: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:, :k], axis=1).astype(np.int32)
 
 
-def grouped_topk_select(x, w_gate, group_size: int, k: int, sub=None, spg=None, bias=None):
-    """Hard top-k group routing.  Returns (idx int32 [T, k], scores fp64 [T, G])."""
-    s = selection_scores(x, w_gate, group_size, sub, spg, bias)
+def grouped_topk_select(x, w_gate, group_size: int, k: int, sub=None, spg=None, bias=None, dtype=np.float64):
+    """Hard top-k group routing.  Returns (idx int32 [T, k], scores [T, G] in
+    ``dtype``, float64 unless the float32 timing variant is asked for)."""
+    s = selection_scores(x, w_gate, group_size, sub, spg, bias, dtype)
     return topk_from_scores(s, k), s
 
 
@@ -215,15 +218,15 @@ def check_routing(idx: np.ndarray, groups: int) -> None:
 # W_down [d, F]; group g owns neurons [g*gs, (g+1)*gs).
 # ---------------------------------------------------------------------------
 
-def group_mask(idx, tokens: int, d_ff: int, group_size: int) -> np.ndarray:
+def group_mask(idx, tokens: int, d_ff: int, group_size: int, dtype=np.float64) -> np.ndarray:
     """M[t, f] = 1 when neuron f's group is among token t's groups.  idx=None
     means every group is active (the dense limit)."""
     if idx is None:
-        return np.ones((tokens, d_ff), dtype=np.float64)
+        return np.ones((tokens, d_ff), dtype=dtype)
     idx = np.asarray(idx, dtype=np.int64)
     groups = d_ff // group_size
     check_routing(idx, groups)
-    gm = np.zeros((tokens, groups), dtype=np.float64)
+    gm = np.zeros((tokens, groups), dtype=dtype)
     np.put_along_axis(gm, idx, 1.0, axis=1)
     return np.repeat(gm, group_size, axis=1)
 
@@ -232,16 +235,17 @@ def _f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def sparse_swiglu_forward(x, w_gate, w_up, w_down, idx, group_size: int, chunk: int = 4096):
-    """y = (SiLU(x W_gate^T) * (x W_up^T) * M) W_down^T, fp64, [T, d]."""
-    x, w_gate, w_up, w_down = map(_f64, (x, w_gate, w_up, w_down))
+def sparse_swiglu_forward(x, w_gate, w_up, w_down, idx, group_size: int, chunk: int = 4096, dtype=np.float64):
+    """y = (SiLU(x W_gate^T) * (x W_up^T) * M) W_down^T, fp64, [T, d]
+    (``dtype`` float32: the same steps in float32, for the timed CPU baseline)."""
+    x, w_gate, w_up, w_down = (np.asarray(a, dtype=dtype) for a in (x, w_gate, w_up, w_down))
     T = x.shape[0]
     F = w_gate.shape[0]
-    y = np.zeros((T, w_down.shape[0]), dtype=np.float64)
+    y = np.zeros((T, w_down.shape[0]), dtype=dtype)
     for t0 in range(0, T, chunk):
         xs = x[t0:t0 + chunk]
         m = group_mask(None if idx is None else np.asarray(idx)[t0:t0 + chunk],
-                       xs.shape[0], F, group_size)
+                       xs.shape[0], F, group_size, dtype)
         hg = xs @ w_gate.T
         hu = xs @ w_up.T
         a = silu(hg) * hu * m
@@ -249,7 +253,8 @@ def sparse_swiglu_forward(x, w_gate, w_up, w_down, idx, group_size: int, chunk: 
     return y
 
 
-def sparse_swiglu_backward(dy, x, w_gate, w_up, w_down, idx, group_size: int, chunk: int = 4096):
+def sparse_swiglu_backward(dy, x, w_gate, w_up, w_down, idx, group_size: int, chunk: int = 4096,
+                           dtype=np.float64):
     """Gradients of L = sum(y * dy) with the routing held fixed (hard top-k: no
     gradient reaches the routing; README, "Pitfalls and limitations").
 
@@ -258,8 +263,9 @@ def sparse_swiglu_backward(dy, x, w_gate, w_up, w_down, idx, group_size: int, ch
       dHu = dA * SiLU(Hg);  dHg = dA * Hu * SiLU'(Hg)
       dx = dHg W_gate + dHu W_up
       dW_gate = dHg^T x;  dW_up = dHu^T x;  dW_down = dy^T A
-    Returns (dx, dw_gate, dw_up, dw_down) in fp64."""
-    dy, x, w_gate, w_up, w_down = map(_f64, (dy, x, w_gate, w_up, w_down))
+    Returns (dx, dw_gate, dw_up, dw_down) in fp64 (``dtype`` float32: the
+    same steps in float32, for the timed CPU baseline)."""
+    dy, x, w_gate, w_up, w_down = (np.asarray(a, dtype=dtype) for a in (dy, x, w_gate, w_up, w_down))
     T = x.shape[0]
     F = w_gate.shape[0]
     dx = np.zeros_like(x)
@@ -270,7 +276,7 @@ def sparse_swiglu_backward(dy, x, w_gate, w_up, w_down, idx, group_size: int, ch
         xs = x[t0:t0 + chunk]
         dys = dy[t0:t0 + chunk]
         m = group_mask(None if idx is None else np.asarray(idx)[t0:t0 + chunk],
-                       xs.shape[0], F, group_size)
+                       xs.shape[0], F, group_size, dtype)
         hg = xs @ w_gate.T
         hu = xs @ w_up.T
         s = sigmoid(hg)

@@ -206,3 +206,21 @@ def test_autograd_wrapper_matches_entry_points():
     assert torch.equal(y.detach(), ref[0])
     for p, r in zip(params, ref[1:]):
         assert torch.equal(p.grad, r)
+
+
+@pytest.mark.parametrize("T", [8192, 300])
+def test_backward_on_a_second_stream_is_bitwise_the_one_stream_backward(T):
+    """esg_sparse_swiglu_bwd_overlap runs the weight gradients on a caller
+    stream beside the dx sum; every gradient is bitwise the one-stream result
+    (8192 tokens: the tile path of the 128M shape; 300: the split forward)."""
+    require_gpu()
+    note(f"bwd overlap T={T}")
+    inp = inputs(T, 768, 2048, 64, "bf16", seed=13, bias=False)
+    idx = I.random_group_idx(T, 32, 8, seed=13).to(DEV)
+    x, wg, wu, wd, dy = (to_dev(inp[n]) for n in ("x", "wg", "wu", "wd", "dy"))
+    _, ctx = E.sparse_swiglu_fwd(x, wg, wu, wd, idx, 64)
+    one = E.sparse_swiglu_bwd(dy, x, wg, wu, wd, ctx)
+    two = E.sparse_swiglu_bwd(dy, x, wg, wu, wd, ctx, aux_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    for u, v in zip(one, two):
+        assert torch.equal(u, v)

@@ -1,7 +1,9 @@
 """The hot path captured as one HIP graph: every replay must reproduce the
 eagerly launched step bit for bit (the kernels are deterministic), also with
 other GPU work and synchronisations between the replays.  Covers the routed
-path with selection and the bias update, and the dense limit."""
+path with selection and the bias update (also with the weight gradients on a
+second caller stream, forked and joined inside the captured backward), and
+the dense limit."""
 import pytest
 import torch
 
@@ -19,11 +21,13 @@ def _bufs(T, d, F, G, k, dtype):
                        torch.empty(F, d, dtype=dtype, device=DEV), torch.empty(d, F, dtype=dtype, device=DEV)))
 
 
-@pytest.mark.parametrize("dense", [False, True], ids=["routed", "dense"])
-def test_graph_replays_match_eager(dense):
+@pytest.mark.parametrize("dense,overlap", [(False, False), (False, True), (True, False)],
+                         ids=["routed", "routed_aux_stream", "dense"])
+def test_graph_replays_match_eager(dense, overlap):
     require_gpu()
     T, d, F, gs, k, spg = 2048, 256, 1024, 64, 4, 8
-    note(f"graph replay {'dense' if dense else 'routed'}")
+    note(f"graph replay {'dense' if dense else 'routed'} overlap={overlap}")
+    aux = torch.cuda.Stream() if overlap else None
     inp = inputs(T, d, F, gs, "bf16", seed=31, bias=True, spg=spg)
     x, wg, wu, wd, dy = (to_dev(inp[n]) for n in ("x", "wg", "wu", "wd", "dy"))
     sub = to_dev(inp["sub"])
@@ -41,7 +45,7 @@ def test_graph_replays_match_eager(dense):
                                   counts_out=b["cnt"])
             _, ctx = E.sparse_swiglu_fwd(x, wg, wu, wd, b["idx"], gs, workspace=ws, out=b["y"], saved=saved[0])
         saved[0] = ctx.saved
-        E.sparse_swiglu_bwd(dy, x, wg, wu, wd, ctx, workspace=ws, outs=b["grads"])
+        E.sparse_swiglu_bwd(dy, x, wg, wu, wd, ctx, workspace=ws, outs=b["grads"], aux_stream=aux)
         if not dense:
             E.update_load_balance_bias_from_counts(bias, ema, b["cnt"], T, k / G, 1e-3, 0.5, 0.99)
 
