@@ -61,6 +61,8 @@ _SIGNATURES = {
                                                   ctypes.POINTER(_c_size)]),
     "esg_sparse_swiglu_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_vp, _c_vp, _c_vp, _c_size, _c_vp, _c_size, _c_vp, _c_vp]),
+    "esg_sparse_swiglu_fwd_noalloc": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                               _c_int, _c_vp, _c_vp, _c_vp, _c_vp]),
     "esg_sparse_swiglu_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_vp, _c_vp, _c_size, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
                                        _c_vp]),

@@ -178,6 +178,29 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
                           size_t scratch_bytes, int32_t* status_dev, void* stream);
 
 /*
+ * The inference forward (the call above with saved = NULL) for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no scratch argument: its
+ * scratch is a device array of ESG_NOALLOC_SCRATCH_BYTES (128 MiB) built into
+ * the library, one per device the library runs on, held until the process
+ * ends.  Arguments and results are those of esg_sparse_swiglu_fwd with
+ * saved = NULL; y is bitwise the same.  Shapes whose forward scratch
+ * (esg_sparse_swiglu_workspace_size's fwd_scratch_bytes) exceeds
+ * ESG_NOALLOC_SCRATCH_BYTES return ESG_ERR_WORKSPACE before anything is
+ * enqueued (every batch from 1 to 2482 tokens fits at the 1.3B shape, k = 11
+ * of 43 groups of 128; 1 to 10355 at the 128M shape, k = 8 of 32 groups of
+ * 64: decode and short prefill batches).  It calls no allocator.  All calls on one device share that
+ * device's array, so calls that overlap on one device (concurrent streams or
+ * threads) race; calls ordered on one stream do not.  The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress) with that
+ * device current; ESG_ERR_HIP if that fails.
+ */
+#define ESG_NOALLOC_SCRATCH_BYTES (128u << 20)
+int esg_sparse_swiglu_fwd_noalloc(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                                  int dtype, int tokens, int d_model, int d_ff, int group_size, int k,
+                                  const int32_t* idx, void* y, int32_t* status_dev, void* stream);
+
+/*
  * Backward of the forward above with the routing held fixed (hard top-k: the
  * README's pitfalls note that only selected groups receive weight gradients
  * and the routing gets none).  With A = SiLU(Hg)*Hu on the selected groups:
