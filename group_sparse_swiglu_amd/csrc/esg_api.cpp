@@ -51,10 +51,12 @@ struct Layout {
   size_t b_dg = 0, b_du = 0, b_act = 0, b_part = 0, bwd = 0;
 };
 
-Layout make_layout(const FfnShape& s) {
+// train: the layout of a forward that saves for the backward, whose groups are
+// padded to tile_pad(s) positions; an inference forward pads to whole tiles only
+Layout make_layout(const FfnShape& s, bool train = true) {
   Layout L;
   const int G = s.groups();
-  L.mt = max_tiles(s.tokens, s.k, G, kTileRows);
+  L.mt = max_tiles(s.tokens, s.k, G, kTileRows, train ? tile_pad(s) : kTileRows);
   L.rows = (size_t)L.mt * kTileRows;
   const size_t es = s.elem_bytes();
   const size_t act_bytes = (size_t)s.nsub() * L.rows * s.gsb() * es;
@@ -97,6 +99,8 @@ hipError_t zero_bytes(void* p, size_t bytes, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t esg::inference_fwd_scratch_bytes(const FfnShape& s) { return make_layout(s, false).fwd; }
 
 extern "C" {
 
@@ -221,15 +225,16 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
                         (const void*)scratch})
     if (!aligned16(p)) return ESG_ERR_INVALID_ARG;
   const FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
-  const Layout L = make_layout(s);
   const bool train = saved != nullptr;  // NULL: forward only, the routing lives in the scratch
+  const Layout L = make_layout(s, train);
   if ((train && saved_bytes < L.saved) || scratch_bytes < L.fwd) return ESG_ERR_WORKSPACE;
   void* route = train ? saved : at<char>(scratch, L.f_route);
   hipStream_t stream_h = (hipStream_t)stream;
   BucketOut out{at<int32_t>(route, L.offsets), nullptr, nullptr, at<int32_t>(route, L.tile_off),
                 at<int32_t>(route, L.tile_group), at<int32_t>(route, L.ptoken), at<int32_t>(route, L.pinv),
                 status_dev};
-  hipError_t e = launch_bucket(idx, tokens, k, s.groups(), kTileRows, out, at<char>(scratch, L.f_bucket), stream_h);
+  hipError_t e = launch_bucket(idx, tokens, k, s.groups(), kTileRows, out, at<char>(scratch, L.f_bucket), stream_h,
+                               train ? tile_pad(s) : kTileRows);
   if (e != hipSuccess) return ESG_ERR_HIP;
   char* hg = train ? at<char>(saved, L.hg) : nullptr;
   char* hu = train ? at<char>(saved, L.hu) : nullptr;

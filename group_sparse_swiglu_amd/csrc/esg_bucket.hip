@@ -207,8 +207,9 @@ __device__ void write_tile_groups(const int* g_toff, int groups, int max_tiles, 
   }
 }
 
-// Padding rows of each group's last tile -> -1: one wavefront per group, its
-// lanes over the group's (contiguous) padding rows.
+// Padding rows after each group's positions (to the end of its last tile, or
+// of its last pair of tiles with a pad of two tiles) -> -1: one wavefront per
+// group, its lanes over the group's (contiguous) padding rows.
 __device__ void write_padding(const int* g_off, const int* g_toff, int groups, int tile_rows, int32_t* ptoken,
                               int wave, int nwaves, int lane) {
   for (int gg = wave; gg < groups; gg += nwaves) {
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(SCAN_NT) void bucket_scan_kernel(int nblocks, int g
                                                               int32_t* __restrict__ base,
                                                               int32_t* __restrict__ pbase,
                                                               int32_t* offsets, int32_t* tile_off,
-                                                              int32_t* tile_group, int32_t* ptoken) {
+                                                              int32_t* tile_group, int32_t* ptoken, int tile_pad) {
   __shared__ int wsum[4 * (SCAN_NT / 64) + 2];
   __shared__ int part[SCAN_NT];     // [slice][group] sums, then exclusive prefix over slices
   __shared__ int g_off[SCAN_NT + 1], g_toff[SCAN_NT + 1];
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(SCAN_NT) void bucket_scan_kernel(int nblocks, int g
   }
   __syncthreads();
   int total = 0, total_tiles = 0, off = 0, toff = 0;
-  const int nt = tid < groups ? (n + tile_rows - 1) / tile_rows : 0;
+  const int nt = tid < groups ? (n + tile_pad - 1) / tile_pad * (tile_pad / tile_rows) : 0;
   block_exclusive_scan2<SCAN_NT>(tid < groups ? n : 0, nt, off, toff, total, total_tiles, wsum);
   if (tid < groups) {
     g_off[tid] = off;
@@ -407,7 +408,8 @@ constexpr int kPlaceMaxTable = 32768;  // count-table entries a placement workgr
 // and the padding rows.
 __global__ __launch_bounds__(PNT) void bucket_place_kernel(const int32_t* __restrict__ idx, int tokens, int k,
                                                            int groups, int tile_rows, int max_tiles, int nblocks,
-                                                           const int32_t* __restrict__ bc, BucketOut out) {
+                                                           const int32_t* __restrict__ bc, BucketOut out,
+                                                           int tile_pad) {
   extern __shared__ uint32_t sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gw = (groups + 31) >> 5, ms = mask_stride(groups), rs = row_stride(k);
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(PNT) void bucket_place_kernel(const int32_t* __rest
     for (int c = 0; c < groups; c += TB) {
       const int g = c + lane;
       const int n = g < groups ? tot[g] : 0;
-      const int ntl = (n + tile_rows - 1) / tile_rows;
+      const int ntl = (n + tile_pad - 1) / tile_pad * (tile_pad / tile_rows);
       const int io = wave_inclusive_scan(n, lane), it = wave_inclusive_scan(ntl, lane);
       if (g < groups) {
         g_off[g] = carry + io - n;
@@ -523,7 +525,7 @@ constexpr int SINGLE_NT = 1024;
 // builds the masks, the ranks and the group scan.
 __global__ __launch_bounds__(SINGLE_NT) void bucket_single_kernel(const int32_t* __restrict__ idx, int tokens,
                                                                   int k, int groups, int tile_rows, int max_tiles,
-                                                                  BucketOut out) {
+                                                                  BucketOut out, int tile_pad) {
   extern __shared__ uint32_t sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gw = (groups + 31) >> 5, ms = mask_stride(groups), rs = row_stride(k);
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(SINGLE_NT) void bucket_single_kernel(const int32_t*
     for (int c = 0; c < groups; c += TB) {
       const int g = c + lane;
       const int n = g < groups ? hist[g] : 0;
-      const int ntl = (n + tile_rows - 1) / tile_rows;
+      const int ntl = (n + tile_pad - 1) / tile_pad * (tile_pad / tile_rows);
       const int io = wave_inclusive_scan(n, lane), it = wave_inclusive_scan(ntl, lane);
       if (g < groups) {
         g_off[g] = carry + io - n;
@@ -580,22 +582,27 @@ size_t bucket_scratch_bytes(int tokens, int groups) {
   return 3 * nb * (size_t)groups * sizeof(int32_t) + 256;
 }
 
-int max_tiles(int tokens, int k, int groups, int tile_rows) {
+int max_tiles(int tokens, int k, int groups, int tile_rows, int tile_pad) {
+  // sum over groups of ceil(n_g / tile_pad) * (tile_pad / tile_rows) tiles,
+  // at most (T*k + G*(tile_pad - 1)) / tile_rows; rounded up to whole pads
   const long long tk = (long long)tokens * k;
-  return (int)((tk + (long long)groups * (tile_rows - 1)) / tile_rows);
+  const long long per = tile_pad / tile_rows;
+  const long long bound = (tk + (long long)groups * (tile_pad - 1)) / tile_rows;
+  return (int)((bound + per - 1) / per * per);
 }
 
 hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int tile_rows,
-                         const BucketOut& out, void* scratch, hipStream_t stream) {
+                         const BucketOut& out, void* scratch, hipStream_t stream, int tile_pad) {
+  if (tile_pad <= 0) tile_pad = tile_rows;
   const int nb = (tokens + TB - 1) / TB;
-  const int mt = max_tiles(tokens, k, groups, tile_rows);
+  const int mt = max_tiles(tokens, k, groups, tile_rows, tile_pad);
   const size_t masks = (size_t)TB * mask_stride(groups) * 4, rows = (size_t)TB * row_stride(k) * 2,
                ranks = (size_t)TB * k;
   if (nb <= 1) {
     LaunchTimer timer("bucket_single", stream);
     const size_t smem = masks + (size_t)(3 * groups + 2) * 4 + rows + ranks;
     hipLaunchKernelGGL(bucket_single_kernel, dim3(1), dim3(SINGLE_NT), smem, stream, idx, tokens, k, groups,
-                       tile_rows, mt, out);
+                       tile_rows, mt, out, tile_pad);
     return hipGetLastError();
   }
   int32_t* bc = (int32_t*)scratch;
@@ -614,13 +621,13 @@ hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int 
   if ((size_t)nb * groups <= (size_t)kPlaceMaxTable && psmem <= 64 * 1024) {
     LaunchTimer timer("bucket_place", stream);
     hipLaunchKernelGGL(bucket_place_kernel, dim3((nb + PW - 1) / PW), dim3(PNT), psmem, stream, idx, tokens, k,
-                       groups, tile_rows, mt, nb, (const int32_t*)bc, out);
+                       groups, tile_rows, mt, nb, (const int32_t*)bc, out, tile_pad);
     return hipGetLastError();
   }
   {
     LaunchTimer timer("bucket_scan", stream);
     hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(SCAN_NT), 0, stream, nb, groups, tile_rows, mt, bc,
-                       base, pbase, out.offsets, out.tile_off, out.tile_group, out.ptoken);
+                       base, pbase, out.offsets, out.tile_off, out.tile_group, out.ptoken, tile_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -41,9 +41,11 @@ struct BucketOut {
   int32_t* status;      // device status word or NULL
 };
 size_t bucket_scratch_bytes(int tokens, int groups);
-int max_tiles(int tokens, int k, int groups, int tile_rows);
+// tile_pad: each group's positions are padded to a multiple of tile_pad (a
+// multiple of tile_rows), so its tile count is a multiple of tile_pad/tile_rows
+int max_tiles(int tokens, int k, int groups, int tile_rows, int tile_pad);
 hipError_t launch_bucket(const int32_t* idx, int tokens, int k, int groups, int tile_rows,
-                         const BucketOut& out, void* scratch, hipStream_t stream);
+                         const BucketOut& out, void* scratch, hipStream_t stream, int tile_pad = 0);
 
 // ---- FFN ----------------------------------------------------------------------
 struct FfnShape {
@@ -65,6 +67,12 @@ struct FfnShape {
   int elem_bytes() const { return dtype == 0 ? 4 : 2; }
 };
 constexpr int kTileRows = 128;  // bucket positions per grouped-GEMM tile
+// bf16 launches with 128-neuron blocks run the dh + dx tiles on pairs of tiles
+// of one group, so their groups are padded to 2 * kTileRows positions
+inline int tile_pad(const FfnShape& s) { return s.dtype == 1 && s.gsb() == 128 ? 2 * kTileRows : kTileRows; }
+// scratch of a routed forward with saved = NULL (no pair padding: at most the
+// fwd_scratch_bytes that esg_sparse_swiglu_workspace_size reports)
+size_t inference_fwd_scratch_bytes(const FfnShape& s);
 
 // Compact per-position activations [nsub][rows/EPC][gsb][EPC]
 hipError_t launch_fwd_grouped(const FfnShape& s, const void* x, const void* wg, const void* wu,

@@ -16,6 +16,7 @@
 #include <mutex>
 
 #include "esg.h"
+#include "esg_internal.hpp"
 
 namespace {
 
@@ -47,10 +48,12 @@ extern "C" int esg_sparse_swiglu_fwd_noalloc(const void* x, const void* w_gate, 
                                              const void* w_down, int dtype, int tokens, int d_model, int d_ff,
                                              int group_size, int k, const int32_t* idx, void* y,
                                              int32_t* status_dev, void* stream) {
-  size_t fwd_bytes = 0;
+  // validates the shape (and, for idx = NULL, rejects the dense limit's k)
   int st = esg_sparse_swiglu_workspace_size(tokens, d_model, d_ff, group_size, k, dtype, idx == nullptr, nullptr,
-                                            &fwd_bytes, nullptr);
+                                            nullptr, nullptr);
   if (st != ESG_OK) return st;
+  const esg::FfnShape s{dtype, tokens, d_model, d_ff, group_size, k};
+  const size_t fwd_bytes = idx == nullptr ? 0 : esg::inference_fwd_scratch_bytes(s);
   if (fwd_bytes > kScratchBytes) return ESG_ERR_WORKSPACE;
   void* ptr = nullptr;
   st = scratch_ptr(&ptr);

@@ -247,18 +247,20 @@ __device__ __forceinline__ void gateup_tile(const bf16_t* __restrict__ x, const 
 // ===========================================================================
 // NW wavefronts: phase 1 WM = NW/2 neuron slices x 2 position halves;
 // phase 2 two d halves (32 each) x NW/2 position slices.
-template <int GSB, int NW = 4>
+// BMT: bucket positions of a phase-1 tile (128, or 256 for a pair of tiles of
+// one group); phase 2 always works on 128 positions at a time.
+template <int GSB, int NW = 4, int BMT = BM>
 struct Dh2 {
   static constexpr int NTH = 64 * NW;
   static constexpr int WM = NW / 2;
   static constexpr int NCH = GSB / 8;            // 16-byte chunks per neuron row segment
   static constexpr int A_BYTES = 64 * GSB * 2;   // N-row: 64 d rows x GSB neurons
-  static constexpr int B_BYTES = BM * 128;       // K-row: BM positions x 64 d
+  static constexpr int B_BYTES = BMT * 128;      // K-row: BMT positions x 64 d
   static constexpr int STAGE1 = A_BYTES + B_BYTES;
   static constexpr int IA = NCH / NW;
-  static constexpr int IB = BM / (8 * NW);
+  static constexpr int IB = BMT / (8 * NW);
   static constexpr int L = IA + IB;
-  static constexpr int FM = GSB / WM / 16, FN = 4;  // wave tile GSB/WM neurons x 64 positions
+  static constexpr int FM = GSB / WM / 16, FN = BMT / 32;  // wave tile GSB/WM neurons x BMT/2 positions
   static constexpr int KSUB2 = 2 * GSB / 64;
   static constexpr int DGU_BYTES = KSUB2 * BM * 128;
   static constexpr int DB2 = 64;
@@ -268,17 +270,17 @@ struct Dh2 {
   static constexpr int FM2 = 2, FN2 = PW2 / 16;  // wave tile 32 d x PW2 positions
   static constexpr int STORES2 = RowStore<DB2, NTH>::IT;
   static constexpr int STAGE = STAGE1 > W2_BYTES ? STAGE1 : W2_BYTES;
-  static_assert(IA * NW == NCH && IB * 8 * NW == BM && IW * 8 * NW == 2 * GSB && FM >= 1, "whole instructions");
+  static_assert(IA * NW == NCH && IB * 8 * NW == BMT && IW * 8 * NW == 2 * GSB && FM >= 1, "whole instructions");
 };
 
 // Phase 1 of a backward tile: dA^T = W_down[:, nb0 .. nb0+GSB)^T . dY_tile^T
 // (K = d) for the 128 bucket positions from prow0 (token ids from ptoken).
-template <int GSB, int NS, int NW = 4>
+template <int GSB, int NS, int NW = 4, int BMT = BM>
 __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf16_t* __restrict__ wd, int tokens,
                                         int d, int F, int nb0, const int32_t* __restrict__ ptoken, uint32_t prow0,
                                         ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2,
-                                        f32x4 (&acc)[Dh2<GSB, NW>::FM][Dh2<GSB, NW>::FN]) {
-  using C = Dh2<GSB, NW>;
+                                        f32x4 (&acc)[Dh2<GSB, NW, BMT>::FM][Dh2<GSB, NW, BMT>::FN]) {
+  using C = Dh2<GSB, NW, BMT>;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t kbytes = (uint32_t)d * 2;
   const DmaSrc ry = make_dma_src(dy, (uint32_t)tokens * kbytes);
@@ -316,7 +318,7 @@ __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf1
   const int wm = w % C::WM, wn = w / C::WM;
   int brow[C::FN];
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) brow[j] = wn * 64 + j * 16 + (lane & 15);
+  for (int j = 0; j < C::FN; ++j) brow[j] = wn * (BMT / 2) + j * 16 + (lane & 15);
   zero_acc(acc);
   auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
     uint4 a[2][C::FM], b[2][C::FN];

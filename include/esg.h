@@ -143,8 +143,12 @@ int esg_bucket_by_group(const int32_t* idx, int tokens, int k, int groups, int32
  * nothing and its forward needs no scratch; its backward scratch holds the
  * recomputed dg, du, a of one chunk of at most 8192 tokens (3 * 2 bytes per
  * neuron per token) plus, when there is more than one chunk, float32
- * accumulators for the three weight gradients.  Errors: as for the forward;
- * ESG_ERR_UNSUPPORTED for a dense shape the dense kernels do not cover.
+ * accumulators for the three weight gradients.  fwd_scratch is what a
+ * forward with `saved` needs; a forward with saved = NULL needs at most that
+ * (bf16 training layouts with 128-neuron blocks pad each group's bucket to a
+ * whole pair of 128-position tiles for the backward; inference pads to one
+ * tile).  Errors: as for the forward; ESG_ERR_UNSUPPORTED for a dense shape the
+ * dense kernels do not cover.
  */
 int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int group_size, int k,
                                      int dtype, int dense, size_t* saved_bytes,
@@ -184,16 +188,16 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
  * scratch is a device array of ESG_NOALLOC_SCRATCH_BYTES (128 MiB) built into
  * the library, one per device the library runs on, held until the process
  * ends.  Arguments and results are those of esg_sparse_swiglu_fwd with
- * saved = NULL; y is bitwise the same.  Shapes whose forward scratch
- * (esg_sparse_swiglu_workspace_size's fwd_scratch_bytes) exceeds
- * ESG_NOALLOC_SCRATCH_BYTES return ESG_ERR_WORKSPACE before anything is
- * enqueued (every batch from 1 to 2482 tokens fits at the 1.3B shape, k = 11
- * of 43 groups of 128; 1 to 10355 at the 128M shape, k = 8 of 32 groups of
- * 64: decode and short prefill batches).  It calls no allocator.  All calls on one device share that
- * device's array, so calls that overlap on one device (concurrent streams or
- * threads) race; calls ordered on one stream do not.  The first call on a
- * device looks up the array's device address (hipGetSymbolAddress) with that
- * device current; ESG_ERR_HIP if that fails.
+ * saved = NULL; y is bitwise the same.  Shapes whose inference-forward
+ * scratch exceeds ESG_NOALLOC_SCRATCH_BYTES return ESG_ERR_WORKSPACE before
+ * anything is enqueued (every batch from 1 to 2482 tokens fits at the 1.3B
+ * shape, k = 11 of 43 groups of 128; 1 to 10355 at the 128M shape, k = 8 of
+ * 32 groups of 64: decode and short prefill batches).  It calls no allocator.
+ * All calls on one device share that device's array, so calls that overlap
+ * on one device (concurrent streams or threads) race; calls ordered on one
+ * stream do not.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress) with that device current; ESG_ERR_HIP if that
+ * fails.
  */
 #define ESG_NOALLOC_SCRATCH_BYTES (128u << 20)
 int esg_sparse_swiglu_fwd_noalloc(const void* x, const void* w_gate, const void* w_up, const void* w_down,

@@ -95,6 +95,30 @@ def test_forward_scratch_holds_split_partials_exactly_under_the_tile_limit():
     assert f32_a <= f32_b < f32_a + 64 * 1024
 
 
+def _saved_rows(T, d, F, gs, k):
+    """Bucket rows implied by the size of `saved`: per row 4 bytes of ptoken,
+    2 * gs bytes each of bf16 hg and hu, and 4 bytes of tile group per 128
+    rows; besides them T*k*4 bytes of pinv and the group offsets."""
+    _, sv, _, _ = _sizes(T, d, F, gs, k, E.ESG_BF16, 0)
+    return (sv - T * k * 4) / (4 + 4 / 128 + 2 * 2 * gs)
+
+
+@pytest.mark.parametrize("T,d,F,gs,k,pad", [(32768, 2048, 5504, 128, 11, 256), (16384, 1024, 2688, 128, 5, 256),
+                                            (8192, 768, 2048, 64, 8, 128), (100, 2048, 5504, 128, 11, 128)])
+def test_training_layout_pads_each_group_to_its_tile_unit(T, d, F, gs, k, pad):
+    """Each group's bucket holds at most n_g + pad - 1 rows, rounded to whole
+    pads of 128-position tiles: pairs of tiles (pad 256) where the backward's
+    dh + dx kernel takes two tiles of one group (bf16, 128-neuron blocks),
+    single tiles otherwise (64-neuron blocks, and 128-neuron groups of launches
+    under 128 tiles, which take 64-neuron blocks)."""
+    G = F // gs
+    per = pad // 128
+    tiles = (T * k + G * (pad - 1)) // 128
+    tiles = (tiles + per - 1) // per * per
+    rows = _saved_rows(T, d, F, gs, k)
+    assert abs(rows - tiles * 128) < 16, (rows, tiles * 128)
+
+
 def test_entry_points_reject_bad_arguments_before_launch():
     lib = E.lib()
     # NULL weights / misaligned pointers / bad shapes return before any HIP call
