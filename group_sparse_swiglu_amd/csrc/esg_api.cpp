@@ -233,13 +233,14 @@ int esg_sparse_swiglu_fwd(const void* x, const void* w_gate, const void* w_up, c
   BucketOut out{at<int32_t>(route, L.offsets), nullptr, nullptr, at<int32_t>(route, L.tile_off),
                 at<int32_t>(route, L.tile_group), at<int32_t>(route, L.ptoken), at<int32_t>(route, L.pinv),
                 status_dev};
+  const int pad = train ? tile_pad(s) : kTileRows;
   hipError_t e = launch_bucket(idx, tokens, k, s.groups(), kTileRows, out, at<char>(scratch, L.f_bucket), stream_h,
-                               train ? tile_pad(s) : kTileRows);
+                               pad);
   if (e != hipSuccess) return ESG_ERR_HIP;
   char* hg = train ? at<char>(saved, L.hg) : nullptr;
   char* hu = train ? at<char>(saved, L.hu) : nullptr;
   e = bf16_pipelined(s, L.mt)
-          ? launch_fwd2(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, hg, hu,
+          ? launch_fwd2(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, pad, hg, hu,
                         at<char>(scratch, L.f_part), at<char>(scratch, L.f_act), stream_h)
           : launch_fwd_grouped(s, x, w_gate, w_up, w_down, out.tile_group, out.ptoken, L.mt, hg, hu,
                                at<char>(scratch, L.f_part), stream_h);

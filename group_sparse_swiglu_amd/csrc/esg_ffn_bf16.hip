@@ -51,6 +51,78 @@ constexpr int dw_subtiles() {
   return GSB >= 128 ? 2 : 1;
 }
 
+// Phase 2 of a forward tile: the partial rows of 128 bucket positions,
+// P^T = W_down[d-block, nb0 .. nb0+GSB) . a^T for the d-blocks [blk0, blk0 +
+// nblk), K = the group block.  act: the LDS K-row tile a[position][neuron]
+// (published by the first step's barrier); wbuf: two W_down buffers; out0 /
+// out1: row staging; rp, row_off: the 128 partial rows (kOOB for padding).
+// Every outstanding load or store of the caller is waited for at the first
+// step.
+template <int GSB, int NW, int CPOL>
+__device__ __forceinline__ void fwd_down_blocks(const bf16_t* __restrict__ wd, int d, int F, int nb0, int blk0,
+                                                int nblk, const ESG_LDS char* act, ESG_LDS char* const (&wbuf)[2],
+                                                ESG_LDS char* out0, ESG_LDS char* out1, rsrc_t rp,
+                                                const uint32_t (&row_off)[RowStore<DB, 64 * NW>::IT]) {
+  using C = Fwd2<GSB, NW>;
+  using RS = RowStore<DB, C::NTH>;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int wm = w % C::WM, wn = w / C::WM;
+  const int c_lane = (lane & 7) ^ (lane >> 3);
+  const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
+  uint32_t voffW[C::IW2];
+#pragma unroll
+  for (int i = 0; i < C::IW2; ++i) {
+    const int r = (w * C::IW2 + i) * 8 + (lane >> 3);
+    voffW[i] = (uint32_t)r * F * 2 + (uint32_t)nb0 * 2 + c_lane * 16;
+  }
+  auto issueW = [&](ESG_LDS char* st, int blk) __attribute__((always_inline)) {
+    const int db0 = (blk0 + blk) * DB;
+#pragma unroll
+    for (int sb = 0; sb < C::KSUB; ++sb)
+#pragma unroll
+      for (int i = 0; i < C::IW2; ++i) {
+        const int r = (w * C::IW2 + i) * 8 + (lane >> 3);
+        const uint32_t off = db0 + r < d ? voffW[i] + (uint32_t)db0 * F * 2 + sb * 128 : kOOB;
+        dma16(rd, st + sb * DB * 128 + (w * C::IW2 + i) * 1024, off);
+      }
+  };
+  int arow2[C::FM2], brow2[C::FN2];
+#pragma unroll
+  for (int i = 0; i < C::FM2; ++i) arow2[i] = wm * (DB / C::WM) + i * 16 + (lane & 15);
+#pragma unroll
+  for (int j = 0; j < C::FN2; ++j) brow2[j] = wn * 64 + j * 16 + (lane & 15);
+  auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
+    f32x4 acc2[C::FM2][C::FN2];
+    zero_acc(acc2);
+#pragma unroll
+    for (int kb = 0; kb < GSB / 32; ++kb) {
+      const int sb = kb >> 1, c = (kb & 1) * 4 + (lane >> 4);
+      uint4 a[C::FM2], b[C::FN2];
+#pragma unroll
+      for (int i = 0; i < C::FM2; ++i) a[i] = frag_krow(cur + sb * DB * 128, arow2[i], c);
+#pragma unroll
+      for (int j = 0; j < C::FN2; ++j) b[j] = frag_krow(act + sb * BM * 128, brow2[j], c);
+#pragma unroll
+      for (int i = 0; i < C::FM2; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN2; ++j) mma_bf16(acc2[i][j], a[i], b[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < C::FM2; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN2; ++j) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
+        RS::put(out0, out1, brow2[j], wm * (DB / C::WM) + i * 16 + (lane >> 4) * 4, v);
+      }
+    wait_lgkm0();
+    barrier();  // the whole block is staged
+    RS::template flush<CPOL>(out0, out1, rp, row_off, (blk0 + blk) * DB, d);
+  };
+  kloop_ring<2, C::KSUB * C::IW2, C::STORES2>(nblk, wbuf, issueW, compute2);
+}
+
 // NW: waves (fwd_waves<GSB>(); 8 for 64-neuron blocks when the grid leaves each
 // workgroup alone on its CU).
 // MODE 0: both phases.  With few tiles the two phases run as two launches, so
@@ -191,69 +263,207 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   const int per = MODE == 2 ? (nblk_all + gridDim.z - 1) / gridDim.z : nblk_all;
   const int blk0 = MODE == 2 ? blockIdx.z * per : 0;
   const int nblk = min(per, nblk_all - blk0);
-  const int c_lane = (lane & 7) ^ (lane >> 3);
-  const DmaSrc rd = make_dma_src(wd, (uint32_t)d * F * 2);
   const rsrc_t rp = make_rsrc(partials + ((size_t)s * rows_total + prow0) * d, (uint32_t)BM * d * 2);
-  uint32_t voffW[C::IW2];
-#pragma unroll
-  for (int i = 0; i < C::IW2; ++i) {
-    const int r = (w * C::IW2 + i) * 8 + (lane >> 3);
-    voffW[i] = (uint32_t)r * F * 2 + (uint32_t)nb0 * 2 + c_lane * 16;
-  }
-  auto issueW = [&](ESG_LDS char* st, int blk) __attribute__((always_inline)) {
-    const int db0 = (blk0 + blk) * DB;
-#pragma unroll
-    for (int sb = 0; sb < C::KSUB; ++sb)
-#pragma unroll
-      for (int i = 0; i < C::IW2; ++i) {
-        const int r = (w * C::IW2 + i) * 8 + (lane >> 3);
-        const uint32_t off = db0 + r < d ? voffW[i] + (uint32_t)db0 * F * 2 + sb * 128 : kOOB;
-        dma16(rd, st + sb * DB * 128 + (w * C::IW2 + i) * 1024, off);
-      }
-  };
-  int arow2[C::FM2], brow2[C::FN2];
-#pragma unroll
-  for (int i = 0; i < C::FM2; ++i) arow2[i] = wm * (DB / C::WM) + i * 16 + (lane & 15);
-#pragma unroll
-  for (int j = 0; j < C::FN2; ++j) brow2[j] = wn * 64 + j * 16 + (lane & 15);
   // staging of the output block: stage tails the W_down tiles and the act tile leave free
   ESG_LDS char* out0 = NS == 3 ? st1 + C::W2_BYTES : st0 + C::ACT_BYTES;
   ESG_LDS char* out1 = NS == 3 ? st[NS - 1] + C::W2_BYTES : st1 + C::W2_BYTES;
-  auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
-    f32x4 acc2[C::FM2][C::FN2];
-    zero_acc(acc2);
-#pragma unroll
-    for (int kb = 0; kb < GSB / 32; ++kb) {
-      const int sb = kb >> 1, c = (kb & 1) * 4 + (lane >> 4);
-      uint4 a[C::FM2], b[C::FN2];
-#pragma unroll
-      for (int i = 0; i < C::FM2; ++i) a[i] = frag_krow(cur + sb * DB * 128, arow2[i], c);
-#pragma unroll
-      for (int j = 0; j < C::FN2; ++j) b[j] = frag_krow(act + sb * BM * 128, brow2[j], c);
-#pragma unroll
-      for (int i = 0; i < C::FM2; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN2; ++j) mma_bf16(acc2[i][j], a[i], b[j]);
-    }
-#pragma unroll
-    for (int i = 0; i < C::FM2; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN2; ++j) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
-        RS::put(out0, out1, brow2[j], wm * (DB / C::WM) + i * 16 + (lane >> 4) * 4, v);
-      }
-    wait_lgkm0();
-    barrier();  // the whole block is staged
-    RS::template flush<CPOL>(out0, out1, rp, row_off, (blk0 + blk) * DB, d);
-  };
   // the stages after st0 are free (the barrier above); the first step's wait
   // covers the epilogue stores (they precede every W_down load), and its
   // barrier publishes the act tile.  The two W_down buffers: st1 and the last
   // stage (three stages) or the region after st1 (two)
   ESG_LDS char* const wbuf[2] = {st1, NS == 2 ? st1 + C::STAGE : st[NS - 1]};
-  kloop_ring<2, C::KSUB * C::IW2, C::STORES2>(nblk, wbuf, issueW, compute2);
+  fwd_down_blocks<GSB, NW, CPOL>(wd, d, F, nb0, blk0, nblk, act, wbuf, out0, out1, rp, row_off);
+}
+
+// ===========================================================================
+// Forward for 128-neuron blocks on a pair of tiles of one group (256 bucket
+// positions; groups are padded to an even number of tiles for it).
+// Phase 1 ([Hg; Hu]^T, K = d) runs over all 256 positions, so each staged
+// 64-wide K slice of the gate/up rows feeds twice the MFMAs of a 128-position
+// tile: a stage is 32 KB of weight rows and 32 KB of x rows for 8.4 MFLOP.
+// The weight slices come from L2 (every tile of the group reads them), the x
+// rows are gathered from HBM, so the x ring is one stage deeper: two weight
+// buffers and three x buffers (160 KB), x slice t+2 and weight slice t+1
+// issued while slice t is consumed.
+// The epilogue saves hg, hu and keeps a = SiLU(hg)*hu packed in registers;
+// phase 2 (partial rows) then runs on the two 128-position halves in turn,
+// each half's act tile written into LDS by the four waves that hold it.
+// ===========================================================================
+template <int CPOL>
+__global__ __launch_bounds__(512, 1) void fwd2_pair_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ wu,
+    const bf16_t* __restrict__ wd, int tokens, int d, int F, int gs, const int32_t* __restrict__ tile_group,
+    const int32_t* __restrict__ ptoken, uint32_t rows_total, bf16_t* __restrict__ hg_saved,
+    bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials) {
+  constexpr int GSB = 128, NW = 8, BMT = 2 * BM;
+  using C = Fwd2<GSB, NW>;  // phase-1 weight tile and the phase 2 of 128 positions
+  using RS = RowStore<DB, C::NTH>;
+  constexpr int A_BYTES = C::A_BYTES;  // 256 weight rows x 64 K
+  constexpr int B_BYTES = BMT * 128;   // 256 positions x 64 K
+  constexpr int IA = C::IA;            // DMA instructions per lane per weight slice
+  constexpr int IB = BMT / (8 * NW);   // ... per x slice
+  constexpr int FMP = C::FMP, FN = BMT / 2 / 16;  // wave tile: 2*FMP*16 rows x 128 positions
+  static_assert(A_BYTES == 32768 && B_BYTES == 32768 && IA == 4 && IB == 4, "pair tile shape");
+  // phase 1: weight buffers at 0 and 32 KB, x buffers at 64, 96 and 128 KB;
+  // phase 2: act at 0, W_down buffers at 32 and 64 KB, row staging at 96 KB
+  __shared__ __attribute__((aligned(1024))) char lds_[2 * A_BYTES + 3 * B_BYTES];
+  ESG_LDS char* const base = (ESG_LDS char*)lds_;
+  static_assert(C::ACT_BYTES + 2 * C::W2_BYTES + 128 * RS::RB <= 2 * A_BYTES + 3 * B_BYTES, "phase-2 LDS");
+
+  const int tile0 = 2 * blockIdx.x;
+  const int g = tile_group[tile0];
+  if (g < 0) return;
+  const int s = blockIdx.y;
+  const int nb0 = g * gs + s * GSB;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const uint32_t prow0 = (uint32_t)tile0 * BM;
+  const uint32_t kbytes = (uint32_t)d * 2;
+
+  // partial-row offsets of both halves (loaded now: the latency hides behind phase 1)
+  uint32_t row_off[2][RS::IT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int it = 0; it < RS::IT; ++it) {
+      const int r = RS::row(it, threadIdx.x);
+      row_off[h][it] = ptoken[prow0 + h * BM + r] >= 0 ? (uint32_t)r * d * 2 : kOOB;
+    }
+
+  // ---- phase 1 DMA: lane (row = lane/8 of an 8-row group, slot = lane%8) ----
+  const DmaSrc rx = make_dma_src(x, (uint32_t)tokens * kbytes);
+  const DmaSrc rg = make_dma_src(wg, (uint32_t)F * kbytes);
+  const DmaSrc ru = make_dma_src(wu, (uint32_t)F * kbytes);
+  const int c_lane = (lane & 7) ^ (lane >> 3);
+  uint32_t voffA[IA], voffB[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = (w * IA + i) * 8 + (lane >> 3);
+    const int grow = nb0 + (r < GSB ? r : r - GSB);
+    voffA[i] = grow < F ? (uint32_t)grow * kbytes + c_lane * 16 : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int r = (w * IB + i) * 8 + (lane >> 3);
+    const int t = ptoken[prow0 + r];
+    voffB[i] = t >= 0 ? (uint32_t)t * kbytes + c_lane * 16 : kOOB;
+  }
+  auto issueA = [&](int kt) __attribute__((always_inline)) {
+    ESG_LDS char* st = base + (kt & 1) * A_BYTES;
+    const uint32_t kb = (uint32_t)kt * 128;
+    const bool kin = kb + c_lane * 16 < kbytes;
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+      const bool gate = (w * IA + i) * 8 < GSB;  // wave-uniform
+      dma16(gate ? rg : ru, st + (w * IA + i) * 1024, (kin && voffA[i] != kOOB) ? voffA[i] + kb : kOOB);
+    }
+  };
+  auto issueB = [&](int kt) __attribute__((always_inline)) {
+    ESG_LDS char* st = base + 2 * A_BYTES + (kt % 3) * B_BYTES;
+    const uint32_t kb = (uint32_t)kt * 128;
+    const bool kin = kb + c_lane * 16 < kbytes;
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+      dma16(rx, st + (w * IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
+  };
+
+  // wave (wm, wn): gate and up neurons [wm*GSB/WM, +GSB/WM), positions [wn*128, +128)
+  const int wm = w % C::WM, wn = w / C::WM;
+  int arow[2 * FMP], brow[FN];
+#pragma unroll
+  for (int p = 0; p < FMP; ++p) {
+    arow[p] = wm * (GSB / C::WM) + p * 16 + (lane & 15);
+    arow[FMP + p] = GSB + arow[p];
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) brow[j] = wn * BM + j * 16 + (lane & 15);
+  f32x4 acc[2 * FMP][FN];
+  zero_acc(acc);
+  // Issue order: x0, w0, x1, then per step t: w(t+1), x(t+2).  At step t the
+  // loads younger than weight slice t are those of x slice t+1 (if any), and
+  // x slice t is older than weight slice t, so one vmcnt of IB (or 0) waits
+  // for both operands of slice t.  The buffers a step refills were read at
+  // step t-1, which the step's barrier closes.
+  const int nk = (int)((kbytes + 127) / 128);
+  issueB(0);
+  issueA(0);
+  if (nk > 1) issueB(1);
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) wait_vmcnt<IB>();
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+    if (t + 1 < nk) issueA(t + 1);
+    if (t + 2 < nk) issueB(t + 2);
+    const ESG_LDS char* sa = base + (t & 1) * A_BYTES;
+    const ESG_LDS char* sb = base + 2 * A_BYTES + (t % 3) * B_BYTES;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int c = kb * 4 + (lane >> 4);
+      uint4 a[2 * FMP], b[FN];
+#pragma unroll
+      for (int i = 0; i < 2 * FMP; ++i) a[i] = frag_krow(sa, arow[i], c);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = frag_krow(sb, brow[j], c);
+#pragma unroll
+      for (int i = 0; i < 2 * FMP; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma_bf16(acc[i][j], a[i], b[j]);
+    }
+  }
+
+  // ---- epilogue: hg, hu saved; a = SiLU(hg)*hu kept packed ----
+  const uint32_t sv_bytes = gridDim.y * rows_total * GSB * 2;
+  const rsrc_t rsv_g = make_rsrc(hg_saved, sv_bytes);
+  const rsrc_t rsv_u = make_rsrc(hu_saved, sv_bytes);
+  const uint32_t sub_off = (uint32_t)s * rows_total * GSB * 2;
+  uint2 apk[FMP][FN];
+#pragma unroll
+  for (int p = 0; p < FMP; ++p) {
+    const int n = wm * (GSB / C::WM) + p * 16 + (lane >> 4) * 4;  // 4 consecutive neurons
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      float hg[4], hu[4], a[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hg[e] = acc[p][j][e];
+        hu[e] = acc[FMP + p][j][e];
+        a[e] = hg[e] * sigmoid_f(hg[e]) * hu[e];
+      }
+      if (hg_saved != nullptr) {  // NULL: inference, nothing kept for a backward
+        const uint32_t so = sub_off + ((prow0 + brow[j]) * GSB + n) * 2;
+        store8(rsv_g, so, hg);
+        store8(rsv_u, so, hu);
+      }
+      apk[p][j] = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    }
+  }
+
+  // ---- phase 2 per half: P^T = W_down[d-block, nb0 .. nb0+GSB) . a^T ----
+  ESG_LDS char* const act = base;
+  ESG_LDS char* wbuf[2];  // (not a const array: its initializer would become a global)
+  wbuf[0] = base + C::ACT_BYTES;
+  wbuf[1] = base + C::ACT_BYTES + C::W2_BYTES;
+  ESG_LDS char* const out0 = base + C::ACT_BYTES + 2 * C::W2_BYTES;
+  ESG_LDS char* const out1 = out0 + 64 * RS::RB;
+  const int nblk = (d + DB - 1) / DB;
+  for (int h = 0; h < 2; ++h) {
+    wait_lgkm0();
+    barrier();  // phase 1 (or the previous half's phase 2) is done with these bytes
+    if (wn == h) {
+#pragma unroll
+      for (int p = 0; p < FMP; ++p) {
+        const int n = wm * (GSB / C::WM) + p * 16 + (lane >> 4) * 4;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int r = j * 16 + (lane & 15);
+          lds_write8(act + (n >> 6) * BM * 128 + krow_off(r, (n & 63) >> 3) + (n & 7) * 2, apk[p][j].x,
+                     apk[p][j].y);
+        }
+      }
+    }
+    const rsrc_t rp = make_rsrc(partials + ((size_t)s * rows_total + prow0 + h * BM) * d, (uint32_t)BM * d * 2);
+    fwd_down_blocks<GSB, NW, CPOL>(wd, d, F, nb0, 0, nblk, act, wbuf, out0, out1, rp, row_off[h]);
+  }
 }
 
 // ===========================================================================
@@ -637,7 +847,7 @@ bool partials_nontemporal(const FfnShape& s, int ntiles_max) {
 // same way on every device and partition mode.
 template <int GSB>
 hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
-                  const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg, void* hu,
+                  const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, int pad, void* hg, void* hu,
                   void* partials, void* act, hipStream_t stream) {
   LaunchTimer timer("fwd_grouped", stream);
   constexpr int NW = fwd_waves<GSB>();
@@ -660,6 +870,16 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
                          (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
                          s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
                          (bf16_t*)hu, (bf16_t*)partials, (float*)act, kz);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (GSB == 128) {
+    if (pad == 2 * BM) {  // pairs of tiles of one group (the bucketing padded groups to pairs)
+      auto kp = partials_nontemporal(s, ntiles_max) ? fwd2_pair_kernel<kCpolNontemporal> : fwd2_pair_kernel<0>;
+      hipLaunchKernelGGL(kp, dim3(ntiles_max / 2, s.nsub()), dim3(512), 0, stream, (const bf16_t*)x,
+                         (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
+                         s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
+                         (bf16_t*)partials);
       return hipGetLastError();
     }
   }
@@ -730,14 +950,14 @@ bool fwd_split(const FfnShape& s, int ntiles_max) {
 }
 
 hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
-                       const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg_saved,
+                       const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, int pad, void* hg_saved,
                        void* hu_saved, void* partials, void* act, hipStream_t stream) {
   if (ntiles_max == 0) return hipSuccess;
   if (!fwd_split(s, ntiles_max)) act = nullptr;
-  return s.gsb() == 64 ? fwd2_t<64>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, partials,
-                                    act, stream)
-                       : fwd2_t<128>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, partials,
-                                     act, stream);
+  return s.gsb() == 64 ? fwd2_t<64>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved,
+                                    partials, act, stream)
+                       : fwd2_t<128>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved,
+                                     partials, act, stream);
 }
 
 hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const void* wu, const void* wd,

@@ -104,9 +104,10 @@ bool fwd_split(const FfnShape& s, int ntiles_max);
 inline size_t fwd_split_bytes(const FfnShape& s, int ntiles_max) {
   return fwd_split(s, ntiles_max) ? (size_t)s.nsub() * ntiles_max * kFwdSplitK * kTileRows * 2 * s.gsb() * 4 : 0;
 }
-// act: the fwd_split_bytes partials for fwd_split shapes (ignored otherwise)
+// act: the fwd_split_bytes partials for fwd_split shapes (ignored otherwise);
+// pad: the bucket pad of the layout (2 * kTileRows: groups padded to tile pairs)
 hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const void* wu, const void* wd,
-                       const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, void* hg_saved,
+                       const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, int pad, void* hg_saved,
                        void* hu_saved, void* partials, void* act, hipStream_t stream);
 hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const void* wu, const void* wd,
                         const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, const void* hg_saved,
