@@ -57,6 +57,9 @@ WORKLOADS = {
     "s1p3b_bf16": Workload("s1p3b_bf16", "bf16", 32768, 2048, 5504, 128, 11, 16, True, False),
     "dense1p3b_bf16": Workload("dense1p3b_bf16", "bf16", 65536, 2048, 5504, 128, 43, None, False, False,
                                dense=True),
+    # the eugen_sparse README's training layer: d_model 512, d_ff 4096, groups of 32, 8 active (6.25 %),
+    # 8 subsampled gate rows per group, with the balancing bias and its update
+    "gs32_d512_bf16": Workload("gs32_d512_bf16", "bf16", 16384, 512, 4096, 32, 8, 8, True, True),
     # forward-only (inference) shapes: one decode step of a batch of 64 sequences, and a 4096-token prefill
     "decode1p3b_bf16": Workload("decode1p3b_bf16", "bf16", 64, 2048, 5504, 128, 11, 16, True, False),
     "prefill1p3b_bf16": Workload("prefill1p3b_bf16", "bf16", 4096, 2048, 5504, 128, 11, 16, True, False),

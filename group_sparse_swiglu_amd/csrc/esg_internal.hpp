@@ -67,9 +67,20 @@ struct FfnShape {
   int elem_bytes() const { return dtype == 0 ? 4 : 2; }
 };
 constexpr int kTileRows = 128;  // bucket positions per grouped-GEMM tile
-// bf16 launches with 128-neuron blocks run the dh + dx tiles on pairs of tiles
-// of one group, so their groups are padded to 2 * kTileRows positions
-inline int tile_pad(const FfnShape& s) { return s.dtype == 1 && s.gsb() == 128 ? 2 * kTileRows : kTileRows; }
+constexpr int kNominalCUs = 256;  // MI355X (see compute_units)
+// Large bf16 launches with 128-neuron blocks run the forward and the dh + dx
+// tiles on pairs of tiles of one group, so their training layouts pad groups
+// to 2 * kTileRows positions.  "Large": at least kPairMinTiles single tiles
+// (by the single-tile bound), i.e. at least four rounds of pair workgroups on
+// the nominal CUs; with fewer, the coarser pair grid loses more to its last
+// round than the pairs save (the 370M shape's 660 tiles: 330 pairs, 1.3
+// rounds).
+constexpr long long kPairMinTiles = 8ll * kNominalCUs;
+inline int tile_pad(const FfnShape& s) {
+  if (s.dtype != 1 || s.gsb() != 128) return kTileRows;
+  const long long tiles = ((long long)s.tokens * s.k + (long long)s.groups() * (kTileRows - 1)) / kTileRows;
+  return tiles * s.nsub() >= kPairMinTiles ? 2 * kTileRows : kTileRows;
+}
 // scratch of a routed forward with saved = NULL (no pair padding: at most the
 // fwd_scratch_bytes that esg_sparse_swiglu_workspace_size reports)
 size_t inference_fwd_scratch_bytes(const FfnShape& s);
@@ -166,9 +177,8 @@ hipError_t launch_sigmoid_topk(const float* logits, const float* bias, int bias_
 
 // Compute units of the current device (cached per device): for launch sizes
 // that do not change results.  Rules that decide how a sum is split (and so
-// its rounding) use kNominalCUs instead, so a shape rounds the same way on
-// every device and partition mode.
+// its rounding) or how buffers are laid out use kNominalCUs instead, so a
+// shape rounds the same way on every device and partition mode.
 int compute_units();
-constexpr int kNominalCUs = 256;  // MI355X
 
 }  // namespace esg

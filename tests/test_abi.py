@@ -103,14 +103,17 @@ def _saved_rows(T, d, F, gs, k):
     return (sv - T * k * 4) / (4 + 4 / 128 + 2 * 2 * gs)
 
 
-@pytest.mark.parametrize("T,d,F,gs,k,pad", [(32768, 2048, 5504, 128, 11, 256), (16384, 1024, 2688, 128, 5, 256),
+@pytest.mark.parametrize("T,d,F,gs,k,pad", [(32768, 2048, 5504, 128, 11, 256), (23335, 2048, 5504, 128, 11, 256),
+                                            (23334, 2048, 5504, 128, 11, 128), (16384, 1024, 2688, 128, 5, 128),
                                             (8192, 768, 2048, 64, 8, 128), (100, 2048, 5504, 128, 11, 128)])
 def test_training_layout_pads_each_group_to_its_tile_unit(T, d, F, gs, k, pad):
     """Each group's bucket holds at most n_g + pad - 1 rows, rounded to whole
-    pads of 128-position tiles: pairs of tiles (pad 256) where the backward's
-    dh + dx kernel takes two tiles of one group (bf16, 128-neuron blocks),
-    single tiles otherwise (64-neuron blocks, and 128-neuron groups of launches
-    under 128 tiles, which take 64-neuron blocks)."""
+    pads of 128-position tiles: pairs of tiles (pad 256) where the forward and
+    the dh + dx kernels take two tiles of one group (bf16, 128-neuron blocks,
+    at least 2048 single tiles by the bound floor((T*k + G*127)/128): 23335
+    tokens at the 1.3B shape, not 23334), single tiles otherwise (64-neuron
+    blocks; 128-neuron launches under 2048 tiles, e.g. the 370M shape; under
+    128 tiles 128-neuron groups take 64-neuron blocks)."""
     G = F // gs
     per = pad // 128
     tiles = (T * k + G * (pad - 1)) // 128

@@ -224,3 +224,57 @@ def test_backward_on_a_second_stream_is_bitwise_the_one_stream_backward(T):
     torch.cuda.synchronize()
     for u, v in zip(one, two):
         assert torch.equal(u, v)
+
+
+def _ragged_pair_routing(T, k, G, special):
+    """Token t takes special group g iff t < special[g] (so group g holds
+    exactly special[g] tokens), then fills its k slots from groups
+    len(special) .. G-1 by a fixed stride pattern (distinct per token)."""
+    ns = len(special)
+    rest = G - ns
+    idx = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        row = [g for g in range(ns) if t < special[g]]
+        j = 0
+        while len(row) < k:
+            row.append(ns + (t * 7 + j * 3) % rest)
+            j += 1
+        idx[t] = row
+    return idx
+
+
+def test_pair_tiles_with_ragged_and_empty_groups():
+    """23335 tokens of the 1.3B shape: the first size whose training layout
+    pads groups to pairs of tiles (2048 single tiles by the bound).  Groups of
+    0, 1, 128, 129, 255, 256, 257, 383, 384 and 385 tokens give pairs with one
+    real row, a whole padding tile, a ragged second tile, and no pair at all.
+    y and dx on sampled tokens (the group boundaries among them), dW on
+    neurons of every special group, against the fp64 oracle; the empty group's
+    weight gradients are exact zeros."""
+    require_gpu()
+    T, d, F, gs, k = 23335, 2048, 5504, 128, 11
+    G = F // gs
+    special = [1, 128, 129, 255, 256, 257, 0, 383, 384, 385]
+    assert (T * k + G * 127) // 128 == 2048
+    note(f"pair tiles ragged T={T}")
+    inp = inputs(T, d, F, gs, "bf16", seed=57, bias=False)
+    idx = _ragged_pair_routing(T, k, G, special)
+    counts = np.bincount(idx.ravel(), minlength=G)
+    assert list(counts[:len(special)]) == special and all(len(set(r)) == k for r in idx[:400])
+    y, dx, dwg, dwu, dwd = _run(inp, torch.as_tensor(idx).to(DEV))
+    rng = np.random.default_rng(58)
+    toks = np.unique(np.concatenate([[0, 1, 127, 128, 129, 254, 255, 256, 257, 382, 383, 384, 385, T - 1],
+                                     rng.choice(T, 40, replace=False)]))
+    W = [f64(inp[n]) for n in ("wg", "wu", "wd")]
+    xs, dys = f64(inp["x"][toks]), f64(inp["dy"][toks])
+    assert_close("y", f64(y[toks]), O.swiglu_rows(xs, *W, idx[toks], gs), "bf16")
+    assert_close("dx", f64(dx[toks]), O.dx_rows(dys, xs, *W, idx[toks], gs), "bf16")
+    neu = np.array([g * gs + o for g in range(len(special)) if special[g] > 0 for o in (0, 77, gs - 1)]
+                   + [30 * gs + 5])
+    rg, ru, rd = O.dw_neuron_rows(neu, f64(inp["dy"]), f64(inp["x"]), *W, idx, gs)
+    assert_close("dW_gate", f64(dwg[neu]), rg, "bf16")
+    assert_close("dW_up", f64(dwu[neu]), ru, "bf16")
+    assert_close("dW_down", f64(dwd[:, neu]), rd, "bf16")
+    sl = slice(6 * gs, 7 * gs)       # group 6 holds no token
+    assert torch.count_nonzero(dwg[sl]) == 0 and torch.count_nonzero(dwu[sl]) == 0
+    assert torch.count_nonzero(dwd[:, sl]) == 0

@@ -41,11 +41,11 @@ def test_inference_decode_matches_oracle(case):
         E.sparse_swiglu_bwd(to_dev(inp["dy"]), x, wg, wu, wd, ctx)
 
 
-# With 128-neuron blocks the training forward pads each group to a pair of
-# tiles for the backward and the inference forward to one tile: the two
-# layouts differ, the results must not.
+# At 24576 tokens of the 1.3B shape (2154 single tiles) the training forward
+# pads each group to a pair of tiles and runs the pair kernel, the inference
+# forward pads to one tile: the two layouts differ, the results must not.
 @pytest.mark.parametrize("T,d,F,gs,k", [(3000, 512, 2048, 64, 6), (3000, 512, 2048, 128, 6),
-                                        (4096, 2048, 5504, 128, 11)])
+                                        (24576, 2048, 5504, 128, 11)])
 def test_inference_equals_training_forward(T, d, F, gs, k):
     require_gpu()
     note(f"inference vs training T={T} d={d} gs={gs}")
