@@ -627,12 +627,19 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
 // ===========================================================================
 // Backward dh + dx for 128-neuron blocks on a pair of tiles of one group (256
 // bucket positions; groups are padded to an even number of tiles for it).
+// Wave w owns positions [32w, 32w+32) with all 128 neurons.
 // Phase 1 (dA^T = W_down[:, block]^T . dY^T, K = d) runs over all 256
 // positions, so each staged 64-row slice of W_down feeds twice the MFMAs of a
-// 128-position tile (48 KB per stage for 4.2 MFLOP instead of 32 KB for 2.1).
-// The epilogue stores dg, du, a for all 256 positions and keeps dg, du packed in
-// registers; phase 2 (dx partials, K = 2*128) then runs on the two 128-position
-// halves in turn, each half's [dg du] written into LDS by the waves that hold it.
+// 128-position tile.  The epilogue stores dg, du, a and keeps dg, du packed in
+// registers, as accumulator fragments: lane l holds four consecutive neurons
+// 16i + 4(l/16) .. of position 16j + l%16 of its wave's slice.
+// Phase 2 (dx partials, Q^T = [W_g; W_u]^T[d-block] . [dg du]^T, K = 256)
+// takes those registers as the B operand: a K step of 32 neurons pairs two
+// stacked fragments, and the weight tile is read in the same neuron order
+// (frag_nrow_acc).  So [dg du] never goes through LDS, and one staged weight
+// d-block serves all 256 positions (a quarter of the LDS the weights and the
+// [dg du] tile took per 128 positions before): three 32 KB weight buffers
+// and 32 KB of row staging for the two halves' partial rows.
 // ===========================================================================
 template <int CPOL>
 __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
@@ -643,22 +650,19 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
     bf16_t* __restrict__ act_out, bf16_t* __restrict__ partials) {
   constexpr int GSB = 128, NW = 8, BMT = 2 * BM;
   using C = Dh2<GSB, NW, BMT>;
-  using C2 = Dh2<GSB, NW>;  // phase 2 on 128 positions
+  using WV = DaWave<GSB, NW, BMT, 1>;
+  constexpr int FM = WV::FM, FN = WV::FN;  // 8 neuron fragments x 2 position fragments
   constexpr int NS = 3;
-  using RS = RowStore<C2::DB2, C2::NTH>;
-  // phase 1: NS stages; afterwards the same bytes hold the [dg du] tile of one
-  // half, two W tiles and the output staging
+  constexpr int DB2 = 64;                  // d per phase-2 step
+  constexpr int W2 = 2 * GSB * DB2 * 2;    // N-row: 256 neuron rows x 64 d
+  constexpr int IW = 2 * GSB / (8 * NW);   // weight DMA instructions per lane per step
+  constexpr int NWB = 3;                   // weight buffers
+  using RS = RowStore<DB2, 64 * NW>;
   constexpr int LDS1 = NS * C::STAGE1;
-  constexpr int LDS2 = C2::DGU_BYTES + 2 * C2::W2_BYTES + 128 * RS::RB;
-  __shared__ __attribute__((aligned(1024))) char lds_[LDS1 > LDS2 ? LDS1 : LDS2];
-  ESG_LDS char* const st0 = (ESG_LDS char*)lds_;
-  ESG_LDS char* const st1 = st0 + C::STAGE1;
-  ESG_LDS char* const st2 = st1 + C::STAGE1;
-  ESG_LDS char* const dgu = (ESG_LDS char*)lds_;
-  ESG_LDS char* const wb0 = dgu + C2::DGU_BYTES;
-  ESG_LDS char* const wb1 = wb0 + C2::W2_BYTES;
-  ESG_LDS char* const out0 = wb1 + C2::W2_BYTES;
-  ESG_LDS char* const out1 = out0 + 64 * RS::RB;
+  constexpr int LDS2 = NWB * W2 + 2 * 128 * RS::RB;
+  static_assert(FM == 8 && FN == 2 && IW == 4 && W2 == 32768 && LDS2 <= LDS1, "pair tile shape");
+  __shared__ __attribute__((aligned(1024))) char lds_[LDS1];
+  ESG_LDS char* const base = (ESG_LDS char*)lds_;
 
   const int tile0 = 2 * blockIdx.x;
   const int g = tile_group[tile0];
@@ -668,32 +672,40 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t prow0 = (uint32_t)tile0 * BM;
   const uint32_t kbytes = (uint32_t)d * 2;
+  const int p0 = WV::pos0(w);  // the wave's first position in the pair
 
-  const int wm = w % C::WM, wn = w / C::WM;  // neuron slice of 32, position half of 128
-  int brow[C::FN];
+  // partial-row offsets of both halves, and the saved hg, hu of the wave's
+  // positions (loaded now: the latency hides behind phase 1)
+  uint32_t row_off[2][RS::IT];
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) brow[j] = wn * BM + j * 16 + (lane & 15);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int it = 0; it < RS::IT; ++it) {
+      const int r = RS::row(it, threadIdx.x);
+      row_off[h][it] = ptoken[prow0 + h * BM + r] >= 0 ? (uint32_t)r * d * 2 : kOOB;
+    }
   const size_t sub_el = (size_t)s * rows_total * GSB;
-  uint2 hgq[C::FM][C::FN], huq[C::FM][C::FN];
+  uint2 hgq[FM][FN], huq[FM][FN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const size_t q = sub_el + (size_t)(prow0 + brow[j]) * GSB + wm * (GSB / C::WM) + i * 16 + (lane >> 4) * 4;
+    for (int j = 0; j < FN; ++j) {
+      const size_t q = sub_el + (size_t)(prow0 + p0 + j * 16 + (lane & 15)) * GSB + i * 16 + (lane >> 4) * 4;
       hgq[i][j] = *(const uint2*)(hg_saved + q);
       huq[i][j] = *(const uint2*)(hu_saved + q);
     }
-  f32x4 acc[C::FM][C::FN];
-  da_tile<GSB, NS, NW, BMT>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, acc);
+  f32x4 acc[FM][FN];
+  da_tile<GSB, NS, NW, BMT, 1>(dy, wd, tokens, d, F, nb0, ptoken, prow0, base, base + C::STAGE1,
+                               base + 2 * C::STAGE1, acc);
 
-  // ---- epilogue: SiLU'; dg, du kept packed for phase 2 ----
-  uint2 dgp[C::FM][C::FN], dup[C::FM][C::FN];
+  // ---- epilogue: SiLU'; dg, du kept packed as accumulator fragments ----
+  uint2 dgp[FM][FN], dup[FM][FN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int n = wm * (GSB / C::WM) + i * 16 + (lane >> 4) * 4;
+  for (int i = 0; i < FM; ++i) {
+    const int n = i * 16 + (lane >> 4) * 4;
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const size_t q = sub_el + (size_t)(prow0 + brow[j]) * GSB + n;
+    for (int j = 0; j < FN; ++j) {
+      const size_t q = sub_el + (size_t)(prow0 + p0 + j * 16 + (lane & 15)) * GSB + n;
       float hg[4], hu[4], dgv[4], duv[4], av[4];
       unpack_bf16x4(hgq[i][j], hg);
       unpack_bf16x4(huq[i][j], hu);
@@ -714,93 +726,79 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
     }
   }
 
-  // ---- phase 2 per half: Q^T = [Wg; Wu]^T[d-block] . [dg du]^T ----
+  // ---- phase 2: Q^T = [Wg; Wu]^T[d-block] . [dg du]^T over all 256 positions ----
+  // LDS: NWB weight buffers, then the row staging of half 0 and of half 1
+  ESG_LDS char* wbuf[NWB];  // (not a const array: its initializer would become a global)
+#pragma unroll
+  for (int i = 0; i < NWB; ++i) wbuf[i] = base + i * W2;
+  ESG_LDS char* const stg = base + NWB * W2;  // half h: rows 0..63 at stg + h*128*RB, 64..127 after
+  const int h = p0 / BM;                      // the half the wave's positions lie in (wave-uniform)
+  ESG_LDS char* const out0 = stg + h * 128 * RS::RB;
+  ESG_LDS char* const out1 = out0 + 64 * RS::RB;
+  const rsrc_t rp0 = make_rsrc(partials + ((size_t)s * rows_total + prow0) * d, (uint32_t)BM * d * 2);
+  const rsrc_t rp1 = make_rsrc(partials + ((size_t)s * rows_total + prow0 + BM) * d, (uint32_t)BM * d * 2);
   const DmaSrc rg = make_dma_src(wg, (uint32_t)F * kbytes);
   const DmaSrc ru = make_dma_src(wu, (uint32_t)F * kbytes);
-  uint32_t voffW[C2::IW];
-  int jW[C2::IW];
+  uint32_t voffW[IW];
+  int jW[IW];
 #pragma unroll
-  for (int i = 0; i < C2::IW; ++i) {
-    const int row = (w * C2::IW + i) * 8 + (lane >> 3);  // neuron row of [Wg; Wu]
+  for (int i = 0; i < IW; ++i) {
+    const int row = (w * IW + i) * 8 + (lane >> 3);  // neuron row of [Wg; Wu]
     const int j = (lane & 7) ^ mn_swz<8>(row);
     const int grow = nb0 + (row < GSB ? row : row - GSB);
     jW[i] = j;
     voffW[i] = (uint32_t)grow * kbytes + j * 16;
   }
   auto issueW = [&](ESG_LDS char* st, int blk) __attribute__((always_inline)) {
-    const uint32_t db0 = (uint32_t)blk * C2::DB2;
+    const uint32_t db0 = (uint32_t)blk * DB2;
 #pragma unroll
-    for (int i = 0; i < C2::IW; ++i) {
-      const bool gate = (w * C2::IW + i) * 8 < GSB;  // wave-uniform
-      dma16(gate ? rg : ru, st + (w * C2::IW + i) * 1024,
+    for (int i = 0; i < IW; ++i) {
+      const bool gate = (w * IW + i) * 8 < GSB;  // wave-uniform
+      dma16(gate ? rg : ru, st + (w * IW + i) * 1024,
             db0 + jW[i] * 8 < (uint32_t)d ? voffW[i] + db0 * 2 : kOOB);
     }
   };
-  const int wm2 = w & 1, wn2 = w >> 1;  // d half of 32 x position slice of PW2
-  int brow2[C2::FN2];
+  auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
+    constexpr int FMD = DB2 / 16;  // d fragments
+    f32x4 acc2[FMD][FN];
+    zero_acc(acc2);
 #pragma unroll
-  for (int j = 0; j < C2::FN2; ++j) brow2[j] = wn2 * C2::PW2 + j * 16 + (lane & 15);
-  const int nblk = (d + C2::DB2 - 1) / C2::DB2;
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t hrow0 = prow0 + h * BM;
-    const rsrc_t rp = make_rsrc(partials + ((size_t)s * rows_total + hrow0) * d, (uint32_t)BM * d * 2);
-    uint32_t row_off[RS::IT];
+    for (int kb = 0; kb < 2 * GSB / 32; ++kb) {
+      // K step kb: neurons 32*kb .. of [dg du] (gate rows first), i.e. the
+      // stacked fragments 2*(kb%4) and 2*(kb%4)+1 of dg (kb < 4) or du
+      const int i0 = 2 * (kb % 4);
+      uint4 b[FN];
 #pragma unroll
-    for (int it = 0; it < RS::IT; ++it) {
-      const int r = RS::row(it, threadIdx.x);
-      row_off[it] = ptoken[hrow0 + r] >= 0 ? (uint32_t)r * d * 2 : kOOB;
+      for (int j = 0; j < FN; ++j) {
+        const uint2 lo = kb < 4 ? dgp[i0][j] : dup[i0][j];
+        const uint2 hi = kb < 4 ? dgp[i0 + 1][j] : dup[i0 + 1][j];
+        b[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+      uint4 a[FMD];
+#pragma unroll
+      for (int m = 0; m < FMD; ++m) a[m] = frag_nrow_acc<8>(cur, kb, m * 16, lane);
+#pragma unroll
+      for (int m = 0; m < FMD; ++m)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma_bf16(acc2[m][j], a[m], b[j]);
     }
+#pragma unroll
+    for (int m = 0; m < FMD; ++m)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc2[m][j][e];
+        RS::put(out0, out1, (p0 % BM) + j * 16 + (lane & 15), m * 16 + (lane >> 4) * 4, v);
+      }
     wait_lgkm0();
-    barrier();  // phase 1 (or the previous half's phase 2) is done with these bytes
-    if (wn == h) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int n = wm * (GSB / C::WM) + i * 16 + (lane >> 4) * 4, n2 = GSB + n;
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int r = j * 16 + (lane & 15);
-          lds_write8(dgu + (n >> 6) * BM * 128 + krow_off(r, (n & 63) >> 3) + (n & 7) * 2, dgp[i][j].x, dgp[i][j].y);
-          lds_write8(dgu + (n2 >> 6) * BM * 128 + krow_off(r, (n2 & 63) >> 3) + (n2 & 7) * 2, dup[i][j].x,
-                     dup[i][j].y);
-        }
-      }
-    }
-    auto compute2 = [&](const ESG_LDS char* cur, int blk) __attribute__((always_inline)) {
-      constexpr int KB = 2 * GSB / 32;
-      uint4 a[KB][C2::FM2];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < C2::FM2; ++i) a[kb][i] = frag_nrow<8>(cur, kb, wm2 * 32 + i * 16, lane);
-      f32x4 acc2[C2::FM2][C2::FN2];
-      zero_acc(acc2);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int c = (kb & 1) * 4 + (lane >> 4);
-        uint4 b[C2::FN2];
-#pragma unroll
-        for (int j = 0; j < C2::FN2; ++j) b[j] = frag_krow(dgu + (kb >> 1) * BM * 128, brow2[j], c);
-#pragma unroll
-        for (int i = 0; i < C2::FM2; ++i)
-#pragma unroll
-          for (int j = 0; j < C2::FN2; ++j) mma_bf16(acc2[i][j], a[kb][i], b[j]);
-      }
-#pragma unroll
-      for (int i = 0; i < C2::FM2; ++i)
-#pragma unroll
-        for (int j = 0; j < C2::FN2; ++j) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc2[i][j][e];
-          RS::put(out0, out1, brow2[j], wm2 * 32 + i * 16 + (lane >> 4) * 4, v);
-        }
-      wait_lgkm0();
-      barrier();  // the whole block is staged
-      RS::template flush<CPOL>(out0, out1, rp, row_off, blk * C2::DB2, d);
-    };
-    // the first step's barrier publishes the half's [dg du] tile
-    kloop<2, 0, C2::STORES2>(nblk, wb0, wb1, wb0, issueW, compute2);
-  }
+    barrier();  // both halves' blocks are staged
+    RS::template flush<CPOL>(stg, stg + 64 * RS::RB, rp0, row_off[0], blk * DB2, d);
+    RS::template flush<CPOL>(stg + 128 * RS::RB, stg + 192 * RS::RB, rp1, row_off[1], blk * DB2, d);
+  };
+  wait_lgkm0();
+  barrier();  // every wave is done with the phase-1 stages
+  kloop_ring<NWB, IW, 2 * RS::IT>((d + DB2 - 1) / DB2, wbuf, issueW, compute2);
 }
 
 // ===========================================================================

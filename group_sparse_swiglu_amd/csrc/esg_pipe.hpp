@@ -151,6 +151,24 @@ __device__ __forceinline__ uint4 frag_nrow(const ESG_LDS char* t, int kb, int n0
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// frag_nrow with the K rows of a 32-row block taken in the order of two
+// stacked 16-row accumulator fragments: lane (q = l/16) gets rows
+// kb*32 + 4q + 0..3, then kb*32 + 16 + 4q + 0..3.  A B operand built from
+// two accumulator fragments of an earlier product (lane q holding their rows
+// 4q .. 4q+3) pairs with it element for element, so the product sums the same
+// 32 K rows, in another order.
+template <int NCH>
+__device__ __forceinline__ uint4 frag_nrow_acc(const ESG_LDS char* t, int kb, int n0, int lane) {
+  const int q = lane >> 4, i = lane & 15;
+  const int row = kb * 32 + q * 4 + (i >> 2);
+  const int colb = n0 * 2 + (i & 3) * 8;
+  const int j = colb >> 4, half = colb & 15;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + mnrow_off<NCH>(row, j) + half));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + mnrow_off<NCH>(row + 16, j) + half));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 // The same transposed fragment (columns m0..m0+15, K rows kb*32 ..) read from
 // a K-row tile (128-byte rows, K-row swizzle): the tile's rows are taken as
 // the K index and its 64 columns as the M/N index.  Used where one staged

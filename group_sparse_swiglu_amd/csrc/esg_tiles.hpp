@@ -273,14 +273,27 @@ struct Dh2 {
   static_assert(IA * NW == NCH && IB * 8 * NW == BMT && IW * 8 * NW == 2 * GSB && FM >= 1, "whole instructions");
 };
 
+// Wave tile of a backward phase 1.  WL = 0: wave w takes neuron slice w % WM
+// (GSB/WM neurons) of position half w / WM (BMT/2 positions); WL = 1: wave w
+// takes all GSB neurons of position slice w (BMT/NW positions).
+template <int GSB, int NW, int BMT, int WL>
+struct DaWave {
+  static constexpr int FM = WL == 0 ? Dh2<GSB, NW, BMT>::FM : GSB / 16;
+  static constexpr int FN = WL == 0 ? Dh2<GSB, NW, BMT>::FN : BMT / NW / 16;
+  static __device__ __forceinline__ int neuron0(int w) { return WL == 0 ? (w % (NW / 2)) * (GSB / (NW / 2)) : 0; }
+  static __device__ __forceinline__ int pos0(int w) { return WL == 0 ? (w / (NW / 2)) * (BMT / 2) : w * (BMT / NW); }
+};
+
 // Phase 1 of a backward tile: dA^T = W_down[:, nb0 .. nb0+GSB)^T . dY_tile^T
-// (K = d) for the 128 bucket positions from prow0 (token ids from ptoken).
-template <int GSB, int NS, int NW = 4, int BMT = BM>
+// (K = d) for the BMT bucket positions from prow0 (token ids from ptoken).
+// acc[i][j]: neurons neuron0 + 16i.., positions pos0 + 16j.. (DaWave).
+template <int GSB, int NS, int NW = 4, int BMT = BM, int WL = 0>
 __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf16_t* __restrict__ wd, int tokens,
                                         int d, int F, int nb0, const int32_t* __restrict__ ptoken, uint32_t prow0,
                                         ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2,
-                                        f32x4 (&acc)[Dh2<GSB, NW, BMT>::FM][Dh2<GSB, NW, BMT>::FN]) {
+                                        f32x4 (&acc)[DaWave<GSB, NW, BMT, WL>::FM][DaWave<GSB, NW, BMT, WL>::FN]) {
   using C = Dh2<GSB, NW, BMT>;
+  using WV = DaWave<GSB, NW, BMT, WL>;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t kbytes = (uint32_t)d * 2;
   const DmaSrc ry = make_dma_src(dy, (uint32_t)tokens * kbytes);
@@ -315,27 +328,27 @@ __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf1
     for (int i = 0; i < C::IB; ++i)
       dma16(ry, st + C::A_BYTES + (w * C::IB + i) * 1024, (kin && voffB[i] != kOOB) ? voffB[i] + kb : kOOB);
   };
-  const int wm = w % C::WM, wn = w / C::WM;
-  int brow[C::FN];
+  const int n0 = WV::neuron0(w);
+  int brow[WV::FN];
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) brow[j] = wn * (BMT / 2) + j * 16 + (lane & 15);
+  for (int j = 0; j < WV::FN; ++j) brow[j] = WV::pos0(w) + j * 16 + (lane & 15);
   zero_acc(acc);
   auto compute = [&](const ESG_LDS char* st, int) __attribute__((always_inline)) {
-    uint4 a[2][C::FM], b[2][C::FN];
+    uint4 a[2][WV::FM], b[2][WV::FN];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int c = kb * 4 + (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) a[kb][i] = frag_nrow<C::NCH>(st, kb, wm * (GSB / C::WM) + i * 16, lane);
+      for (int i = 0; i < WV::FM; ++i) a[kb][i] = frag_nrow<C::NCH>(st, kb, n0 + i * 16, lane);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) b[kb][j] = frag_krow(st + C::A_BYTES, brow[j], c);
+      for (int j = 0; j < WV::FN; ++j) b[kb][j] = frag_krow(st + C::A_BYTES, brow[j], c);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < WV::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) mma_bf16(acc[i][j], a[kb][i], b[kb][j]);
+        for (int j = 0; j < WV::FN; ++j) mma_bf16(acc[i][j], a[kb][i], b[kb][j]);
   };
   kloop<NS, C::L, 0>((d + 63) / 64, st0, st1, st2, issue, compute);
 }
