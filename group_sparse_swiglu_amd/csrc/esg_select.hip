@@ -494,10 +494,16 @@ hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
     // (one 256-row super-chunk: eight waves in eight column groups, two waves
     // per SIMD at one workgroup per CU; 128M select 19 -> 16 us)
     if (groups * rpg > 128 && groups * rpg <= 256) return launch_select_t<T, 32, 2, 8>(a, st);
-    // (128-token blocks run eight waves: one workgroup per CU, two waves per SIMD)
-    if (a.tokens >= 128 * compute_units() &&
-        SelCfg<T, 128, 2>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
-      return launch_select_t<T, 128, 2, kSel128Waves>(a, st);
+    // (128-token blocks run eight waves: one workgroup per CU, two waves per SIMD,
+    // with 256-column super-chunks (four fragments per wave) when their |SiLU|
+    // table fits: each super-chunk streams the x tile again, and at the 1.3B
+    // shape 688 sampled rows then take 3 passes instead of 6: select 171 -> 162 us)
+    if (a.tokens >= 128 * compute_units()) {
+      if (SelCfg<T, 128, 4, true, kSel128Waves>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
+        return launch_select_t<T, 128, 4, kSel128Waves>(a, st);
+      if (SelCfg<T, 128, 2, true, kSel128Waves>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
+        return launch_select_t<T, 128, 2, kSel128Waves>(a, st);
+    }
     return launch_select_t<T, 32, 2>(a, st);  // (eight waves measured slower here: 16 waves per CU)
   } else {
     switch (pick_fnw(groups * rpg)) {
