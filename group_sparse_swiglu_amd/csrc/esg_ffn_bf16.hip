@@ -636,7 +636,7 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
 // Phase 2 (dx partials, Q^T = [W_g; W_u]^T[d-block] . [dg du]^T, K = 256)
 // takes those registers as the B operand: a K step of 32 neurons pairs two
 // stacked fragments, and the weight tile is read in the same neuron order
-// (frag_nrow_acc).  So [dg du] never goes through LDS, and one staged weight
+// (frag_nrow_acc8).  So [dg du] never goes through LDS, and one staged weight
 // d-block serves all 256 positions (a quarter of the LDS the weights and the
 // [dg du] tile took per 128 positions before): three 32 KB weight buffers
 // and 32 KB of row staging for the two halves' partial rows.
@@ -744,7 +744,7 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
 #pragma unroll
   for (int i = 0; i < IW; ++i) {
     const int row = (w * IW + i) * 8 + (lane >> 3);  // neuron row of [Wg; Wu]
-    const int j = (lane & 7) ^ mn_swz<8>(row);
+    const int j = (lane & 7) ^ swz_acc8(row);  // the phase-2 tile's swizzle (frag_nrow_acc8)
     const int grow = nb0 + (row < GSB ? row : row - GSB);
     jW[i] = j;
     voffW[i] = (uint32_t)grow * kbytes + j * 16;
@@ -776,7 +776,7 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
       }
       uint4 a[FMD];
 #pragma unroll
-      for (int m = 0; m < FMD; ++m) a[m] = frag_nrow_acc<8>(cur, kb, m * 16, lane);
+      for (int m = 0; m < FMD; ++m) a[m] = frag_nrow_acc8(cur, kb, m * 16, lane);
 #pragma unroll
       for (int m = 0; m < FMD; ++m)
 #pragma unroll

@@ -157,14 +157,23 @@ __device__ __forceinline__ uint4 frag_nrow(const ESG_LDS char* t, int kb, int n0
 // two accumulator fragments of an earlier product (lane q holding their rows
 // 4q .. 4q+3) pairs with it element for element, so the product sums the same
 // 32 K rows, in another order.
-template <int NCH>
-__device__ __forceinline__ uint4 frag_nrow_acc(const ESG_LDS char* t, int kb, int n0, int lane) {
+// The tile has 128-byte rows (8 chunks) in its own swizzle, swz_acc8: one
+// read instruction touches rows 4q..4q+3 of each lane quarter, i.e. eight
+// consecutive rows per 32 lanes, and each needs two neighbouring chunks.  With
+// 64 four-byte banks a row's parity picks the bank half, so the chunk pairs of
+// the four even (and the four odd) rows of eight must differ, and so must
+// those of four consecutive rows (16 lanes at a time): the pair index
+// (k & 3) ^ bit 2 of k is a bijection on each of these sets.
+__device__ __forceinline__ int swz_acc8(int k) { return ((k & 3) ^ ((k >> 2) & 1)) << 1; }
+__device__ __forceinline__ uint4 frag_nrow_acc8(const ESG_LDS char* t, int kb, int n0, int lane) {
   const int q = lane >> 4, i = lane & 15;
   const int row = kb * 32 + q * 4 + (i >> 2);
   const int colb = n0 * 2 + (i & 3) * 8;
   const int j = colb >> 4, half = colb & 15;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + mnrow_off<NCH>(row, j) + half));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ESG_LDS v4i16*)(t + mnrow_off<NCH>(row + 16, j) + half));
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (ESG_LDS v4i16*)(t + row * 128 + ((j ^ swz_acc8(row)) << 4) + half));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (ESG_LDS v4i16*)(t + (row + 16) * 128 + ((j ^ swz_acc8(row + 16)) << 4) + half));
   const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   return make_uint4(a.x, a.y, b.x, b.y);
 }
