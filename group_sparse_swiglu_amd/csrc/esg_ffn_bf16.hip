@@ -1,6 +1,6 @@
-// Pipelined bf16 kernels of the sparse SwiGLU layer for group blocks of 64 or
-// 128 neurons (eugen_sparse README, "What it does", sparse_swiglu_ffn; the
-// math is the one of esg_ffn.hip, which also serves fp32 and narrow groups).
+// Pipelined bf16 kernels of the sparse SwiGLU layer for group blocks of 32, 64
+// or 128 neurons (eugen_sparse README, "What it does", sparse_swiglu_ffn; the
+// math is the one of esg_ffn.hip, which also serves fp32 and 16-neuron groups).
 //
 // Forward tile (one group sub-block g x 128 padded bucket positions):
 //   phase 1  [Hg; Hu]^T = [W_gate rows; W_up rows] . X_tile^T   (K = d)
@@ -147,8 +147,16 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
     bf16_t* __restrict__ hu_saved, bf16_t* __restrict__ partials, float* __restrict__ part_buf, int kparts) {
   using C = Fwd2<GSB, NW>;
   constexpr int NS = stages_for<GSB>();
-  // with two stages a third W_down buffer follows them
-  __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE + (NS == 2 ? C::W2_BYTES : 0)];
+  // Phase 2 keeps the act tile in st0 and puts the W_down buffers and the row
+  // staging into the stages (with two stages a second W_down buffer follows
+  // them).  32-neuron stages are too small for that: phase 2 then lays act,
+  // two W_down buffers and the staging out one after another.
+  constexpr int RSB = 64 * RowStore<DB, C::NTH>::RB;  // half of the row staging
+  constexpr bool FLAT = GSB < 64;
+  constexpr int P1 = NS * C::STAGE + (NS == 2 ? C::W2_BYTES : 0);
+  constexpr int P2 = C::ACT_BYTES + 2 * C::W2_BYTES + 2 * RSB;
+  static_assert(FLAT || (C::ACT_BYTES + RSB <= C::STAGE && C::W2_BYTES + RSB <= C::STAGE), "stage tails");
+  __shared__ __attribute__((aligned(1024))) char stages_[FLAT && P2 > P1 ? P2 : P1];
   ESG_LDS char* st[NS];
 #pragma unroll
   for (int i = 0; i < NS; ++i) st[i] = (ESG_LDS char*)stages_ + i * C::STAGE;
@@ -265,13 +273,15 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   const int nblk = min(per, nblk_all - blk0);
   const rsrc_t rp = make_rsrc(partials + ((size_t)s * rows_total + prow0) * d, (uint32_t)BM * d * 2);
   // staging of the output block: stage tails the W_down tiles and the act tile leave free
-  ESG_LDS char* out0 = NS == 3 ? st1 + C::W2_BYTES : st0 + C::ACT_BYTES;
-  ESG_LDS char* out1 = NS == 3 ? st[NS - 1] + C::W2_BYTES : st1 + C::W2_BYTES;
+  ESG_LDS char* out0 = FLAT ? st0 + C::ACT_BYTES + 2 * C::W2_BYTES
+                            : (NS == 3 ? st1 + C::W2_BYTES : st0 + C::ACT_BYTES);
+  ESG_LDS char* out1 = FLAT ? out0 + RSB : (NS == 3 ? st[NS - 1] + C::W2_BYTES : st1 + C::W2_BYTES);
   // the stages after st0 are free (the barrier above); the first step's wait
   // covers the epilogue stores (they precede every W_down load), and its
   // barrier publishes the act tile.  The two W_down buffers: st1 and the last
   // stage (three stages) or the region after st1 (two)
-  ESG_LDS char* const wbuf[2] = {st1, NS == 2 ? st1 + C::STAGE : st[NS - 1]};
+  ESG_LDS char* const wbuf[2] = {FLAT ? st0 + C::ACT_BYTES : st1,
+                                 FLAT ? st0 + C::ACT_BYTES + C::W2_BYTES : (NS == 2 ? st1 + C::STAGE : st[NS - 1])};
   fwd_down_blocks<GSB, NW, CPOL>(wd, d, F, nb0, blk0, nblk, act, wbuf, out0, out1, rp, row_off);
 }
 
@@ -881,11 +891,16 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
       return hipGetLastError();
     }
   }
-  // a grid of at most one workgroup per CU: eight waves issue the loads
-  const bool alone = NW == 4 && (long long)ntiles_max * s.nsub() <= kNominalCUs;
-  auto kern = partials_nontemporal(s, ntiles_max) ? fwd2_kernel<GSB, kCpolNontemporal, NW>
-                                                  : (alone ? fwd2_kernel<GSB, 0, 8> : fwd2_kernel<GSB, 0, NW>);
-  hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * (alone ? 8 : NW)), 0, stream, (const bf16_t*)x,
+  auto kern = partials_nontemporal(s, ntiles_max) ? fwd2_kernel<GSB, kCpolNontemporal, NW> : fwd2_kernel<GSB, 0, NW>;
+  int waves = NW;
+  if constexpr (NW == 4 && GSB >= 64) {
+    // a grid of at most one workgroup per CU (cached partial rows): eight waves issue the loads
+    if ((long long)ntiles_max * s.nsub() <= kNominalCUs && !partials_nontemporal(s, ntiles_max)) {
+      kern = fwd2_kernel<GSB, 0, 8>;
+      waves = 8;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * waves), 0, stream, (const bf16_t*)x,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
                      (bf16_t*)partials, nullptr, 0);
@@ -935,7 +950,7 @@ hipError_t dw2_t(const FfnShape& s, const void* x, const void* dy, const int32_t
 // (gathered rows), the weights and the compact activations.  The partial rows
 // are addressed per tile, so their total size is not limited.
 bool bf16_pipelined(const FfnShape& s, int ntiles_max) {
-  if (s.dtype != 1 || (s.gsb() != 64 && s.gsb() != 128)) return false;
+  if (s.dtype != 1 || (s.gsb() != 32 && s.gsb() != 64 && s.gsb() != 128)) return false;
   const unsigned long long lim = 1ull << 31;
   const unsigned long long rows = (unsigned long long)ntiles_max * BM;
   return (unsigned long long)s.tokens * s.d_model * 2 < lim && (unsigned long long)s.d_ff * s.d_model * 2 < lim &&
@@ -952,27 +967,38 @@ hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const v
                        void* hu_saved, void* partials, void* act, hipStream_t stream) {
   if (ntiles_max == 0) return hipSuccess;
   if (!fwd_split(s, ntiles_max)) act = nullptr;
-  return s.gsb() == 64 ? fwd2_t<64>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved,
-                                    partials, act, stream)
-                       : fwd2_t<128>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved,
-                                     partials, act, stream);
+  switch (s.gsb()) {
+    case 32: return fwd2_t<32>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved, partials,
+                               act, stream);
+    case 64: return fwd2_t<64>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved, partials,
+                               act, stream);
+    default: return fwd2_t<128>(s, x, wg, wu, wd, tile_group, ptoken, ntiles_max, pad, hg_saved, hu_saved, partials,
+                                act, stream);
+  }
 }
 
 hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const void* wu, const void* wd,
                         const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, const void* hg_saved,
                         const void* hu_saved, void* dg, void* du, void* act, void* partials, hipStream_t stream) {
   if (ntiles_max == 0) return hipSuccess;
-  return s.gsb() == 64 ? dhdx2_t<64>(s, dy, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, dg, du,
-                                     act, partials, stream)
-                       : dhdx2_t<128>(s, dy, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, dg, du,
-                                      act, partials, stream);
+  switch (s.gsb()) {
+    case 32: return dhdx2_t<32>(s, dy, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, dg, du, act,
+                                partials, stream);
+    case 64: return dhdx2_t<64>(s, dy, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, dg, du, act,
+                                partials, stream);
+    default: return dhdx2_t<128>(s, dy, wg, wu, wd, tile_group, ptoken, ntiles_max, hg_saved, hu_saved, dg, du, act,
+                                 partials, stream);
+  }
 }
 
 hipError_t launch_dw2(const FfnShape& s, const void* x, const void* dy, const int32_t* tile_off, const int32_t* ptoken,
                       int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
                       hipStream_t stream) {
-  return s.gsb() == 64 ? dw2_t<64>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream)
-                       : dw2_t<128>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
+  switch (s.gsb()) {
+    case 32: return dw2_t<32>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
+    case 64: return dw2_t<64>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
+    default: return dw2_t<128>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
+  }
 }
 
 }  // namespace esg

@@ -131,6 +131,10 @@ template <>
 __device__ __forceinline__ int mn_swz<8>(int k) {  // 128-byte rows: row parity picks the bank half
   return (((k & 1) ^ ((k >> 3) & 1)) << 1) | (((k >> 1) & 1) << 2) | ((k >> 4) & 1);
 }
+template <>
+__device__ __forceinline__ int mn_swz<4>(int k) {  // 64-byte rows: rows k and k+2 (and k+8) share banks
+  return (((k >> 1) & 1) ^ ((k >> 3) & 1)) << 1;
+}
 template <int NCH>
 __device__ __forceinline__ int mnrow_off(int k, int j) {
   return k * NCH * 16 + ((j ^ mn_swz<NCH>(k)) << 4);

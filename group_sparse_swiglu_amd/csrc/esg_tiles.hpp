@@ -149,7 +149,7 @@ struct Fwd2 {
   static constexpr int L = IA + IB;
   static constexpr int FMP = GSB / WM / 16;    // gate/up fragment pairs per wave
   static constexpr int FN = 4;                 // 64 positions per wave
-  static constexpr int KSUB = GSB / 64;        // 64-wide K sub-tiles of the group width
+  static constexpr int KSUB = GSB >= 64 ? GSB / 64 : 1;  // 64-wide K sub-tiles of the group width (32: half of one)
   static constexpr int ACT_BYTES = KSUB * BM * 128;
   static constexpr int W2_BYTES = KSUB * DB * 128;
   static constexpr int IW2 = DB / (8 * NW);    // W_down DMA instructions per lane per K sub-tile

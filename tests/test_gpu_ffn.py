@@ -42,6 +42,8 @@ def _full_compare(inp, idx, dtype):
 WORKLOAD_FULL = [
     ("tiny_f32", 256, 128, 512, 32, 4, "f32", None, False),
     ("s128m_bf16", 8192, 768, 2048, 64, 8, "bf16", 8, True),
+    # the eugen_sparse README's layer (groups of 32, 8 of 128 active) at 1024 tokens
+    ("gs32_d512_1k", 1024, 512, 4096, 32, 8, "bf16", 8, True),
 ]
 
 
@@ -59,6 +61,11 @@ WORKLOAD_SAMPLED = [
     ("s1p3b_bf16", 32768, 2048, 5504, 128, 11, "bf16", 16, True),
     # 64-neuron groups with partial rows past the cached-store limit (about 270 MB)
     ("gs64_partials_270mb", 16384, 2048, 4096, 64, 4, "bf16", 8, True),
+    # at most 256 tiles (one workgroup per CU) whose partial rows (213 MB at d 4096)
+    # still pass the cached-store limit: the four-wave nontemporal forward
+    ("gs64_d4096_one_round", 12000, 4096, 1024, 64, 2, "bf16", 16, True),
+    # the eugen_sparse README's layer at its full bench size: 32-neuron blocks
+    ("gs32_d512_readme", 16384, 512, 4096, 32, 8, "bf16", 8, True),
 ]
 
 
