@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel HIP events")
+    ap.add_argument("--second-stream", action="store_true",
+                    help="run the weight gradients on a second stream beside the dx sum "
+                         "(esg_sparse_swiglu_bwd_overlap); by default they follow it on the step's stream")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--inference", action="store_true",
@@ -679,9 +682,9 @@ def measure(args, w, dev, cpu=True):
                         device=dev)
     ws = {}
     saved = [None]
-    # a second stream for the weight gradients beside the dx sum (the library
-    # creates none of its own)
-    AUX = torch.cuda.Stream(device=dev)
+    # optionally a second stream for the weight gradients beside the dx sum
+    # (the library creates none of its own)
+    AUX = torch.cuda.Stream(device=dev) if args.second_stream else None
 
     def step():
         if args.inference:
@@ -806,6 +809,7 @@ def measure(args, w, dev, cpu=True):
                             else "dense fwd+bwd (recompute)" if w.dense else
                             "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else ""))},
         "launch": "hip_graph_replay" if graph is not None else "eager",
+        "backward_streams": 2 if AUX is not None else 1,
         "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
         "active_mfma_frac": round(active / (elapsed / args.steps) / 1e12 / peak, 4),
         "roofline": roofline,

@@ -814,18 +814,28 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
 // ===========================================================================
 // Backward weight gradients (see dw2_body).
 // ===========================================================================
+// Waves of the weight-gradient workgroup: eight for 128-neuron blocks (one
+// workgroup per CU: two waves per SIMD, each holding an eighth of the output),
+// four for narrower blocks (two workgroups per CU).
 template <int GSB>
-__global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
+constexpr int dw_waves() {
+  return GSB >= 128 ? 8 : 4;
+}
+
+template <int GSB>
+__global__ __launch_bounds__(64 * dw_waves<GSB>(), GSB >= 128 ? 1 : 2) void dw2_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, int tokens, int d, int F, int gs, int nsub,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ ptoken, uint32_t rows_total,
     const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du, const bf16_t* __restrict__ act,
     bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu, bf16_t* __restrict__ dwd) {
   constexpr int XS = dw_subtiles<GSB>();
-  using C = Dw2<GSB, XS>;
+  constexpr int NWD = dw_waves<GSB>();
+  using C = Dw2<GSB, XS, NWD>;
   constexpr int NS = XS == 2 ? 2 : stages_for<GSB>();
   __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE];  // no placeholder for a third stage
   DwWork wk;
-  if (!dw_work(blockIdx.x, 2 * (F / gs) * nsub, (d + C::DW - 1) / C::DW, wk)) return;
+  const int units = 2 * (F / gs) * nsub, ndb = (d + C::DW - 1) / C::DW;
+  if (!(NWD == 8 ? dw_work_xcd(blockIdx.x, units, ndb, wk) : dw_work(blockIdx.x, units, ndb, wk))) return;
   const int g = (wk.unit >> 1) / nsub, s = (wk.unit >> 1) % nsub;
   const int db0 = wk.db * C::DW;
   const int nb0 = g * gs + s * GSB;
@@ -836,11 +846,11 @@ __global__ __launch_bounds__(NT, GSB >= 128 ? 1 : 2) void dw2_kernel(
   ESG_LDS char* st1 = st0 + C::STAGE;
   ESG_LDS char* st2 = NS == 3 ? st1 + C::STAGE : st0;
   if ((wk.unit & 1) == 0)
-    dw2_body<GSB, 0, NS, 0, XS>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du, pbytes,
-                         dwg, dwu, db0, st0, st1, st2);
+    dw2_body<GSB, 0, NS, 0, XS, NWD>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du,
+                                     pbytes, dwg, dwu, db0, st0, st1, st2);
   else
-    dw2_body<GSB, 1, NS, 0, XS>(dy, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, act, act, pbytes,
-                         dwd, dwd, db0, st0, st1, st2);
+    dw2_body<GSB, 1, NS, 0, XS, NWD>(dy, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, act, act,
+                                     pbytes, dwd, dwd, db0, st0, st1, st2);
 }
 
 // ===========================================================================
@@ -935,9 +945,11 @@ hipError_t dw2_t(const FfnShape& s, const void* x, const void* dy, const int32_t
                  int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
                  hipStream_t stream) {
   LaunchTimer timer("bwd_dw", stream);
-  const dim3 grid(dw_grid(2 * s.groups() * s.nsub(), (s.d_model + 128 * dw_subtiles<GSB>() - 1) /
-                                                         (128 * dw_subtiles<GSB>())));  // order: dw_work
-  hipLaunchKernelGGL((dw2_kernel<GSB>), grid, dim3(NT), 0, stream, (const bf16_t*)x, (const bf16_t*)dy, s.tokens,
+  const int units = 2 * s.groups() * s.nsub();
+  const int ndb = (s.d_model + 128 * dw_subtiles<GSB>() - 1) / (128 * dw_subtiles<GSB>());
+  const dim3 grid(dw_waves<GSB>() == 8 ? dw_grid_xcd(units, ndb) : dw_grid(units, ndb));  // order: dw_work(_xcd)
+  hipLaunchKernelGGL((dw2_kernel<GSB>), grid, dim3(64 * dw_waves<GSB>()), 0, stream, (const bf16_t*)x,
+                     (const bf16_t*)dy, s.tokens,
                      s.d_model, s.d_ff, s.group_size, s.nsub(), tile_off, ptoken, (uint32_t)rows_total,
                      (const bf16_t*)dg, (const bf16_t*)du, (const bf16_t*)act, (bf16_t*)dwg, (bf16_t*)dwu,
                      (bf16_t*)dwd);

@@ -367,27 +367,40 @@ __device__ __forceinline__ void da_tile(const bf16_t* __restrict__ dy, const bf1
 // XS 128-d sub-tiles of the gathered operand per stage: a workgroup covers
 // DW = 128*XS d of one neuron block, so the packed dg/du/a rows (which every
 // d-block of the block reads again) are read ceil(d/DW) times.
-template <int GSB, int XS = 1>
+// NWD wavefronts: 4 (one per SIMD, each holding a quarter of the output), or
+// 8 (two per SIMD, an eighth each: kind 0 splits the d range in four, kind 1
+// in four along d as well).
+template <int GSB, int XS = 1, int NWD = 4>
 struct Dw2 {
+  static constexpr int NTH = 64 * NWD;
   static constexpr int DW = 128 * XS;
   static constexpr int NCHP = GSB / 8;           // chunks per position row of dg/du/a
   static constexpr int X_SUB = 64 * 256;         // N-row: 64 positions x 128 d
   static constexpr int X_BYTES = XS * X_SUB;
   static constexpr int P_BYTES = 64 * GSB * 2;   // N-row: 64 positions x GSB neurons
   static constexpr int STAGE = X_BYTES + 2 * P_BYTES;
-  static constexpr int IX = 4 * XS;
-  static constexpr int IP = NCHP / 4;
+  static constexpr int IXS = 16 / NWD;           // x DMA instructions per lane per 128-d sub-tile
+  static constexpr int IX = IXS * XS;
+  static constexpr int IP = NCHP * 4 / NWD / 4;  // packed-tile DMA instructions per lane
   static constexpr int L0 = IX + 2 * IP, L1 = IX + IP;
-  static constexpr int FM0 = 4 * XS, FN0 = GSB / 16;  // kind 0 wave tile: 64*XS d x GSB neurons
-  static constexpr int FM1 = GSB / 32, FN1 = 4 * XS;  // kind 1 wave tile: GSB/2 neurons x 64*XS d
+  static constexpr int WM0 = NWD / 2;            // kind 0: d slices x {gate, up}
+  static constexpr int FM0 = 8 * XS / WM0, FN0 = GSB / 16;   // kind 0 wave tile: DW/WM0 d x GSB neurons
+  static constexpr int WN1 = NWD / 2;            // kind 1: neuron halves x d slices
+  static constexpr int FM1 = GSB / 32, FN1 = 8 * XS / WN1;   // kind 1 wave tile: GSB/2 neurons x DW/WN1 d
+  static_assert(IXS >= 1 && IP >= 1 && FM0 >= 1 && FN1 >= 1, "whole instructions and fragments");
 };
 
 // Order of the weight-gradient workgroups.  A "unit" is one (neuron block,
-// kind) pair; its ndb d-blocks read the same packed dg/du/a rows.  Workgroup L
-// takes neuron block L % GB, then d-block, then kind (GB = units / 2), so the
-// workgroups in flight together spread over all neuron blocks.  (Keeping one
-// unit's d-blocks together on one XCD measured slower on the 1.3B shapes.)
-// Returns false for workgroups past the last unit.
+// kind) pair; its ndb d-blocks read the same packed dg/du/a rows.
+// dw_work: workgroup L takes neuron block L % GB, then d-block, then kind
+// (GB = units / 2), so the workgroups in flight together spread over all
+// neuron blocks (four-wave workgroups, 64-neuron and dense blocks).
+// dw_work_xcd: workgroups go to the 8 XCDs round-robin, so workgroup L runs
+// on XCD L % 8; XCD x takes the flat items [x*per, (x+1)*per) in order (unit
+// major, d-block minor), so a unit's d-blocks run together in one L2 and read
+// its packed rows from there (eight-wave 128-neuron workgroups: at the 1.3B
+// shape 4.24 -> 3.26 GB of L2 misses; with four waves it measured slower).
+// Both return false for workgroups past the last item.
 struct DwWork {
   int unit, db;
 };
@@ -400,6 +413,15 @@ __device__ __forceinline__ bool dw_work(int L, int units, int ndb, DwWork& w) {
   return true;
 }
 inline int dw_grid(int units, int ndb) { return units * ndb; }
+__device__ __forceinline__ bool dw_work_xcd(int L, int units, int ndb, DwWork& w) {
+  const int n = units * ndb, per = (n + 7) / 8;
+  const int f = (L % 8) * per + L / 8;
+  if (f >= n) return false;
+  w.unit = f / ndb;  // neuron block unit / 2, kind unit % 2
+  w.db = f % ndb;
+  return true;
+}
+inline int dw_grid_xcd(int units, int ndb) { return (units * ndb + 7) / 8 * 8; }
 
 template <int MODE>
 __device__ __forceinline__ void store_dw(bf16_t* out, float* acc32, float (&v)[4]) {
@@ -421,16 +443,20 @@ __device__ __forceinline__ int dw_perm(int r) { return (r & ~15) | ((r & 3) << 2
 // f0/f1; 3 adds f0/f1 and stores bf16 (K split over consecutive launches, in
 // a fixed order).  Ids of the K positions come from ptoken[pid0 ..], their
 // packed dg/du/a rows start at row p0; np positions (a multiple of 64).
-template <int GSB, int KIND, int NS, int MODE = 0, int XS = 1>
+template <int GSB, int KIND, int NS, int MODE = 0, int XS = 1, int NWD = 4>
 __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tokens, int d, int F, int nb0,
                                          const int32_t* __restrict__ ptoken, int pid0, int p0, int np,
                                          size_t sub_el, float* __restrict__ f0, float* __restrict__ f1,
                                          const bf16_t* __restrict__ pa, const bf16_t* __restrict__ pb,
                                          uint32_t pbytes, bf16_t* __restrict__ out0, bf16_t* __restrict__ out1,
                                          int db0, ESG_LDS char* st0, ESG_LDS char* st1, ESG_LDS char* st2) {
-  using C = Dw2<GSB, XS>;
+  using C = Dw2<GSB, XS, NWD>;
   constexpr int NP = KIND == 0 ? 2 : 1;  // packed operand tiles per stage
   constexpr int L = KIND == 0 ? C::L0 : C::L1;
+  constexpr int IXS = C::IXS;
+  // row order within a stage: four waves use perm (positions 16w + 4q + i in
+  // the rows of instruction i); eight waves keep positions in row order
+  constexpr bool PERM = NWD == 4;
   const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t kbytes = (uint32_t)d * 2;
   const DmaSrc rz = make_dma_src(src, (uint32_t)tokens * kbytes);
@@ -439,18 +465,19 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
   const int nk = np / 64;
 
   // gathered tile (x or dY): instruction i of wave w fills LDS rows
-  // (w*4 + i)*4 + q, q = lane/16, holding positions 16w + 4q + i
+  // (w*IXS + i)*4 + q, q = lane/16, holding positions 16w + 4q + i (four
+  // waves) or the rows' own positions (eight)
   const int q = lane >> 4;
-  int jz[4];
+  int jz[IXS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) jz[i] = (lane & 15) ^ mn_swz<16>((w * 4 + i) * 4 + q);
+  for (int i = 0; i < IXS; ++i) jz[i] = (lane & 15) ^ mn_swz<16>((w * IXS + i) * 4 + q);
   // packed tiles (dg / du / a rows of positions)
   uint32_t voffP[C::IP];
 #pragma unroll
   for (int i = 0; i < C::IP; ++i) {
     const int R = (w * C::IP + i) * (64 / C::NCHP) + lane / C::NCHP;
     const int j = (lane % C::NCHP) ^ mn_swz<C::NCHP>(R);
-    voffP[i] = (uint32_t)((sub_el + (size_t)(p0 + dw_perm(R)) * GSB) * 2) + j * 16;
+    voffP[i] = (uint32_t)((sub_el + (size_t)(p0 + (PERM ? dw_perm(R) : R)) * GSB) * 2) + j * 16;
   }
   // The wave's 16 token ids of a tile come through the scalar unit (constant
   // address space: ptoken is not written while this kernel runs), so that
@@ -462,11 +489,12 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
   struct IdBlock {
     i32x4 v[4];
   };
+  // the wave's 64/NWD ids of a tile
   auto load_ids = [&](int kt) __attribute__((always_inline)) {
-    const cint4* src = (const cint4*)(ptoken + pid0 + kt * 64 + w * 16);
+    const cint4* src = (const cint4*)(ptoken + pid0 + kt * 64 + w * (64 / NWD));
     IdBlock r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = src[i];
+    for (int i = 0; i < 16 / NWD; ++i) r.v[i] = src[i];
     return r;
   };
   IdBlock next_ids;  // ids of the next tile to issue, loaded one issue ahead
@@ -474,20 +502,27 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
   auto issue = [&](ESG_LDS char* st, int kt) __attribute__((always_inline)) {
     const IdBlock r = next_ids;
     if (kt + 1 < nk) next_ids = load_ids(kt + 1);
-    int tk[4];
+    int tk[IXS];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {  // branch-free pick of r.v[q][c]
-      const int lo = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[1][c] : r.v[0][c];
-      const int hi = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[3][c] : r.v[2][c];
-      tk[c] = q >= 2 ? hi : lo;
+    for (int c = 0; c < IXS; ++c) {
+      if constexpr (PERM) {  // branch-free pick of r.v[q][c]
+        const int lo = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[1][c] : r.v[0][c];
+        const int hi = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[3][c] : r.v[2][c];
+        tk[c] = q >= 2 ? hi : lo;
+      } else {  // row (w*IXS + c)*4 + q holds position 8w + 4c + q: r.v[c][q]
+        const int lo = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[c][1] : r.v[c][0];
+        const int hi = __builtin_amdgcn_ubfe(q, 0, 1) ? r.v[c][3] : r.v[c][2];
+        tk[c] = q >= 2 ? hi : lo;
+      }
     }
 #pragma unroll
     for (int x = 0; x < XS; ++x)  // 128-d sub-tile x: d from db0 + 128x
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < IXS; ++i) {
         const int dx = db0 + x * 128 + jz[i] * 8;
         const bool ok = tk[i] >= 0 && dx < d;
-        dma16(rz, st + x * C::X_SUB + (w * 4 + i) * 1024, ok ? (uint32_t)tk[i] * kbytes + (uint32_t)dx * 2 : kOOB);
+        dma16(rz, st + x * C::X_SUB + (w * IXS + i) * 1024,
+              ok ? (uint32_t)tk[i] * kbytes + (uint32_t)dx * 2 : kOOB);
       }
     const uint32_t kofs = (uint32_t)kt * 64 * GSB * 2;
 #pragma unroll
@@ -499,7 +534,10 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
     }
   };
 
-  const int wm = w & 1, wn = w >> 1;
+  // kind 0: wave (wm, wn) = (d slice of DW/WM0, gate or up);
+  // kind 1: wave (wm, wn) = (neuron half, d slice of DW/WN1)
+  const int wm = KIND == 0 ? w % C::WM0 : w & 1;
+  const int wn = KIND == 0 ? w / C::WM0 : w >> 1;
   constexpr int FM = KIND == 0 ? C::FM0 : C::FM1;
   constexpr int FN = KIND == 0 ? C::FN0 : C::FN1;
   f32x4 acc[FM][FN];
@@ -511,7 +549,7 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
       if constexpr (KIND == 0) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int dl = wm * 64 * XS + i * 16;  // d within the workgroup's DW
+          const int dl = wm * (C::DW / C::WM0) + i * 16;  // d within the workgroup's DW
           a[kb][i] = frag_nrow<16>(st + (dl >> 7) * C::X_SUB, kb, dl & 127, lane);
         }
         const ESG_LDS char* tb = st + C::X_BYTES + wn * C::P_BYTES;
@@ -523,7 +561,7 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
           a[kb][i] = frag_nrow<C::NCHP>(st + C::X_BYTES, kb, wm * (GSB / 2) + i * 16, lane);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int dl = wn * 64 * XS + j * 16;
+          const int dl = wn * (C::DW / C::WN1) + j * 16;
           b[kb][j] = frag_nrow<16>(st + (dl >> 7) * C::X_SUB, kb, dl & 127, lane);
         }
       }
@@ -540,7 +578,7 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
   if constexpr (KIND == 0) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int dd = db0 + wm * 64 * XS + i * 16 + (lane >> 4) * 4;
+      const int dd = db0 + wm * (C::DW / C::WM0) + i * 16 + (lane >> 4) * 4;
       if (dd >= d) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -559,7 +597,7 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
       const int n = wm * (GSB / 2) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int dd = db0 + wn * 64 * XS + j * 16 + (lane & 15);
+        const int dd = db0 + wn * (C::DW / C::WN1) + j * 16 + (lane & 15);
         if (dd >= d) continue;
         float v[4];
 #pragma unroll
