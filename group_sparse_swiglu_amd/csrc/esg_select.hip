@@ -166,6 +166,52 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
         if (counts) atomicAdd(&cnt[lane], 1);
       }
     }
+  } else if (groups <= 256) {
+    // one token per wave at a time; lane l holds groups l, l+64, l+128, l+192
+    // in registers and every other score comes from a lane read with a
+    // constant lane index (no LDS round trip per compared group)
+    for (int r = wave; r < BM; r += NW) {
+      const int t = t0 + r;
+      if (t >= tokens) break;
+      const float* row = E + r * ES;
+      float sv[4];
+      int beat[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sv[c] = c * 64 + lane < groups ? row[c * 64 + lane] : 0.0f;
+        beat[c] = 0;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c * 64 >= groups) break;  // wave-uniform
+        const int lmax = min(64, groups - c * 64);
+#pragma unroll 8
+        for (int l = 0; l < lmax; ++l) {  // l: a uniform (scalar) lane index
+          const int qg = c * 64 + l;
+          const float sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[c]), l));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (e * 64 >= groups) break;  // wave-uniform
+            const int g = e * 64 + lane;
+            beat[e] += (sq > sv[e]) || (sq == sv[e] && qg < g);
+          }
+        }
+      }
+      int base = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e * 64 >= groups) break;  // wave-uniform
+        const int g = e * 64 + lane;
+        const bool sel = g < groups && beat[e] < k;
+        const uint64_t m = __ballot(sel);
+        const int pos = base + __popcll(m & lt);
+        if (sel && pos < k) {  // NaN scores could select more than k: never write past the row
+          idx_out[(size_t)t * k + pos] = g;
+          if (counts) atomicAdd(&cnt[g], 1);
+        }
+        base += __popcll(m);
+      }
+    }
   } else {
     for (int r = wave; r < BM; r += NW) {
       const int t = t0 + r;

@@ -41,6 +41,9 @@ CASES = [
     ("rows256_t16384", 16384, 256, 2048, 64, 6, "bf16", 8, True, None),
     ("bm128_g24_ragged", 32900, 128, 1536, 64, 5, "bf16", 4, True, None),
     ("bm128_g100", 32768, 64, 1600, 16, 4, "bf16", 1, True, None),
+    # the eugen_sparse README's layer: 128 groups of 32, 8 sampled rows each
+    ("readme_g128", 16384, 512, 4096, 32, 8, "bf16", 8, True, None),
+    ("g200_ragged", 333, 64, 3200, 16, 9, "bf16", 4, True, None),
 ]
 
 
@@ -75,10 +78,14 @@ def test_select_batch_invariant_and_deterministic():
     assert torch.equal(a[1000:3001], c)
 
 
-def test_select_exact_ties_take_lowest_ids():
+@pytest.mark.parametrize("G", [6, 100, 200])
+def test_select_exact_ties_take_lowest_ids(G):
+    """Every group identical: the k lowest ids win (the rank rule's tie
+    break), for the one-wave ranking (G <= 64) and the lane-held scores of
+    64 < G <= 256."""
     require_gpu()
-    note("select exact ties")
-    T, d, gs, G, k = 70, 64, 16, 6, 3
+    note(f"select exact ties G={G}")
+    T, d, gs, k = 70, 64, 16, 3
     inp = inputs(T, d, gs * G, gs, "bf16", seed=4, bias=False)
     inp["wg"] = inp["wg"][:gs].repeat(G, 1)           # every group identical
     idx, counts = _select(inp, k)
