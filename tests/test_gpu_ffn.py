@@ -66,6 +66,8 @@ WORKLOAD_SAMPLED = [
     ("gs64_d4096_one_round", 12000, 4096, 1024, 64, 2, "bf16", 16, True),
     # the eugen_sparse README's layer at its full bench size: 32-neuron blocks
     ("gs32_d512_readme", 16384, 512, 4096, 32, 8, "bf16", 8, True),
+    # groups of 256 (two 128-neuron sub-blocks) past the pair threshold (1039 tiles x 2)
+    ("gs256_pairs_two_subblocks", 32768, 1024, 4096, 256, 4, "bf16", 16, True),
 ]
 
 
