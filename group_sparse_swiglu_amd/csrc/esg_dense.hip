@@ -410,8 +410,10 @@ __global__ __launch_bounds__(64 * DDx::NW, 1) void dense_dx_kernel(const bf16_t*
 
 // Weight gradients of one chunk: the sparse path's dW tiles with the chunk's
 // tokens as the K positions of every neuron block.
+constexpr int kDenseDwWaves = 8;  // two waves per SIMD, as the sparse 128-neuron weight gradients
+
 template <int MODE>
-__global__ __launch_bounds__(NT, 1) void dense_dw_kernel(const bf16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kDenseDwWaves, 1) void dense_dw_kernel(const bf16_t* __restrict__ x,
                                                          const bf16_t* __restrict__ dy, int tokens, int d, int F,
                                                          const int32_t* __restrict__ ptoken, int tc_pad, int np,
                                                          const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du,
@@ -420,23 +422,23 @@ __global__ __launch_bounds__(NT, 1) void dense_dw_kernel(const bf16_t* __restric
                                                          bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu,
                                                          bf16_t* __restrict__ dwd) {
   // 256 d per workgroup (two 128-d sub-tiles, two 64 KB stages): the packed
-  // dg/du/a rows are read d/256 times
-  using C = Dw2<NB, DENSE_DW_XS>;
+  // dg/du/a rows are read d/256 times; items in the XCD-local order
+  using C = Dw2<NB, DENSE_DW_XS, kDenseDwWaves>;
   __shared__ __attribute__((aligned(1024))) char st0_[C::STAGE], st1_[C::STAGE];
   ESG_LDS char* st0 = (ESG_LDS char*)st0_;
   ESG_LDS char* st1 = (ESG_LDS char*)st1_;
   const int nblk = (F + NB - 1) / NB;
   DwWork wk;
-  if (!dw_work(blockIdx.x, 2 * nblk, (d + C::DW - 1) / C::DW, wk)) return;
+  if (!dw_work_xcd(blockIdx.x, 2 * nblk, (d + C::DW - 1) / C::DW, wk)) return;
   const int blk = wk.unit >> 1, db0 = wk.db * C::DW;
   const uint32_t pbytes = (uint32_t)((size_t)nblk * tc_pad * NB * 2);
   const int p0 = blk * tc_pad;
   if ((wk.unit & 1) == 0)
-    dw2_body<NB, 0, 2, MODE, DENSE_DW_XS>(x, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fg, fu, dg, du, pbytes,
-                                          dwg, dwu, db0, st0, st1, st1);
+    dw2_body<NB, 0, 2, MODE, DENSE_DW_XS, kDenseDwWaves>(x, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fg, fu,
+                                                         dg, du, pbytes, dwg, dwu, db0, st0, st1, st1);
   else
-    dw2_body<NB, 1, 2, MODE, DENSE_DW_XS>(dy, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fd, fd, act, act, pbytes, dwd,
-                             dwd, db0, st0, st1, st1);
+    dw2_body<NB, 1, 2, MODE, DENSE_DW_XS, kDenseDwWaves>(dy, tokens, d, F, blk * NB, ptoken, 0, p0, np, 0, fd, fd,
+                                                         act, act, pbytes, dwd, dwd, db0, st0, st1, st1);
 }
 
 }  // namespace
@@ -522,10 +524,11 @@ hipError_t launch_dense_bwd(const FfnShape& s, const void* dy, const void* x, co
     }
     {
       LaunchTimer timer("dense_dw", stream);
-      const dim3 grid(dw_grid(2 * L.nblk, (d + 128 * DENSE_DW_XS - 1) / (128 * DENSE_DW_XS)));  // order: dw_work
+      const dim3 grid(dw_grid_xcd(2 * L.nblk, (d + 128 * DENSE_DW_XS - 1) / (128 * DENSE_DW_XS)));  // order: dw_work_xcd
       const int mode = L.chunks == 1 ? 0 : (c == 0 ? 1 : (c == L.chunks - 1 ? 3 : 2));
 #define ESG_DW(M)                                                                                                  \
-  hipLaunchKernelGGL(dense_dw_kernel<M>, grid, dim3(NT), 0, stream, (const bf16_t*)x, (const bf16_t*)dy, s.tokens, \
+  hipLaunchKernelGGL(dense_dw_kernel<M>, grid, dim3(64 * kDenseDwWaves), 0, stream, (const bf16_t*)x,            \
+                     (const bf16_t*)dy, s.tokens,                                                                  \
                      d, F, ptoken, L.tc, tiles * kTileRows, dg, du, act, fg, fu, fd, (bf16_t*)dwg, (bf16_t*)dwu,   \
                      (bf16_t*)dwd)
       if (mode == 0)
