@@ -49,9 +49,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true", help="skip the per-kernel HIP events")
-    ap.add_argument("--second-stream", action="store_true",
-                    help="run the weight gradients on a second stream beside the dx sum "
-                         "(esg_sparse_swiglu_bwd_overlap); by default they follow it on the step's stream")
+    ap.add_argument("--backward-streams", choices=["auto", "1", "2"], default="auto",
+                    help="1: the weight gradients follow the dx sum on the step's stream; 2: they run on a second "
+                         "stream beside it (esg_sparse_swiglu_bwd_overlap); auto: both step graphs are captured, "
+                         "timed for a few replays each, and the faster one is timed (the line reports the choice)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replaying the step as one HIP graph")
     ap.add_argument("--inference", action="store_true",
@@ -684,7 +685,12 @@ def measure(args, w, dev, cpu=True):
     saved = [None]
     # optionally a second stream for the weight gradients beside the dx sum
     # (the library creates none of its own)
-    AUX = torch.cuda.Stream(device=dev) if args.second_stream else None
+    AUX2 = torch.cuda.Stream(device=dev)
+    uses_aux = not (args.inference or w.dense)
+    stream_modes = [1, 2] if (args.backward_streams == "auto" and uses_aux) else \
+        [int(args.backward_streams) if args.backward_streams != "auto" and uses_aux else 1]
+    aux_of = {1: None, 2: AUX2}
+    cur = {"aux": aux_of[stream_modes[0]]}
 
     def step():
         if args.inference:
@@ -706,28 +712,54 @@ def measure(args, w, dev, cpu=True):
                               workspace=SELWS)
         _, ctx = E.sparse_swiglu_fwd(X, WG, WU, WD, IDX, w.group_size, workspace=ws, out=Y, saved=saved[0])
         saved[0] = ctx.saved
-        E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS, aux_stream=AUX)
+        E.sparse_swiglu_bwd(DY, X, WG, WU, WD, ctx, workspace=ws, outs=GRADS, aux_stream=cur["aux"])
         if w.bias_update:
             E.update_load_balance_bias_from_routing(BIAS, EMA, ctx, w.k / G, 1e-3, 0.5, 0.99)
 
-    for _ in range(args.warmup):
-        step()
+    for mode in stream_modes:
+        cur["aux"] = aux_of[mode]
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
 
     # Headline: the step's launches captured once as a HIP graph and replayed (the library enqueues
-    # kernels only: no host synchronisation, allocation or memset inside a step).
-    graph = None
-    if not args.no_graph:
+    # kernels only: no host synchronisation, allocation or memset inside a step).  With two backward
+    # arrangements to choose from, each is captured and timed for a few replays, and the faster is timed.
+    graphs = {}
+    for mode in stream_modes:
+        cur["aux"] = aux_of[mode]
+        if args.no_graph:
+            graphs[mode] = None
+            continue
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             step()
         torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             step()
-        graph.replay()
+        g.replay()
         torch.cuda.synchronize()
+        graphs[mode] = g
+    trial_ms = {}
+    if len(stream_modes) > 1:
+        n_trial = max(3, min(10, args.steps // 4))
+        for _rep in range(3):   # alternate the two, keep each one's best of three
+            for mode in stream_modes:
+                cur["aux"] = aux_of[mode]
+                run = graphs[mode].replay if graphs[mode] is not None else step
+                run()
+                torch.cuda.synchronize()
+                tt = time.perf_counter()
+                for _ in range(n_trial):
+                    run()
+                torch.cuda.synchronize()
+                ms = 1e3 * (time.perf_counter() - tt) / n_trial
+                trial_ms[mode] = min(ms, trial_ms.get(mode, ms))
+    chosen = min(trial_ms, key=trial_ms.get) if trial_ms else stream_modes[0]
+    cur["aux"] = aux_of[chosen]
+    graph = graphs[chosen]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -809,7 +841,8 @@ def measure(args, w, dev, cpu=True):
                             else "dense fwd+bwd (recompute)" if w.dense else
                             "select+bucket+fwd+bwd" + ("+bias_update" if w.bias_update else ""))},
         "launch": "hip_graph_replay" if graph is not None else "eager",
-        "backward_streams": 2 if AUX is not None else 1,
+        "backward_streams": chosen if uses_aux else None,
+        "backward_streams_trial_ms": {str(m): round(v, 4) for m, v in trial_ms.items()} or None,
         "active_tflops": round(active / (elapsed / args.steps) / 1e12, 2),
         "active_mfma_frac": round(active / (elapsed / args.steps) / 1e12 / peak, 4),
         "roofline": roofline,

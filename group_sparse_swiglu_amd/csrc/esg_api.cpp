@@ -48,7 +48,8 @@ struct Layout {
   size_t rows = 0;       // padded positions
   size_t offsets = 0, tile_off = 0, tile_group = 0, ptoken = 0, pinv = 0, hg = 0, hu = 0, saved = 0;
   size_t f_bucket = 0, f_part = 0, f_route = 0, f_act = 0, fwd = 0;
-  size_t b_dg = 0, b_du = 0, b_act = 0, b_part = 0, bwd = 0;
+  size_t b_dg = 0, b_du = 0, b_act = 0, b_part = 0, b_slots = 0, bwd = 0;
+  int cht = 0;           // weight-gradient chunk tiles (dw_chunk_tiles)
 };
 
 // train: the layout of a forward that saves for the backward, whose groups are
@@ -81,6 +82,8 @@ Layout make_layout(const FfnShape& s, bool train = true) {
   L.b_du = o;       o = align256(o + act_bytes);
   L.b_act = o;      o = align256(o + act_bytes);
   L.b_part = o;     o = align256(o + part_bytes);
+  L.cht = train ? dw_chunk_tiles(s, L.mt, tile_pad(s)) : 0;
+  L.b_slots = o;    o = align256(o + dw_slot_bytes(s, L.rows, L.cht));
   L.bwd = o;
   return L;
 }
@@ -330,7 +333,8 @@ int esg_sparse_swiglu_bwd_overlap(const void* dy, const void* x, const void* w_g
   }
   if (e == hipSuccess)
     e = v2 ? launch_dw2(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
-                        at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, aux)
+                        at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, L.cht,
+                        at<char>(scratch, L.b_slots), aux)
            : launch_bwd_dw(s, x, dy, tile_off, ptoken, (int)L.rows, at<char>(scratch, L.b_dg),
                            at<char>(scratch, L.b_du), at<char>(scratch, L.b_act), dw_gate, dw_up, dw_down, aux);
   if (e == hipSuccess) e = launch_rowsum(s, at<char>(scratch, L.b_part), L.rows, pinv, dx, stream_h);

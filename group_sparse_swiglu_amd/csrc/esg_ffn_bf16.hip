@@ -827,30 +827,127 @@ __global__ __launch_bounds__(64 * dw_waves<GSB>(), GSB >= 128 ? 1 : 2) void dw2_
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, int tokens, int d, int F, int gs, int nsub,
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ ptoken, uint32_t rows_total,
     const bf16_t* __restrict__ dg, const bf16_t* __restrict__ du, const bf16_t* __restrict__ act,
-    bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu, bf16_t* __restrict__ dwd) {
+    bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu, bf16_t* __restrict__ dwd, int cht,
+    float* __restrict__ slots) {
   constexpr int XS = dw_subtiles<GSB>();
   constexpr int NWD = dw_waves<GSB>();
   using C = Dw2<GSB, XS, NWD>;
   constexpr int NS = XS == 2 ? 2 : stages_for<GSB>();
   __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE];  // no placeholder for a third stage
-  DwWork wk;
-  const int units = 2 * (F / gs) * nsub, ndb = (d + C::DW - 1) / C::DW;
-  if (!(NWD == 8 ? dw_work_xcd(blockIdx.x, units, ndb, wk) : dw_work(blockIdx.x, units, ndb, wk))) return;
-  const int g = (wk.unit >> 1) / nsub, s = (wk.unit >> 1) % nsub;
-  const int db0 = wk.db * C::DW;
+  const int G = F / gs, units = 2 * G * nsub, ndb = (d + C::DW - 1) / C::DW;
+  // eight waves: the chunked plan (cht = 0: one item per (unit, d-block), in
+  // dw_work_xcd's order); four waves: dw_work
+  DwItem it;
+  if constexpr (NWD == 8) {
+    if (!dw_plan_xcd(blockIdx.x, tile_off, G, 2 * nsub, ndb, cht, it)) return;
+  } else {
+    DwWork wk;
+    if (!dw_work(blockIdx.x, units, ndb, wk)) return;
+    const int g = (wk.unit >> 1) / nsub;
+    it = DwItem{wk.unit, wk.db, tile_off[g], tile_off[g + 1] - tile_off[g], -1};
+  }
+  const int g = (it.unit >> 1) / nsub, s = (it.unit >> 1) % nsub;
+  const int db0 = it.db * C::DW;
   const int nb0 = g * gs + s * GSB;
-  const int p0 = tile_off[g] * BM, p1 = tile_off[g + 1] * BM;
+  const int p0 = it.t0 * BM, np = it.nt * BM;
   const size_t sub_el = (size_t)s * rows_total * GSB;
   const uint32_t pbytes = (uint32_t)(nsub * rows_total * GSB * 2);
   ESG_LDS char* st0 = (ESG_LDS char*)stages_;
   ESG_LDS char* st1 = st0 + C::STAGE;
   ESG_LDS char* st2 = NS == 3 ? st1 + C::STAGE : st0;
-  if ((wk.unit & 1) == 0)
-    dw2_body<GSB, 0, NS, 0, XS, NWD>(x, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, dg, du,
+  if constexpr (NWD == 8) {
+    if (it.slot >= 0) {  // a chunk of a split group: fp32 sums into its slot ([nsub][gate, up, down] blocks)
+      float* sb = slots + (size_t)it.slot * 3 * gs * d + (size_t)s * 3 * GSB * d;
+      if ((it.unit & 1) == 0)
+        dw2_body<GSB, 0, NS, 4, XS, NWD>(x, tokens, d, F, nb0, ptoken, p0, p0, np, sub_el, sb,
+                                         sb + (size_t)GSB * d, dg, du, pbytes, dwg, dwu, db0, st0, st1, st2);
+      else
+        dw2_body<GSB, 1, NS, 4, XS, NWD>(dy, tokens, d, F, nb0, ptoken, p0, p0, np, sub_el,
+                                         sb + (size_t)2 * GSB * d, nullptr, act, act, pbytes, dwd, dwd, db0, st0,
+                                         st1, st2);
+      return;
+    }
+  }
+  if ((it.unit & 1) == 0)
+    dw2_body<GSB, 0, NS, 0, XS, NWD>(x, tokens, d, F, nb0, ptoken, p0, p0, np, sub_el, nullptr, nullptr, dg, du,
                                      pbytes, dwg, dwu, db0, st0, st1, st2);
   else
-    dw2_body<GSB, 1, NS, 0, XS, NWD>(dy, tokens, d, F, nb0, ptoken, p0, p0, p1 - p0, sub_el, nullptr, nullptr, act, act,
+    dw2_body<GSB, 1, NS, 0, XS, NWD>(dy, tokens, d, F, nb0, ptoken, p0, p0, np, sub_el, nullptr, nullptr, act, act,
                                      pbytes, dwd, dwd, db0, st0, st1, st2);
+}
+
+// The slot sums of split groups (see dw_plan_xcd): workgroup (x, y) takes
+// elements [x*E, (x+1)*E), E = 256 threads x 4 x kDwSumIt, of the split
+// groups y, y + gridDim.y, ... (in group order), adds each one's c slots in
+// chunk order in fp32 and stores bf16 like the one-item groups.  A slot holds,
+// per 128-neuron sub-block, [gate: GSB][d], [up: GSB][d] and [down: d][GSB].
+constexpr int kDwSumIt = 8;
+__global__ __launch_bounds__(256) void dw_slot_sum_kernel(const int32_t* __restrict__ tile_off, int G, int cht,
+                                                          int gs, int d, int F, const float* __restrict__ slots,
+                                                          bf16_t* __restrict__ dwg, bf16_t* __restrict__ dwu,
+                                                          bf16_t* __restrict__ dwd) {
+  constexpr int GSB = 128;
+  const int lane = threadIdx.x & 63;
+  const size_t per_slot = (size_t)3 * gs * d;
+  const size_t blk = (size_t)3 * GSB * d;
+  const size_t e0 = (size_t)blockIdx.x * kDwSumIt * 1024 + threadIdx.x * 4;
+  for (int j = blockIdx.y;; j += gridDim.y) {
+    // the j-th group with more than one chunk: g, its chunk count c, first slot ps
+    int seen = 0, g = -1, c = 0, ps = 0, sc = 0;
+    for (int g0 = 0; g0 < G && g < 0; g0 += 64) {
+      const int gg = g0 + lane;
+      const int cc = gg < G ? dw_chunks(tile_off, gg, cht) : 1;
+      const uint64_t split = __ballot(cc >= 2);
+      const int inc = wave_incl_scan(cc >= 2 ? cc : 0) + sc;
+      const int n = __popcll(split);
+      if (j < seen + n) {
+        uint64_t m = split;
+        for (int i = 0; i < j - seen; ++i) m &= m - 1;  // drop the lower split groups
+        const int src = __builtin_ctzll(m);
+        g = g0 + src;
+        c = __builtin_amdgcn_readfirstlane(__shfl(cc, src));
+        ps = __builtin_amdgcn_readfirstlane(__shfl(inc, src)) - c;
+      }
+      seen += n;
+      sc = __builtin_amdgcn_readfirstlane(__shfl(inc, 63));
+    }
+    if (g < 0) return;
+    float v[kDwSumIt][4];
+#pragma unroll
+    for (int u = 0; u < kDwSumIt; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[u][i] = 0.0f;
+    for (int q = 0; q < c; ++q) {  // chunk order
+      const float* src = slots + (size_t)(ps + q) * per_slot;
+#pragma unroll
+      for (int u = 0; u < kDwSumIt; ++u) {
+        const size_t e = e0 + (size_t)u * 1024;
+        if (e < per_slot) {
+          float o[4];
+          Quad<float>::load(src + e, o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[u][i] += o[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDwSumIt; ++u) {
+      const size_t e = e0 + (size_t)u * 1024;
+      if (e >= per_slot) break;
+      const int sb = (int)(e / blk);
+      const size_t r = e % blk;
+      const int part = (int)(r / ((size_t)GSB * d));
+      const int w = (int)(r % ((size_t)GSB * d));
+      const int nb0 = g * gs + sb * GSB;
+      if (part < 2) {
+        const int n = w / d, dd = w % d;
+        Quad<bf16_t>::store((part == 0 ? dwg : dwu) + (size_t)(nb0 + n) * d + dd, v[u]);
+      } else {
+        const int dd = w / GSB, n = w % GSB;
+        Quad<bf16_t>::store(dwd + (size_t)dd * F + nb0 + n, v[u]);
+      }
+    }
+  }
 }
 
 // ===========================================================================
@@ -943,16 +1040,25 @@ hipError_t dhdx2_t(const FfnShape& s, const void* dy, const void* wg, const void
 template <int GSB>
 hipError_t dw2_t(const FfnShape& s, const void* x, const void* dy, const int32_t* tile_off, const int32_t* ptoken,
                  int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
-                 hipStream_t stream) {
+                 int cht, void* slots, hipStream_t stream) {
   LaunchTimer timer("bwd_dw", stream);
-  const int units = 2 * s.groups() * s.nsub();
+  const int G = s.groups(), units = 2 * G * s.nsub();
   const int ndb = (s.d_model + 128 * dw_subtiles<GSB>() - 1) / (128 * dw_subtiles<GSB>());
-  const dim3 grid(dw_waves<GSB>() == 8 ? dw_grid_xcd(units, ndb) : dw_grid(units, ndb));  // order: dw_work(_xcd)
+  if (dw_waves<GSB>() != 8) cht = 0;
+  // order: dw_plan_xcd (eight waves; sized for the most chunks the rows allow) or dw_work
+  const dim3 grid(dw_waves<GSB>() == 8 ? dw_plan_grid(G, 2 * s.nsub(), ndb, rows_total, cht) : dw_grid(units, ndb));
   hipLaunchKernelGGL((dw2_kernel<GSB>), grid, dim3(64 * dw_waves<GSB>()), 0, stream, (const bf16_t*)x,
                      (const bf16_t*)dy, s.tokens,
                      s.d_model, s.d_ff, s.group_size, s.nsub(), tile_off, ptoken, (uint32_t)rows_total,
                      (const bf16_t*)dg, (const bf16_t*)du, (const bf16_t*)act, (bf16_t*)dwg, (bf16_t*)dwu,
-                     (bf16_t*)dwd);
+                     (bf16_t*)dwd, cht, (float*)slots);
+  hipError_t e = hipGetLastError();
+  const int sg = std::min(G, dw_split_groups_max(rows_total, cht));
+  if (e != hipSuccess || sg == 0) return e;
+  const size_t per_slot = (size_t)3 * s.group_size * s.d_model;
+  const dim3 sgrid((unsigned)((per_slot + 1024 * kDwSumIt - 1) / (1024 * kDwSumIt)), (unsigned)std::min(sg, 8));
+  hipLaunchKernelGGL(dw_slot_sum_kernel, sgrid, dim3(256), 0, stream, tile_off, G, cht, s.group_size, s.d_model,
+                     s.d_ff, (const float*)slots, (bf16_t*)dwg, (bf16_t*)dwu, (bf16_t*)dwd);
   return hipGetLastError();
 }
 
@@ -1005,12 +1111,27 @@ hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const
 
 hipError_t launch_dw2(const FfnShape& s, const void* x, const void* dy, const int32_t* tile_off, const int32_t* ptoken,
                       int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
-                      hipStream_t stream) {
+                      int cht, void* slots, hipStream_t stream) {
   switch (s.gsb()) {
-    case 32: return dw2_t<32>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
-    case 64: return dw2_t<64>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
-    default: return dw2_t<128>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, stream);
+    case 32: return dw2_t<32>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, 0, slots, stream);
+    case 64: return dw2_t<64>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, 0, slots, stream);
+    default:
+      return dw2_t<128>(s, x, dy, tile_off, ptoken, rows_total, dg, du, act, dwg, dwu, dwd, cht, slots, stream);
   }
+}
+
+int dw_chunk_tiles(const FfnShape& s, int ntiles_max, int pad) {
+  if (!bf16_pipelined(s, ntiles_max) || s.gsb() != 128 || s.tokens <= 0) return 0;
+  // 1.5 times the mean bucket (no cut under an even load), at least 16 tiles
+  const long long mean_rows = ((long long)s.tokens * s.k + s.groups() - 1) / s.groups();
+  const long long cht = std::max(16ll, (3 * mean_rows + 2 * BM - 1) / (2 * BM));
+  // a bucket holds at most one position per token, padded to the pad unit
+  const long long most = ((long long)s.tokens + pad - 1) / pad * (pad / BM);
+  return cht >= most ? 0 : (int)cht;
+}
+
+size_t dw_slot_bytes(const FfnShape& s, size_t rows, int cht) {
+  return (size_t)dw_split_slots_max((long long)rows, cht) * 3 * s.group_size * s.d_model * 4;
 }
 
 }  // namespace esg

@@ -123,9 +123,14 @@ hipError_t launch_fwd2(const FfnShape& s, const void* x, const void* wg, const v
 hipError_t launch_dhdx2(const FfnShape& s, const void* dy, const void* wg, const void* wu, const void* wd,
                         const int32_t* tile_group, const int32_t* ptoken, int ntiles_max, const void* hg_saved,
                         const void* hu_saved, void* dg, void* du, void* act, void* partials, hipStream_t stream);
+// cht, slots: 128-neuron blocks cut a group's positions into chunks of cht
+// tiles when its bucket holds more (0: never; dw_chunk_tiles), summing the
+// chunks in fp32 slots of dw_slot_bytes (then added in chunk order)
 hipError_t launch_dw2(const FfnShape& s, const void* x, const void* dy, const int32_t* tile_off, const int32_t* ptoken,
                       int rows_total, const void* dg, const void* du, const void* act, void* dwg, void* dwu, void* dwd,
-                      hipStream_t stream);
+                      int cht, void* slots, hipStream_t stream);
+int dw_chunk_tiles(const FfnShape& s, int ntiles_max, int pad);
+size_t dw_slot_bytes(const FfnShape& s, size_t rows, int cht);
 
 // ---- dense limit (all groups active) ----------------------------------------------
 constexpr int kDenseChunkTokens = 8192;  // backward token chunk (recompute workspace)

@@ -423,9 +423,103 @@ __device__ __forceinline__ bool dw_work_xcd(int L, int units, int ndb, DwWork& w
 }
 inline int dw_grid_xcd(int units, int ndb) { return (units * ndb + 7) / 8 * 8; }
 
+// Weight-gradient work with heavy groups cut by positions.  Under uneven
+// routing a popular group's (unit, d-block) workgroups sum many times the
+// positions of the others and finish last.  A group whose bucket holds more
+// than cht tiles is cut into c = ceil(tiles / cht) chunks of cht tiles (the
+// last one shorter); each chunk is an item per (unit, d-block) that sums its
+// positions into an fp32 slot, and a second launch adds a group's slots in
+// chunk order.  Groups of at most cht tiles (every group when cht = 0) keep
+// one item per (unit, d-block) that writes bf16 directly.  The (unit, chunk)
+// pairs are numbered group-major, then chunk, then unit; workgroups go to the
+// 8 XCDs round-robin (workgroup L runs on XCD L % 8), and the m-th pair of XCD
+// x is j = 8m + (x + m) % 8, with all d-blocks of a pair in a row: a pair's
+// d-blocks read its packed rows from one L2, the chunks of a hot group land on
+// different XCDs, and every XCD gets both kinds (kind 0 does twice the work
+// of kind 1, and with j = 8m + x the even XCDs would take every kind-0 pair).
+// Every wave of the workgroup derives the same item from tile_off (a
+// wave-wide scan of the per-group chunk counts).
+struct DwItem {
+  int unit, db;  // as in DwWork
+  int t0, nt;    // the chunk's first tile and tile count
+  int slot;      // the chunk's fp32 slot (group-major, chunk order), or -1
+};
+__device__ __forceinline__ int dw_chunks(const int32_t* __restrict__ tile_off, int g, int cht) {
+  const int nt = tile_off[g + 1] - tile_off[g];
+  return cht > 0 && nt > cht ? (nt + cht - 1) / cht : 1;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+// The group holding chunk-unit q (q counts chunks over the groups in order):
+// g, its chunk count c, its first chunk index pc and its first slot ps (split
+// groups only take slots).  False when q is past the last chunk.
+struct DwGroupAt {
+  int g, c, pc, ps;
+};
+__device__ __forceinline__ bool dw_group_at(const int32_t* __restrict__ tile_off, int G, int cht, int q,
+                                            DwGroupAt& r) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0, scarry = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    const int c = g < G ? dw_chunks(tile_off, g, cht) : 0;
+    const int s = c >= 2 ? c : 0;
+    const int inc = wave_incl_scan(c) + carry;
+    const int sinc = wave_incl_scan(s) + scarry;
+    const uint64_t hit = __ballot(inc > q);
+    if (hit != 0) {  // (lane reads return vector registers: readfirstlane keeps the item scalar)
+      const int src = __builtin_ctzll(hit);
+      r.g = g0 + src;
+      r.c = __builtin_amdgcn_readfirstlane(__shfl(c, src));
+      r.pc = __builtin_amdgcn_readfirstlane(__shfl(inc, src)) - r.c;
+      r.ps = __builtin_amdgcn_readfirstlane(__shfl(sinc, src) - __shfl(s, src));
+      return true;
+    }
+    carry = __shfl(inc, 63);
+    scarry = __shfl(sinc, 63);
+  }
+  return false;
+}
+// upg: units per group (2 * nsub).  Returns false past the last item (the
+// grid is sized for the most chunks the rows allow).
+__device__ __forceinline__ bool dw_plan_xcd(int L, const int32_t* __restrict__ tile_off, int G, int upg, int ndb,
+                                            int cht, DwItem& it) {
+  const int i = L / 8, m = i / ndb, j = 8 * m + ((L + m) & 7);
+  DwGroupAt r;
+  if (!dw_group_at(tile_off, G, cht, j / upg, r)) return false;  // past the last pair
+  const int local = j - r.pc * upg;
+  const int chunk = local / upg;
+  it.unit = r.g * upg + local % upg;
+  it.db = i % ndb;
+  const int ta = __builtin_amdgcn_readfirstlane(tile_off[r.g]), tb = __builtin_amdgcn_readfirstlane(tile_off[r.g + 1]);
+  it.t0 = ta + chunk * cht;
+  it.nt = min(r.c == 1 ? tb - ta : cht, tb - it.t0);
+  it.slot = r.c >= 2 ? r.ps + chunk : -1;
+  return true;
+}
+// Upper bounds for a launch of `rows` bucket rows (padding included) and
+// chunks of cht tiles: a split group holds more than cht tiles, so there are
+// fewer than rows / (cht * 128) of them, and its c chunks number fewer than
+// twice its tiles / cht.
+inline int dw_split_groups_max(long long rows, int cht) { return cht > 0 ? (int)(rows / ((long long)BM * cht)) : 0; }
+inline int dw_split_slots_max(long long rows, int cht) {
+  return cht > 0 ? (int)(2 * rows / ((long long)BM * cht)) : 0;
+}
+inline int dw_plan_grid(int G, int upg, int ndb, long long rows, int cht) {
+  const long long chunks = (long long)G + dw_split_groups_max(rows, cht);
+  return (int)(8ll * ndb * ((chunks * upg + 7) / 8));
+}
+
 template <int MODE>
 __device__ __forceinline__ void store_dw(bf16_t* out, float* acc32, float (&v)[4]) {
-  if constexpr (MODE >= 2) {
+  if constexpr (MODE == 2 || MODE == 3) {
     float o[4];
     Quad<float>::load(acc32, o);
 #pragma unroll
@@ -441,7 +535,8 @@ __device__ __forceinline__ int dw_perm(int r) { return (r & ~15) | ((r & 3) << 2
 
 // MODE: 0 stores bf16; 1 stores the fp32 sums to f0/f1; 2 adds them to
 // f0/f1; 3 adds f0/f1 and stores bf16 (K split over consecutive launches, in
-// a fixed order).  Ids of the K positions come from ptoken[pid0 ..], their
+// a fixed order); 4 stores the fp32 sums to f0/f1 laid out for this block
+// alone (kind 0: [GSB][d], kind 1: [d][GSB]), a chunk's slot.  Ids of the K positions come from ptoken[pid0 ..], their
 // packed dg/du/a rows start at row p0; np positions (a multiple of 64).
 template <int GSB, int KIND, int NS, int MODE = 0, int XS = 1, int NWD = 4>
 __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tokens, int d, int F, int nb0,
@@ -588,7 +683,8 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
         if (nb0 + n >= F) continue;
         const size_t o = (size_t)(nb0 + n) * d + dd;
-        store_dw<MODE>((wn == 0 ? out0 : out1) + o, (wn == 0 ? f0 : f1) + o, v);
+        const size_t of = MODE == 4 ? (size_t)n * d + dd : o;
+        store_dw<MODE>((wn == 0 ? out0 : out1) + o, (wn == 0 ? f0 : f1) + of, v);
       }
     }
   } else {
@@ -604,7 +700,8 @@ __device__ __forceinline__ void dw2_body(const bf16_t* __restrict__ src, int tok
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e];
         if (nb0 + n >= F) continue;
         const size_t o = (size_t)dd * F + nb0 + n;
-        store_dw<MODE>(out0 + o, f0 + o, v);
+        const size_t of = MODE == 4 ? (size_t)dd * GSB + n : o;
+        store_dw<MODE>(out0 + o, f0 + of, v);
       }
     }
   }

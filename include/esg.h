@@ -147,8 +147,11 @@ int esg_bucket_by_group(const int32_t* idx, int tokens, int k, int groups, int32
  * forward with `saved` needs; a forward with saved = NULL needs at most that
  * (bf16 training layouts with 128-neuron blocks pad each group's bucket to a
  * whole pair of 128-position tiles for the backward; inference pads to one
- * tile).  Errors: as for the forward; ESG_ERR_UNSUPPORTED for a dense shape the
- * dense kernels do not cover.
+ * tile).  The routed backward's scratch holds dg, du and a of every bucket
+ * position, the bf16 partial rows of dx and, for bf16 128-neuron blocks whose
+ * buckets could exceed 1.5 times the mean, float32 slots for the weight
+ * gradients of such buckets summed in chunks.  Errors: as for the forward;
+ * ESG_ERR_UNSUPPORTED for a dense shape the dense kernels do not cover.
  */
 int esg_sparse_swiglu_workspace_size(int tokens, int d_model, int d_ff, int group_size, int k,
                                      int dtype, int dense, size_t* saved_bytes,

@@ -93,7 +93,9 @@ def test_hot_bias_on_four_groups(case):
 
 def test_one_group_holds_every_token():
     """T = 16384 tokens all routed to group 7 (plus two others each): one
-    bucket of T positions, 128 tiles of one group."""
+    bucket of T positions, 128 tiles of one group.  Its weight gradients are
+    summed by position chunks (the bucket is far above the mean load) added in
+    a fixed order, so a second backward gives the same bits."""
     require_gpu()
     T, d, F, gs, G = 16384, 1024, 2688, 128, 21
     note(f"skew one group T={T}")
@@ -106,6 +108,9 @@ def test_one_group_holds_every_token():
     neurons = {7 * gs + int(v) for v in rng.choice(gs, 6, replace=False)}
     neurons |= {int(v) for v in rng.choice(F, 12, replace=False)}
     _sampled_compare(inp, idx, outs, neurons)
+    again = _run(inp, idx)
+    for name, a, b in zip(("y", "dx", "dW_gate", "dW_up", "dW_down"), outs, again):
+        assert torch.equal(a, b), f"{name} differs between two runs"
 
 
 def test_four_groups_only_leave_the_rest_exactly_zero():
