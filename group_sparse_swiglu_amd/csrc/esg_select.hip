@@ -94,15 +94,29 @@ __device__ __forceinline__ void select_energy(const f32x4 (&acc)[FMW][FNW], floa
   }
 }
 
-// Top-k of the BM tokens whose scores are E[r * ES + g] (LDS), written to
-// idx_out in ascending group id; per-group counts through the LDS table cnt
-// (zeroed by the caller) when counts is given.  NW waves.
+// Scores are compared through an order-preserving integer key: for every
+// non-NaN pair of scores a > b exactly when key(a) > key(b), and -0 and +0 map
+// to the same key; a NaN with its sign bit clear ranks above +inf.
+__device__ __forceinline__ uint32_t score_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k of the BM tokens whose scores are E[r * ES + g] (LDS, complete: the
+// caller synchronised after writing them), written to idx_out in ascending
+// group id; per-group counts through the LDS table cnt (zeroed by the caller)
+// when counts is given.  NW waves.  E is turned into keys in place.
 template <int BM, int NW = 4>
-__device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int t0, int tokens, int groups, int k,
+__device__ __forceinline__ void rank_topk(float* E, int ES, int* cnt, int t0, int tokens, int groups, int k,
                                           int32_t* __restrict__ idx_out, int32_t* __restrict__ counts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // rank top-k: group g is selected when fewer than k groups beat it (higher
-  // score, or equal score and lower id); its output slot is its rank among the
+  uint32_t* const Kt = (uint32_t*)E;
+  for (int i = tid; i < BM * ES; i += 64 * NW) Kt[i] = score_key(E[i]);
+  __syncthreads();
+  // group g is selected when fewer than k groups beat it (higher score, or
+  // equal score and lower id), i.e. it is among the k first in the order
+  // (score descending, id ascending); its output slot is its rank among the
   // selected ids (a ballot prefix)
   const uint64_t lt = (1ull << lane) - 1ull;
   if (groups <= 32) {
@@ -110,18 +124,18 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
     // of token half l / 32; a token's other scores are broadcast reads
     constexpr int TPW = BM / (2 * NW);  // token pairs per wave
     const int hf = lane >> 5, g = lane & 31;
-    float sg[TPW];
+    uint32_t sg[TPW];
     int beat[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int r = wave + NW * (2 * i + hf);
-      sg[i] = g < groups ? E[r * ES + g] : 0.0f;
+      sg[i] = g < groups ? Kt[r * ES + g] : 0u;
       beat[i] = 0;
     }
     for (int q = 0; q < groups; ++q) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
-        const float sq = E[(wave + NW * (2 * i + hf)) * ES + q];
+        const uint32_t sq = Kt[(wave + NW * (2 * i + hf)) * ES + q];
         beat[i] += (sq > sg[i]) || (sq == sg[i] && q < g);
       }
     }
@@ -132,7 +146,7 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
       const bool sel = g < groups && beat[i] < k;
       const uint64_t m = __ballot(sel) & half;
       const int pos = __popcll(m & lt);
-      if (t < tokens && sel && pos < k) {  // NaN scores could select more than k: never write past the row
+      if (t < tokens && sel && pos < k) {
         idx_out[(size_t)t * k + pos] = g;
         if (counts) atomicAdd(&cnt[g], 1);
       }
@@ -141,17 +155,17 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
     // lane g holds group g of the wave's BM/NW tokens at once; every other
     // group's score comes as a broadcast LDS read (same address in all lanes)
     constexpr int TPW = BM / NW;
-    float sg[TPW];
+    uint32_t sg[TPW];
     int beat[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      sg[i] = lane < groups ? E[(wave + NW * i) * ES + lane] : 0.0f;
+      sg[i] = lane < groups ? Kt[(wave + NW * i) * ES + lane] : 0u;
       beat[i] = 0;
     }
     for (int q = 0; q < groups; ++q) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
-        const float sq = E[(wave + NW * i) * ES + q];
+        const uint32_t sq = Kt[(wave + NW * i) * ES + q];
         beat[i] += (sq > sg[i]) || (sq == sg[i] && q < lane);
       }
     }
@@ -161,51 +175,53 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
       const bool sel = lane < groups && beat[i] < k;
       const uint64_t m = __ballot(sel);
       const int pos = __popcll(m & lt);
-      if (t < tokens && sel && pos < k) {  // NaN scores could select more than k: never write past the row
+      if (t < tokens && sel && pos < k) {
         idx_out[(size_t)t * k + pos] = lane;
         if (counts) atomicAdd(&cnt[lane], 1);
       }
     }
   } else if (groups <= 256) {
-    // one token per wave at a time; lane l holds groups l, l+64, l+128, l+192
-    // in registers and every other score comes from a lane read with a
-    // constant lane index (no LDS round trip per compared group)
+    // one token per wave at a time; lane l holds the keys of groups l, l+64,
+    // l+128, l+192.  The key of the k-th group in the order is found bit by
+    // bit from the top (a radix select: per bit, a ballot count of the keys
+    // that match the bits found so far and have this bit set); the groups
+    // above it are selected and, of the groups equal to it, the lowest ids
+    // fill the remaining slots.
     for (int r = wave; r < BM; r += NW) {
       const int t = t0 + r;
       if (t >= tokens) break;
-      const float* row = E + r * ES;
-      float sv[4];
-      int beat[4];
+      const uint32_t* row = Kt + r * ES;
+      uint32_t key[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sv[c] = c * 64 + lane < groups ? row[c * 64 + lane] : 0.0f;
-        beat[c] = 0;
-      }
+      for (int c = 0; c < 4; ++c) key[c] = c * 64 + lane < groups ? row[c * 64 + lane] : 0u;
+      uint32_t pre = 0;  // the bits of the k-th key found so far
+      int need = k;      // its position among the keys that match them
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t hi = ~0u << bit, cand = pre | (1u << bit);
+        int n = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c * 64 >= groups) break;  // wave-uniform
-        const int lmax = min(64, groups - c * 64);
-#pragma unroll 8
-        for (int l = 0; l < lmax; ++l) {  // l: a uniform (scalar) lane index
-          const int qg = c * 64 + l;
-          const float sq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[c]), l));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (e * 64 >= groups) break;  // wave-uniform
-            const int g = e * 64 + lane;
-            beat[e] += (sq > sv[e]) || (sq == sv[e] && qg < g);
-          }
+        for (int c = 0; c < 4; ++c) {
+          if (c * 64 >= groups) break;  // wave-uniform
+          n += __popcll(__ballot(c * 64 + lane < groups && (key[c] & hi) == cand));
         }
+        if (n >= need) pre = cand;
+        else need -= n;
       }
       int base = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (e * 64 >= groups) break;  // wave-uniform
-        const int g = e * 64 + lane;
-        const bool sel = g < groups && beat[e] < k;
+      for (int c = 0; c < 4; ++c) {
+        if (c * 64 >= groups) break;  // wave-uniform
+        const int g = c * 64 + lane;
+        uint64_t eq = __ballot(g < groups && key[c] == pre), take = 0;
+        for (; need > 0 && eq != 0; --need) {  // the lowest ids among the equal keys
+          const uint64_t low = eq & (~eq + 1ull);
+          take |= low;
+          eq ^= low;
+        }
+        const bool sel = g < groups && (key[c] > pre || ((take >> lane) & 1ull));
         const uint64_t m = __ballot(sel);
         const int pos = base + __popcll(m & lt);
-        if (sel && pos < k) {  // NaN scores could select more than k: never write past the row
+        if (sel) {
           idx_out[(size_t)t * k + pos] = g;
           if (counts) atomicAdd(&cnt[g], 1);
         }
@@ -216,16 +232,16 @@ __device__ __forceinline__ void rank_topk(const float* E, int ES, int* cnt, int 
     for (int r = wave; r < BM; r += NW) {
       const int t = t0 + r;
       if (t >= tokens) break;
-      const float* row = E + r * ES;
+      const uint32_t* row = Kt + r * ES;
       int base = 0;
       for (int g0 = 0; g0 < groups; g0 += 64) {
         const int g = g0 + lane;
         bool sel = false;
         if (g < groups) {
-          const float sg = row[g];
+          const uint32_t sg = row[g];
           int beat = 0;
           for (int q = 0; q < groups; ++q) {
-            const float sq = row[q];
+            const uint32_t sq = row[q];
             beat += (sq > sg) || (sq == sg && q < g);
           }
           sel = beat < k;
