@@ -835,8 +835,8 @@ __global__ __launch_bounds__(64 * dw_waves<GSB>(), GSB >= 128 ? 1 : 2) void dw2_
   constexpr int NS = XS == 2 ? 2 : stages_for<GSB>();
   __shared__ __attribute__((aligned(1024))) char stages_[NS * C::STAGE];  // no placeholder for a third stage
   const int G = F / gs, units = 2 * G * nsub, ndb = (d + C::DW - 1) / C::DW;
-  // eight waves: the chunked plan (cht = 0: one item per (unit, d-block), in
-  // dw_work_xcd's order); four waves: dw_work
+  // eight waves: the chunked plan of dw_plan_xcd (with cht = 0 one item per
+  // (unit, d-block)); four waves: dw_work
   DwItem it;
   if constexpr (NWD == 8) {
     if (!dw_plan_xcd(blockIdx.x, tile_off, G, 2 * nsub, ndb, cht, it)) return;

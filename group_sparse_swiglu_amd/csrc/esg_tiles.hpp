@@ -394,12 +394,13 @@ struct Dw2 {
 // kind) pair; its ndb d-blocks read the same packed dg/du/a rows.
 // dw_work: workgroup L takes neuron block L % GB, then d-block, then kind
 // (GB = units / 2), so the workgroups in flight together spread over all
-// neuron blocks (four-wave workgroups, 64-neuron and dense blocks).
+// neuron blocks (four-wave workgroups of 32- and 64-neuron blocks).
 // dw_work_xcd: workgroups go to the 8 XCDs round-robin, so workgroup L runs
 // on XCD L % 8; XCD x takes the flat items [x*per, (x+1)*per) in order (unit
 // major, d-block minor), so a unit's d-blocks run together in one L2 and read
-// its packed rows from there (eight-wave 128-neuron workgroups: at the 1.3B
-// shape 4.24 -> 3.26 GB of L2 misses; with four waves it measured slower).
+// its packed rows from there (the dense limit's eight-wave workgroups; for
+// the routed 128-neuron blocks, measured at the 1.3B shape, 4.24 -> 3.26 GB
+// of L2 misses; they now take dw_plan_xcd below).
 // Both return false for workgroups past the last item.
 struct DwWork {
   int unit, db;
