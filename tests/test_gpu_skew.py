@@ -129,3 +129,28 @@ def test_four_groups_only_leave_the_rest_exactly_zero():
     neurons = {int(g) * gs + int(rng.integers(gs)) for g in used} | {1 * gs + 5, 20 * gs + 7}
     _sampled_compare(inp, idx, outs, neurons)
     assert _exact_zeros_for_unused(idx, outs, G, gs) == G - 4
+
+
+def test_hot_group_of_two_sub_blocks_and_a_ragged_d():
+    """Groups of 256 neurons (two 128-neuron sub-blocks per group) at d = 1040
+    (the last 256-wide d-block of the weight gradients is 16 wide), every
+    token routed to group 3 plus one other: the hot bucket (8192 positions, 4x
+    the mean) is summed in chunks whose slots hold both sub-blocks; two runs
+    give the same bits."""
+    require_gpu()
+    T, d, F, gs = 8192, 1040, 2048, 256
+    G = F // gs
+    note(f"skew two sub-blocks T={T} d={d} gs={gs}")
+    inp = inputs(T, d, F, gs, "bf16", seed=27, bias=False)
+    other = I.random_group_idx(T, G - 1, 1, seed=13).numpy()
+    other = other + (other >= 3)          # skip group 3
+    idx = np.sort(np.concatenate([np.full((T, 1), 3, np.int32), other], axis=1), axis=1).astype(np.int32)
+    outs = _run(inp, idx)
+    rng = np.random.default_rng(10)
+    neurons = {3 * gs + int(v) for v in rng.choice(gs, 8, replace=False)}   # both sub-blocks of the hot group
+    neurons |= {int(v) for v in rng.choice(F, 12, replace=False)}
+    _sampled_compare(inp, idx, outs, neurons)
+    again = _run(inp, idx)
+    for name, a, b in zip(("y", "dx", "dW_gate", "dW_up", "dW_down"), outs, again):
+        assert torch.equal(a, b), f"{name} differs between two runs"
+
