@@ -5,8 +5,8 @@
 // one-pass fused FFN at d_model >= 2048).
 //
 // Forward (dense_fwd_kernel): token-stationary.  A workgroup owns 32 tokens
-// and the whole fp32 [32, d] output accumulator in AGPRs (d <= 2048: 256
-// registers per lane over 4 wavefronts).  It sweeps d_ff in chunks of 128
+// and the whole fp32 [32, d] output accumulator in registers (d <= 2048: 128
+// per lane over 8 wavefronts).  It sweeps d_ff in chunks of 128
 // neurons: phase 1 computes [hg; hu] for the chunk (K = d), the gated
 // activation goes bf16 into an LDS tile, phase 2 adds W_d[:, chunk] . a^T to
 // the accumulator (K = 128).  The [tokens, d_ff] intermediate never exists in
