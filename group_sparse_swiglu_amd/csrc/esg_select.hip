@@ -56,7 +56,7 @@ struct SelCfg {
   static constexpr int PB = Plane<NSC>::BYTES;
   static constexpr int A_BYTES = DMA ? BM * 128 : KC * PA;
   static constexpr int B_BYTES = DMA ? NSC * 128 : KC * PB;
-  static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES + SINK) <= 112 * 1024 ? 3 : 2;
+  static constexpr int DMA_NS = 3 * (A_BYTES + B_BYTES + SINK) <= 120 * 1024 ? 3 : 2;
   static constexpr int DMA_L = IA + IB;  // loads per lane per stage
   static constexpr int STAGES = (DMA ? DMA_NS : 2) * (A_BYTES + B_BYTES + SINK);
   static constexpr int S_STRIDE = NSC + 1;  // odd float stride: conflict-free column walks
@@ -556,11 +556,15 @@ hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
     // (one 256-row super-chunk: eight waves in eight column groups, two waves
     // per SIMD at one workgroup per CU; 128M select 19 -> 16 us)
     if (groups * rpg > 128 && groups * rpg <= 256) return launch_select_t<T, 32, 2, 8>(a, st);
-    // (128-token blocks run eight waves: one workgroup per CU, two waves per SIMD,
-    // with 256-column super-chunks (four fragments per wave) when their |SiLU|
-    // table fits: each super-chunk streams the x tile again, and at the 1.3B
-    // shape 688 sampled rows then take 3 passes instead of 6: select 171 -> 162 us)
+    // (128-token blocks run eight waves: one workgroup per CU, two waves per SIMD.
+    // Each super-chunk streams the x tile again: at the 1.3B shape 688 sampled
+    // rows in 128-row super-chunks took 6 passes (171 us), in 256-row ones 3
+    // passes (162 us), whose 48 KB stages fit a 2-stage ring only, so one stage
+    // was in flight per step and each step waited about a memory latency; 192-row
+    // super-chunks take 4 passes with 40 KB stages in a 3-stage ring: 159 -> 147 us)
     if (a.tokens >= 128 * compute_units()) {
+      if (SelCfg<T, 128, 3, true, kSel128Waves>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
+        return launch_select_t<T, 128, 3, kSel128Waves>(a, st);
       if (SelCfg<T, 128, 4, true, kSel128Waves>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
         return launch_select_t<T, 128, 4, kSel128Waves>(a, st);
       if (SelCfg<T, 128, 2, true, kSel128Waves>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
