@@ -320,7 +320,14 @@ __global__ __launch_bounds__(512, 1) void fwd2_pair_kernel(
   ESG_LDS char* const base = (ESG_LDS char*)lds_;
   static_assert(C::ACT_BYTES + 2 * C::W2_BYTES + 128 * RS::RB <= 2 * A_BYTES + 3 * B_BYTES, "phase-2 LDS");
 
-  const int tile0 = 2 * blockIdx.x;
+  // XCD-local runs of pair tiles: workgroup L runs on XCD L % 8, which takes
+  // the contiguous pairs [x*per, (x+1)*per) (gridDim.x is a multiple of 8), so
+  // the pairs in flight on an XCD share their group's weights in its L2
+  const int npair = (int)(rows_total / (2 * BM));
+  const int per = gridDim.x / 8;
+  const int pr = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (pr >= npair) return;
+  const int tile0 = 2 * pr;
   const int g = tile_group[tile0];
   if (g < 0) return;
   const int s = blockIdx.y;
@@ -674,7 +681,14 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
   __shared__ __attribute__((aligned(1024))) char lds_[LDS1];
   ESG_LDS char* const base = (ESG_LDS char*)lds_;
 
-  const int tile0 = 2 * blockIdx.x;
+  // XCD-local runs of pair tiles: workgroup L runs on XCD L % 8, which takes
+  // the contiguous pairs [x*per, (x+1)*per) (gridDim.x is a multiple of 8), so
+  // the pairs in flight on an XCD share their group's weights in its L2
+  const int npair = (int)(rows_total / (2 * BM));
+  const int per = gridDim.x / 8;
+  const int pr = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (pr >= npair) return;
+  const int tile0 = 2 * pr;
   const int g = tile_group[tile0];
   if (g < 0) return;
   const int s = blockIdx.y;
@@ -991,7 +1005,7 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
   if constexpr (GSB == 128) {
     if (pad == 2 * BM) {  // pairs of tiles of one group (the bucketing padded groups to pairs)
       auto kp = partials_nontemporal(s, ntiles_max) ? fwd2_pair_kernel<kCpolNontemporal> : fwd2_pair_kernel<0>;
-      hipLaunchKernelGGL(kp, dim3(ntiles_max / 2, s.nsub()), dim3(512), 0, stream, (const bf16_t*)x,
+      hipLaunchKernelGGL(kp, dim3((ntiles_max / 2 + 7) / 8 * 8, s.nsub()), dim3(512), 0, stream, (const bf16_t*)x,
                          (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                          s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
                          (bf16_t*)partials);
@@ -1022,7 +1036,7 @@ hipError_t dhdx2_t(const FfnShape& s, const void* dy, const void* wg, const void
   if constexpr (GSB == 128) {
     if (tile_pad(s) == 2 * BM) {  // pairs of tiles of one group (the bucketing padded groups to pairs)
       auto kp = partials_nontemporal(s, ntiles_max) ? dhdx2_pair_kernel<kCpolNontemporal> : dhdx2_pair_kernel<0>;
-      hipLaunchKernelGGL(kp, dim3(ntiles_max / 2, s.nsub()), dim3(512), 0, stream, (const bf16_t*)dy,
+      hipLaunchKernelGGL(kp, dim3((ntiles_max / 2 + 7) / 8 * 8, s.nsub()), dim3(512), 0, stream, (const bf16_t*)dy,
                          (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                          s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (const bf16_t*)hg,
                          (const bf16_t*)hu, (bf16_t*)dg, (bf16_t*)du, (bf16_t*)act, (bf16_t*)partials);
