@@ -163,7 +163,11 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   ESG_LDS char* const st0 = st[0];
   ESG_LDS char* const st1 = st[1];
 
-  const int tile = blockIdx.x;
+  // XCD-local runs of tiles: workgroup L runs on XCD L % 8, which takes the
+  // contiguous tiles [x*per, (x+1)*per) (gridDim.x is a multiple of 8)
+  const int per_x = gridDim.x / 8;
+  const int tile = (int)(blockIdx.x % 8) * per_x + (int)(blockIdx.x / 8);
+  if (tile >= (int)(rows_total / BM)) return;
   const int g = tile_group[tile];
   if (g < 0) return;
   const int s = blockIdx.y;
@@ -505,7 +509,11 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
   ESG_LDS char* st2 = NS == 3 ? st1 + C::STAGE : st0;
   ESG_LDS char* dgu = (ESG_LDS char*)dgu_;
 
-  const int tile = blockIdx.x;
+  // XCD-local runs of tiles: workgroup L runs on XCD L % 8, which takes the
+  // contiguous tiles [x*per, (x+1)*per) (gridDim.x is a multiple of 8)
+  const int per_x = gridDim.x / 8;
+  const int tile = (int)(blockIdx.x % 8) * per_x + (int)(blockIdx.x / 8);
+  if (tile >= (int)(rows_total / BM)) return;
   const int g = tile_group[tile];
   if (g < 0) return;
   const int s = blockIdx.y;
@@ -991,11 +999,12 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
       };
       const int kz = ranges((s.d_model + 63) / 64, std::min(kFwdSplitK, kNominalCUs / tiles));  // one per CU
       const int nz = ranges((s.d_model + DB - 1) / DB, 2 * kNominalCUs / tiles);              // two per CU
-      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, 8, 1>), dim3(ntiles_max, s.nsub(), kz), dim3(64 * 8), 0, stream,
+      const unsigned gx = (ntiles_max + 7) / 8 * 8;  // a multiple of 8 (the tile order is XCD-local)
+      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, 8, 1>), dim3(gx, s.nsub(), kz), dim3(64 * 8), 0, stream,
                          (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
                          s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
                          (bf16_t*)hu, (bf16_t*)partials, (float*)act, kz);
-      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, NW, 2>), dim3(ntiles_max, s.nsub(), nz), dim3(64 * NW), 0, stream,
+      hipLaunchKernelGGL((fwd2_kernel<GSB, 0, NW, 2>), dim3(gx, s.nsub(), nz), dim3(64 * NW), 0, stream,
                          (const bf16_t*)x, (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens,
                          s.d_model, s.d_ff, s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg,
                          (bf16_t*)hu, (bf16_t*)partials, (float*)act, kz);
@@ -1021,7 +1030,8 @@ hipError_t fwd2_t(const FfnShape& s, const void* x, const void* wg, const void* 
       waves = 8;
     }
   }
-  hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * waves), 0, stream, (const bf16_t*)x,
+  const unsigned gx = (ntiles_max + 7) / 8 * 8;  // a multiple of 8 (the tile order is XCD-local)
+  hipLaunchKernelGGL(kern, dim3(gx, s.nsub()), dim3(64 * waves), 0, stream, (const bf16_t*)x,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (bf16_t*)hg, (bf16_t*)hu,
                      (bf16_t*)partials, nullptr, 0);
@@ -1044,7 +1054,8 @@ hipError_t dhdx2_t(const FfnShape& s, const void* dy, const void* wg, const void
     }
   }
   auto kern = partials_nontemporal(s, ntiles_max) ? dhdx2_kernel<GSB, kCpolNontemporal> : dhdx2_kernel<GSB, 0>;
-  hipLaunchKernelGGL(kern, dim3(ntiles_max, s.nsub()), dim3(64 * fwd_waves<GSB>()), 0, stream, (const bf16_t*)dy,
+  const unsigned gx = (ntiles_max + 7) / 8 * 8;  // a multiple of 8 (the tile order is XCD-local)
+  hipLaunchKernelGGL(kern, dim3(gx, s.nsub()), dim3(64 * fwd_waves<GSB>()), 0, stream, (const bf16_t*)dy,
                      (const bf16_t*)wg, (const bf16_t*)wu, (const bf16_t*)wd, s.tokens, s.d_model, s.d_ff,
                      s.group_size, tile_group, ptoken, (uint32_t)ntiles_max * BM, (const bf16_t*)hg,
                      (const bf16_t*)hu, (bf16_t*)dg, (bf16_t*)du, (bf16_t*)act, (bf16_t*)partials);
