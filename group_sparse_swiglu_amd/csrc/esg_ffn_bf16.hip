@@ -1147,14 +1147,22 @@ hipError_t launch_dw2(const FfnShape& s, const void* x, const void* dy, const in
 
 // From the shape alone: buckets above 1.5 times the mean (at least 16
 // tiles) are cut, so an even load runs one item per (unit, d-block) and a hot
-// group's chunks spread over the CUs.  (Cutting every bucket when the items
-// underfill the CUs, e.g. 168 items at the 370M shape into 504, measured
-// slower: weight gradients 145 -> 138 us, but the step 0.443 -> 0.506 ms, the
-// fp32 slots' traffic slowing the kernels around them.)
+// group's chunks spread over the CUs.  A launch whose (unit, d-block) items
+// number fewer than two per CU runs about one round, so its slowest item sets
+// the time: there buckets above 1.125 times the mean are cut (an even load's
+// largest bucket lies far below that: at the 370M shape 35 tiles against 31
+// on average, about 10 standard deviations of the binomial counts).  (Cutting
+// every bucket when the items underfill the CUs, e.g. 168 items at the 370M
+// shape into 504, measured slower: weight gradients 145 -> 138 us, but the
+// step 0.443 -> 0.506 ms, the fp32 slots' traffic slowing the kernels around
+// them.)
 int dw_chunk_tiles(const FfnShape& s, int ntiles_max, int pad) {
   if (!bf16_pipelined(s, ntiles_max) || s.gsb() != 128 || s.tokens <= 0) return 0;
   const long long mean_rows = ((long long)s.tokens * s.k + s.groups() - 1) / s.groups();
-  const long long cht = std::max(16ll, (3 * mean_rows + 2 * BM - 1) / (2 * BM));
+  const long long items = 2ll * s.groups() * s.nsub() * ((s.d_model + 128 * dw_subtiles<128>() - 1) /
+                                                           (128 * dw_subtiles<128>()));
+  const long long num = items >= 2ll * kNominalCUs ? 3 : 9, den = items >= 2ll * kNominalCUs ? 2 : 8;
+  const long long cht = std::max(16ll, (num * mean_rows + den * BM - 1) / (den * BM));
   // a bucket holds at most one position per token, padded to the pad unit
   const long long most = ((long long)s.tokens + pad - 1) / pad * (pad / BM);
   return cht >= most ? 0 : (int)cht;
