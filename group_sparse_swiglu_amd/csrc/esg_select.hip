@@ -30,12 +30,12 @@ constexpr int kSel128Waves = 8;
 // BM tokens per workgroup; each wave owns FNW 16-column fragments of a
 // super-chunk of 4*FNW*16 sampled rows, interleaved across the waves, so the
 // x tile is read once per super-chunk.
-// bf16 with BM = 32 or 128 streams both operands by direct-to-LDS loads
+// bf16 with BM = 32, 64 or 128 streams both operands by direct-to-LDS loads
 // into K-row tiles (64 K per stage, DMA_NS stages); other cases stage through
 // registers.  Every workgroup streams all sampled rows once per K step, so a
 // larger BM divides that traffic over more tokens.
-// Eight waves (NW = 8): 128-token blocks keep four column groups and split
-// their rows in two halves; 32-token blocks take eight column groups (the x
+// Eight waves (NW = 8): 64- and 128-token blocks keep four column groups and
+// split their rows in two halves; 32-token blocks take eight column groups (the x
 // tile's four load instructions then come from four waves, the other four
 // issue an empty load into a sink so that every wave counts the same loads).
 template <typename T, int BM, int FNW, bool USE_DMA = true, int NW = 4>
@@ -46,7 +46,8 @@ struct SelCfg {
   static constexpr int NSC = CG * FNW * 16;  // sampled rows per super-chunk
   static constexpr int FM = BM / 16;
   static constexpr int FMW = FM / RH;        // row fragments per wave
-  static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && (BM == 32 || BM == 128) && FNW <= 4;
+  static constexpr bool DMA = USE_DMA && std::is_same<T, bf16_t>::value && (BM == 32 || BM == 64 || BM == 128) &&
+                              FNW <= 4;
   static constexpr int IA = BM >= 8 * NW ? BM / (8 * NW) : 1;  // x load instructions per lane per stage
   static constexpr int IB = NSC / (8 * NW);
   static constexpr int SINK = BM < 8 * NW ? 1024 : 0;  // where the empty x loads land
@@ -562,6 +563,13 @@ hipError_t select_d(const SelArgs& a, float* ews, hipStream_t st) {
     // passes (162 us), whose 48 KB stages fit a 2-stage ring only, so one stage
     // was in flight per step and each step waited about a memory latency; 192-row
     // super-chunks take 4 passes with 40 KB stages in a 3-stage ring: 159 -> 147 us)
+    // (64 to 128 tokens per CU: 64-token blocks of eight waves, one per CU, with
+    // 192-row super-chunks: every workgroup streams all sampled rows, and 64
+    // tokens divide that over twice the tokens of 32-token blocks: 370M select
+    // 34 -> 29 us, README layer 72 -> 70 us)
+    if (a.tokens >= 64 * compute_units() && a.tokens < 128 * compute_units() &&
+        SelCfg<T, 64, 3, true, kSel128Waves>::FIXED + (size_t)64 * (groups | 1) * 4 + groups * 4 <= kSelLds)
+      return launch_select_t<T, 64, 3, kSel128Waves>(a, st);
     if (a.tokens >= 128 * compute_units()) {
       if (SelCfg<T, 128, 3, true, kSel128Waves>::FIXED + (size_t)128 * (groups | 1) * 4 + groups * 4 <= kSelLds)
         return launch_select_t<T, 128, 3, kSel128Waves>(a, st);
