@@ -154,3 +154,25 @@ def test_hot_group_of_two_sub_blocks_and_a_ragged_d():
     for name, a, b in zip(("y", "dx", "dW_gate", "dW_up", "dW_down"), outs, again):
         assert torch.equal(a, b), f"{name} differs between two runs"
 
+
+
+def test_hot_group_among_more_than_64_groups():
+    """80 groups of 128 (the weight-gradient plan scans the groups' chunk
+    counts in two 64-lane passes), every token routed to group 70 plus three
+    others: the hot bucket (4096 positions, 20 times the mean) is summed in
+    chunks; dW on neurons of the hot group and of groups past 64."""
+    require_gpu()
+    T, d, gs, G = 4096, 256, 128, 80
+    F = G * gs
+    note(f"skew {G} groups T={T}")
+    inp = inputs(T, d, F, gs, "bf16", seed=29, bias=False)
+    other = I.random_group_idx(T, G - 1, 3, seed=17).numpy()
+    other = other + (other >= 70)          # skip group 70
+    idx = np.sort(np.concatenate([np.full((T, 1), 70, np.int32), other], axis=1), axis=1).astype(np.int32)
+    outs = _run(inp, idx)
+    rng = np.random.default_rng(12)
+    neurons = {70 * gs + int(v) for v in rng.choice(gs, 6, replace=False)}
+    neurons |= {g * gs + int(rng.integers(gs)) for g in (64, 65, 79)}
+    neurons |= {int(v) for v in rng.choice(F, 10, replace=False)}
+    _sampled_compare(inp, idx, outs, neurons)
+    _exact_zeros_for_unused(idx, outs, G, gs)
