@@ -68,6 +68,10 @@ WORKLOAD_SAMPLED = [
     ("gs32_d512_readme", 16384, 512, 4096, 32, 8, "bf16", 8, True),
     # groups of 256 (two 128-neuron sub-blocks) past the pair threshold (1039 tiles x 2)
     ("gs256_pairs_two_subblocks", 32768, 1024, 4096, 256, 4, "bf16", 16, True),
+    # the ends of the active-fraction sweep at the 1.3B shape: one group per token
+    # (single tiles), and every group (k = G = 43: pair tiles, 5.8 GB of partial rows)
+    ("s1p3b_k1", 32768, 2048, 5504, 128, 1, "bf16", 16, True),
+    ("s1p3b_k43", 32768, 2048, 5504, 128, 43, "bf16", 16, True),
 ]
 
 
