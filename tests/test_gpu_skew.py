@@ -61,9 +61,12 @@ def _exact_zeros_for_unused(idx, outs, G, gs):
 
 
 HOT_CASES = [
-    # name, T, d, F, gs, k, spg  (the 128M and 1.3B workload shapes)
+    # name, T, d, F, gs, k, spg  (the skewed bench line's workload shapes)
     ("s128m_hot4", 8192, 768, 2048, 64, 8, 8),
     ("s1p3b_hot4", 32768, 2048, 5504, 128, 11, 16),
+    # the other shapes the skewed bench line runs: 370M, and the README's layer (groups of 32)
+    ("s370m_hot4", 16384, 1024, 2688, 128, 5, 16),
+    ("gs32_readme_hot4", 16384, 512, 4096, 32, 8, 8),
 ]
 
 
