@@ -731,13 +731,20 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
                                base + 2 * C::STAGE1, acc);
 
   // ---- epilogue: SiLU'; dg, du kept packed as accumulator fragments ----
-  uint2 dgp[FM][FN], dup[FM][FN];
+  // dg, du and a go out as whole 256-byte rows: staged in the (now idle)
+  // phase-1 LDS as [array][half][128 rows], dg and du first, then a.
+  using RE = RowStore<GSB, 64 * NW>;
+  constexpr int EH = 128 * RE::RB;  // one half of one array (32 KB)
+  static_assert(4 * EH <= LDS1, "dg and du staging");
+  wait_lgkm0();
+  barrier();  // every wave is done with the phase-1 stages
+  const int eh = p0 / BM;  // the half the wave's positions lie in
+  uint2 dgp[FM][FN], dup[FM][FN], apk[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int n = i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const size_t q = sub_el + (size_t)(prow0 + p0 + j * 16 + (lane & 15)) * GSB + n;
       float hg[4], hu[4], dgv[4], duv[4], av[4];
       unpack_bf16x4(hgq[i][j], hg);
       unpack_bf16x4(huq[i][j], hu);
@@ -750,13 +757,43 @@ __global__ __launch_bounds__(512, 1) void dhdx2_pair_kernel(
         duv[e] = da * silu;
         av[e] = silu * hu[e];
       }
-      Quad<bf16_t>::store(dg_out + q, dgv);
-      Quad<bf16_t>::store(du_out + q, duv);
-      Quad<bf16_t>::store(act_out + q, av);
+      const int r = (p0 % BM) + j * 16 + (lane & 15);
+      RE::put(base + eh * EH, base + eh * EH + EH / 2, r, n, dgv);
+      RE::put(base + (2 + eh) * EH, base + (2 + eh) * EH + EH / 2, r, n, duv);
       dgp[i][j] = make_uint2(pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3]));
       dup[i][j] = make_uint2(pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]));
+      apk[i][j] = make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
     }
   }
+  uint32_t roffE[RE::IT];
+#pragma unroll
+  for (int it = 0; it < RE::IT; ++it) roffE[it] = (uint32_t)RE::row(it, threadIdx.x) * GSB * 2;
+  auto rsE = [&](bf16_t* arr, int h) __attribute__((always_inline)) {
+    return make_rsrc(arr + sub_el + (size_t)(prow0 + h * BM) * GSB, (uint32_t)BM * GSB * 2);
+  };
+  wait_lgkm0();
+  barrier();  // dg and du staged
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    RE::template flush<0>(base + h * EH, base + h * EH + EH / 2, rsE(dg_out, h), roffE, 0, GSB);
+    RE::template flush<0>(base + (2 + h) * EH, base + (2 + h) * EH + EH / 2, rsE(du_out, h), roffE, 0, GSB);
+  }
+  wait_lgkm0();
+  barrier();  // their rows are read: stage a
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = (p0 % BM) + j * 16 + (lane & 15);
+      float av[4];
+      unpack_bf16x4(apk[i][j], av);
+      RE::put(base + eh * EH, base + eh * EH + EH / 2, r, i * 16 + (lane >> 4) * 4, av);
+    }
+  wait_lgkm0();
+  barrier();
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    RE::template flush<0>(base + h * EH, base + h * EH + EH / 2, rsE(act_out, h), roffE, 0, GSB);
 
   // ---- phase 2: Q^T = [Wg; Wu]^T[d-block] . [dg du]^T over all 256 positions ----
   // LDS: NWB weight buffers, then the row staging of half 0 and of half 1
