@@ -433,10 +433,16 @@ __global__ __launch_bounds__(512, 1) void fwd2_pair_kernel(
   }
 
   // ---- epilogue: hg, hu saved; a = SiLU(hg)*hu kept packed ----
-  const uint32_t sv_bytes = gridDim.y * rows_total * GSB * 2;
-  const rsrc_t rsv_g = make_rsrc(hg_saved, sv_bytes);
-  const rsrc_t rsv_u = make_rsrc(hu_saved, sv_bytes);
-  const uint32_t sub_off = (uint32_t)s * rows_total * GSB * 2;
+  // hg and hu go out as whole 256-byte rows, staged in the (now idle) phase-1
+  // LDS as [array][half][128 rows]
+  using RE = RowStore<GSB, C::NTH>;
+  constexpr int EH = 128 * RE::RB;  // one half of one array (32 KB)
+  static_assert(4 * EH <= 2 * A_BYTES + 3 * B_BYTES, "hg and hu staging");
+  const bool keep = hg_saved != nullptr;  // NULL: inference, nothing kept for a backward
+  if (keep) {
+    wait_lgkm0();
+    barrier();  // every wave is done with the phase-1 stages
+  }
   uint2 apk[FMP][FN];
 #pragma unroll
   for (int p = 0; p < FMP; ++p) {
@@ -450,12 +456,28 @@ __global__ __launch_bounds__(512, 1) void fwd2_pair_kernel(
         hu[e] = acc[FMP + p][j][e];
         a[e] = hg[e] * sigmoid_f(hg[e]) * hu[e];
       }
-      if (hg_saved != nullptr) {  // NULL: inference, nothing kept for a backward
-        const uint32_t so = sub_off + ((prow0 + brow[j]) * GSB + n) * 2;
-        store8(rsv_g, so, hg);
-        store8(rsv_u, so, hu);
+      if (keep) {
+        const int r = j * 16 + (lane & 15);  // row within the wave's half wn
+        RE::put(base + wn * EH, base + wn * EH + EH / 2, r, n, hg);
+        RE::put(base + (2 + wn) * EH, base + (2 + wn) * EH + EH / 2, r, n, hu);
       }
       apk[p][j] = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    }
+  }
+  if (keep) {
+    uint32_t roffE[RE::IT];
+#pragma unroll
+    for (int it = 0; it < RE::IT; ++it) roffE[it] = (uint32_t)RE::row(it, threadIdx.x) * GSB * 2;
+    const size_t sub_el = (size_t)s * rows_total * GSB;
+    wait_lgkm0();
+    barrier();  // hg and hu staged
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t r0 = sub_el + (size_t)(prow0 + h * BM) * GSB;
+      RE::template flush<0>(base + h * EH, base + h * EH + EH / 2, make_rsrc(hg_saved + r0, BM * GSB * 2), roffE,
+                            0, GSB);
+      RE::template flush<0>(base + (2 + h) * EH, base + (2 + h) * EH + EH / 2,
+                            make_rsrc(hu_saved + r0, BM * GSB * 2), roffE, 0, GSB);
     }
   }
 
