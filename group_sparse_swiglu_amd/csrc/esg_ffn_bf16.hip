@@ -245,6 +245,15 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
   barrier();  // every wave is done with the stages
 
   // ---- epilogue: hg, hu saved; a = SiLU(hg)*hu -> LDS K-row tile [position][neuron] ----
+  // hg and hu go out as whole rows, staged from st1 on as [array][128 rows]
+  // (the act tile lies in st0); 32-neuron rows (64 bytes) keep the direct
+  // 8-byte stores, which measured as fast
+  constexpr bool ROWS = GSB >= 64;
+  using RE = RowStore<GSB, C::NTH>;
+  constexpr int EH = 128 * RE::RB;  // one array (GSB * 256 bytes)
+  static_assert(2 * EH <= (FLAT ? (FLAT && P2 > P1 ? P2 : P1) - C::STAGE : (NS - 1) * C::STAGE),
+                "hg and hu staging after st0");
+  const bool keep = hg_saved != nullptr;  // NULL: inference, nothing kept for a backward
 #pragma unroll
   for (int p = 0; p < C::FMP; ++p) {
     const int n = wm * (GSB / C::WM) + p * 16 + (lane >> 4) * 4;  // 4 consecutive neurons
@@ -258,14 +267,31 @@ __global__ __launch_bounds__(64 * NW, GSB >= 128 || NW == 8 ? 1 : 2) void fwd2_k
         hu[e] = acc[C::FMP + p][j][e];
         a[e] = hg[e] * sigmoid_f(hg[e]) * hu[e];
       }
-      const uint32_t so = sub_off + ((prow0 + r) * GSB + n) * 2;
-      if (hg_saved != nullptr) {  // NULL: inference, nothing kept for a backward
-        store8(rsv_g, so, hg);
-        store8(rsv_u, so, hu);
+      if (keep) {
+        if constexpr (ROWS) {
+          RE::put(st1, st1 + EH / 2, r, n, hg);
+          RE::put(st1 + EH, st1 + EH + EH / 2, r, n, hu);
+        } else {
+          const uint32_t so = sub_off + ((prow0 + r) * GSB + n) * 2;
+          store8(rsv_g, so, hg);
+          store8(rsv_u, so, hu);
+        }
       }
       lds_write8(act + (n >> 6) * BM * 128 + krow_off(r, (n & 63) >> 3) + (n & 7) * 2, pack_bf16x2(a[0], a[1]),
                  pack_bf16x2(a[2], a[3]));
     }
+  }
+  if (ROWS && keep) {
+    uint32_t roffE[RE::IT];
+#pragma unroll
+    for (int it = 0; it < RE::IT; ++it) roffE[it] = (uint32_t)RE::row(it, threadIdx.x) * GSB * 2;
+    const size_t r0 = (size_t)s * rows_total * GSB + (size_t)prow0 * GSB;
+    wait_lgkm0();
+    barrier();  // hg and hu staged
+    RE::template flush<0>(st1, st1 + EH / 2, make_rsrc(hg_saved + r0, BM * GSB * 2), roffE, 0, GSB);
+    RE::template flush<0>(st1 + EH, st1 + EH + EH / 2, make_rsrc(hu_saved + r0, BM * GSB * 2), roffE, 0, GSB);
+    wait_lgkm0();
+    barrier();  // the staged rows are read before the W_down ring refills st1
   }
   }  // MODE 0
 
@@ -564,13 +590,23 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
   da_tile<GSB, NS, NW>(dy, wd, tokens, d, F, nb0, ptoken, prow0, st0, st1, st2, acc);
 
   // ---- epilogue: SiLU' ----
+  // dg and du go to the LDS K-row tile phase 2 reads, a to a row staging in
+  // st0; all three then go out as whole rows (32-neuron rows, 64 bytes, keep
+  // the direct 8-byte stores, which measured as fast)
+  constexpr bool ROWS = GSB >= 64;
+  using RE = RowStore<GSB, C::NTH>;
+  constexpr int EH = 128 * RE::RB;  // the a rows (GSB * 256 bytes)
+  static_assert(EH <= C::STAGE, "a staging in st0");
+  if constexpr (ROWS) {
+    wait_lgkm0();
+    barrier();  // every wave is done with the phase-1 stages
+  }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     const int n = wm * (GSB / C::WM) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int r = brow[j];
-      const size_t q = sub_el + (size_t)(prow0 + r) * GSB + n;
       float hg[4], hu[4], dgv[4], duv[4], av[4];
       unpack_bf16x4(hgq[i][j], hg);
       unpack_bf16x4(huq[i][j], hu);
@@ -583,15 +619,46 @@ __global__ __launch_bounds__(64 * fwd_waves<GSB>(), GSB >= 128 ? 1 : 2) void dhd
         duv[e] = da * silu;
         av[e] = silu * hu[e];
       }
-      Quad<bf16_t>::store(dg_out + q, dgv);
-      Quad<bf16_t>::store(du_out + q, duv);
-      Quad<bf16_t>::store(act_out + q, av);
+      if constexpr (ROWS) {
+        RE::put(st0, st0 + EH / 2, r, n, av);
+      } else {
+        const size_t q = sub_el + (size_t)(prow0 + r) * GSB + n;
+        Quad<bf16_t>::store(dg_out + q, dgv);
+        Quad<bf16_t>::store(du_out + q, duv);
+        Quad<bf16_t>::store(act_out + q, av);
+      }
       const int n2 = GSB + n;
       lds_write8(dgu + (n >> 6) * BM * 128 + krow_off(r, (n & 63) >> 3) + (n & 7) * 2, pack_bf16x2(dgv[0], dgv[1]),
                  pack_bf16x2(dgv[2], dgv[3]));
       lds_write8(dgu + (n2 >> 6) * BM * 128 + krow_off(r, (n2 & 63) >> 3) + (n2 & 7) * 2,
                  pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]));
     }
+  }
+
+  if constexpr (ROWS) {
+    wait_lgkm0();
+    barrier();  // dg, du and a staged
+    // dg, du rows from the K-row tile: chunk c (8 neurons) of row r of an
+    // array sits in sub-tile (c0 + c) / 8 at chunk (c0 + c) % 8, c0 = 0 (dg)
+    // or GSB / 8 (du); lanes take consecutive chunks, so each store
+    // instruction writes whole rows
+    constexpr int CPR = GSB / 8;  // 16-byte chunks per row
+    const size_t r0 = sub_el + (size_t)prow0 * GSB;
+    const rsrc_t rdg = make_rsrc(dg_out + r0, BM * GSB * 2), rdu = make_rsrc(du_out + r0, BM * GSB * 2);
+    for (int qq = threadIdx.x; qq < BM * CPR; qq += C::NTH) {
+      const int r = qq / CPR, c = qq % CPR, cu = CPR + c;
+      const u32x4_t vg = *(const ESG_LDS u32x4_t*)(dgu + (c >> 3) * BM * 128 + krow_off(r, c & 7));
+      const u32x4_t vu = *(const ESG_LDS u32x4_t*)(dgu + (cu >> 3) * BM * 128 + krow_off(r, cu & 7));
+      const uint32_t o = (uint32_t)r * GSB * 2 + c * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32, vg), rdg, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32, vu), rdu, o, 0, 0);
+    }
+    uint32_t roffE[RE::IT];
+#pragma unroll
+    for (int it = 0; it < RE::IT; ++it) roffE[it] = (uint32_t)RE::row(it, threadIdx.x) * GSB * 2;
+    RE::template flush<0>(st0, st0 + EH / 2, make_rsrc(act_out + r0, BM * GSB * 2), roffE, 0, GSB);
+    wait_lgkm0();
+    barrier();  // the a rows are read before phase 2 refills the stages
   }
 
   // ---- phase 2: Q^T = [Wg; Wu]^T[d-block] . [dg du]^T ----
