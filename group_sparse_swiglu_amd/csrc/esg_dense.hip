@@ -281,13 +281,18 @@ __global__ __launch_bounds__(64 * REC_NW, 1) void dense_rec_kernel(const bf16_t*
   // positions wn*64 + j*16 + lane%16
   static_assert(CF::WM == CD::WM && CF::FMP == CD::FM && CF::FN == CD::FN, "one wave mapping");
   const int wm = w % CD::WM, wn = w / CD::WM;
+  // dg, du, a go out as whole rows, staged in st0, st1, st2
+  using RE = RowStore<NB, 64 * REC_NW>;
+  constexpr int EH = 128 * RE::RB;
+  static_assert(EH <= STG, "one array per stage");
+  wait_lgkm0();
+  barrier();  // every wave is done with the stages
 #pragma unroll
   for (int i = 0; i < CD::FM; ++i) {
     const int n = wm * (NB / CD::WM) + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < CD::FN; ++j) {
       const int r = wn * 64 + j * 16 + (lane & 15);
-      const size_t q = ((size_t)blk * tc_pad + prow0 + r) * NB + n;
       float dgv[4], duv[4], av[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -298,11 +303,20 @@ __global__ __launch_bounds__(64 * REC_NW, 1) void dense_rec_kernel(const bf16_t*
         duv[e] = dA * silu;
         av[e] = silu * hu;
       }
-      Quad<bf16_t>::store(dg + q, dgv);
-      Quad<bf16_t>::store(du + q, duv);
-      Quad<bf16_t>::store(act + q, av);
+      RE::put(st0, st0 + EH / 2, r, n, dgv);
+      RE::put(st1, st1 + EH / 2, r, n, duv);
+      RE::put(st2, st2 + EH / 2, r, n, av);
     }
   }
+  uint32_t roffE[RE::IT];
+#pragma unroll
+  for (int it = 0; it < RE::IT; ++it) roffE[it] = (uint32_t)RE::row(it, threadIdx.x) * NB * 2;
+  const size_t r0 = ((size_t)blk * tc_pad + prow0) * NB;
+  wait_lgkm0();
+  barrier();  // the rows are staged
+  RE::template flush<0>(st0, st0 + EH / 2, make_rsrc(dg + r0, BM * NB * 2), roffE, 0, NB);
+  RE::template flush<0>(st1, st1 + EH / 2, make_rsrc(du + r0, BM * NB * 2), roffE, 0, NB);
+  RE::template flush<0>(st2, st2 + EH / 2, make_rsrc(act + r0, BM * NB * 2), roffE, 0, NB);
 }
 
 // dx[t0 + tile*128 + m, d-block] = sum over blocks of dg W_g + du W_u.
